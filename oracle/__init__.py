@@ -1,0 +1,111 @@
+"""CPU oracle for the Mamba2 selective-state scan -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The GPU library never calls it and shares no code
+with it.  The arithmetic lives in ``ssm_oracle.c`` (plain sequential C, built
+by ``oracle/build.py``); this module only marshals numpy arrays.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against things
+other than itself: a brute-force unrolled closed form, hand-worked fixtures,
+prefix sums, T=1 dot products, decay-only powers and invariants.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+DEFAULT_LIB = os.path.join(HERE, "libssm_oracle.so")
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def _ptr(a: np.ndarray, t):
+    return a.ctypes.data_as(t)
+
+
+class Oracle:
+    """Binds one build of the oracle library (the default one, or a test build)."""
+
+    def __init__(self, path: str = DEFAULT_LIB):
+        if not os.path.exists(path):
+            raise FileNotFoundError(
+                f"{path} is missing: build it with `python oracle/build.py`")
+        self.path = path
+        self.lib = ctypes.CDLL(path)
+        common = [ctypes.c_int32] * 5 + [_i32p, _i32p, _u8p] + [_f32p] * 5
+        self.lib.ssm_oracle_scan_f32.argtypes = common + [_f32p, _f32p, ctypes.c_int32]
+        self.lib.ssm_oracle_scan_f32.restype = ctypes.c_int
+        self.lib.ssm_oracle_scan_f64.argtypes = common + [_f64p, _f64p, ctypes.c_int32]
+        self.lib.ssm_oracle_scan_f64.restype = ctypes.c_int
+
+    def scan(self, H, P, N, G, cu_seqlens, slot, fresh, x, dt, A, B, C, state,
+             precision="f32", threads=None):
+        """Run the scan on a packed batch.
+
+        Returns ``(y, state_out)``; the input ``state`` is not modified.
+        precision "f32": fp32 arithmetic; "f64": double arithmetic on the same
+        fp32 inputs (y and state_out are float64 then).
+        """
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        slot = np.ascontiguousarray(slot, dtype=np.int32)
+        fresh = np.ascontiguousarray(fresh, dtype=np.uint8)
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        dt = np.ascontiguousarray(dt, dtype=np.float32)
+        A = np.ascontiguousarray(A, dtype=np.float32)
+        B = np.ascontiguousarray(B, dtype=np.float32)
+        C = np.ascontiguousarray(C, dtype=np.float32)
+        n_seqs = slot.shape[0]
+        T = int(cu[-1]) if cu.shape[0] else 0
+        assert cu.shape[0] == n_seqs + 1
+        assert x.shape == (T, H, P) and dt.shape == (T, H) and A.shape == (H,)
+        assert B.shape == (T, G, N) and C.shape == (T, G, N)
+        assert state.ndim == 4 and state.shape[1:] == (H, P, N)
+        if threads is None:
+            threads = os.cpu_count() or 1
+        if precision == "f32":
+            st = np.array(state, dtype=np.float32, copy=True, order="C")
+            y = np.zeros((T, H, P), dtype=np.float32)
+            fn, fp = self.lib.ssm_oracle_scan_f32, _f32p
+        elif precision == "f64":
+            st = np.array(state, dtype=np.float64, copy=True, order="C")
+            y = np.zeros((T, H, P), dtype=np.float64)
+            fn, fp = self.lib.ssm_oracle_scan_f64, _f64p
+        else:
+            raise ValueError(precision)
+        rc = fn(H, P, N, G, n_seqs, _ptr(cu, _i32p), _ptr(slot, _i32p),
+                _ptr(fresh, _u8p), _ptr(x, _f32p), _ptr(dt, _f32p), _ptr(A, _f32p),
+                _ptr(B, _f32p), _ptr(C, _f32p), _ptr(st, fp), _ptr(y, fp),
+                int(threads))
+        if rc != 0:
+            raise ValueError(f"oracle rejected the dimensions (rc={rc})")
+        return y, st
+
+    def scan_case(self, case, precision="f32", threads=None):
+        """``scan`` on an ``ssm_inputs.ScanCase``."""
+        return self.scan(case.H, case.P, case.N, case.G, case.cu_seqlens, case.slot,
+                         case.fresh, case.x, case.dt, case.A, case.B, case.C,
+                         case.state, precision=precision, threads=threads)
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def scan(*args, **kw):
+    return default().scan(*args, **kw)
+
+
+def scan_case(case, **kw):
+    return default().scan_case(case, **kw)

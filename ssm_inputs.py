@@ -1,0 +1,157 @@
+"""Seeded synthetic inputs for the Mamba2 selective-state scan.
+
+This module only draws random numbers and lays them out; it holds none of the
+scan's arithmetic.  Both the CPU oracle (through the tests) and the GPU path
+(through the tests and the benchmark) receive the very same host arrays from
+here, so the two sides see identical input bits.
+
+Shapes follow the operand table of ggml's CPU scan as transcribed on
+"the-llama-journey" (Day 12, the src0..src6 table): state [slot][head][row][n],
+x [token][head][row], dt [token][head], A [head] (one scalar per head for
+Mamba2), B and C [token][group][n].  Tokens of all sequences are packed one
+after another; ``cu_seqlens`` gives where each sequence starts.
+
+Value distributions (the five workloads named below): x, B, C ~ N(0, 1);
+dt ~ U[0.001, 0.1]; A = -exp(U[0, ln 16]) per head, so A is log-uniform in
+[-16, -1]; a resuming state ~ 0.5 * N(0, 1).  Draw order is fixed: A, dt, x,
+B, C, state.  The generator is numpy's PCG64 seeded with the case's seed.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = ["ScanCase", "make_case", "WORKLOADS", "workload", "lengths_to_cu"]
+
+
+@dataclass
+class ScanCase:
+    """One packed batch: dims, per-sequence metadata and the fp32 operands."""
+
+    H: int
+    P: int
+    N: int
+    G: int
+    lengths: np.ndarray          # int32 [n_seqs]
+    cu_seqlens: np.ndarray       # int32 [n_seqs + 1]
+    slot: np.ndarray             # int32 [n_seqs]
+    fresh: np.ndarray            # uint8 [n_seqs]
+    x: np.ndarray                # f32 [T, H, P]
+    dt: np.ndarray               # f32 [T, H]
+    A: np.ndarray                # f32 [H]
+    B: np.ndarray                # f32 [T, G, N]
+    C: np.ndarray                # f32 [T, G, N]
+    state: np.ndarray            # f32 [n_slots, H, P, N] (initial contents)
+    seed: int = 0
+    name: str = ""
+    notes: dict = field(default_factory=dict)
+
+    @property
+    def n_seqs(self) -> int:
+        return int(self.lengths.shape[0])
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def n_slots(self) -> int:
+        return int(self.state.shape[0])
+
+
+def lengths_to_cu(lengths) -> np.ndarray:
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = np.zeros(lengths.shape[0] + 1, dtype=np.int64)
+    np.cumsum(lengths, out=cu[1:])
+    return cu.astype(np.int32)
+
+
+def make_case(H, P, N, G, lengths, fresh, seed, *, slots=None, n_slots=None,
+              state_std=0.5, dt_lo=0.001, dt_hi=0.1, a_log_hi=math.log(16.0),
+              poison_fresh=False, sentinel_unused=False, name="") -> ScanCase:
+    """Draw one packed batch.
+
+    ``fresh`` is a sequence of 0/1 flags (1 = start from the zero state).
+    ``slots`` defaults to 0..n_seqs-1.  With ``poison_fresh`` the slots of
+    fresh sequences are filled with NaN (a correct scan never reads them).
+    With ``sentinel_unused`` slots that no sequence names are filled with a
+    recognisable finite pattern (they must come back bit-for-bit unchanged).
+    """
+    lengths = np.asarray(lengths, dtype=np.int32)
+    fresh = np.asarray(fresh, dtype=np.uint8)
+    n_seqs = lengths.shape[0]
+    if slots is None:
+        slots = np.arange(n_seqs, dtype=np.int32)
+    slots = np.asarray(slots, dtype=np.int32)
+    if n_slots is None:
+        n_slots = int(slots.max()) + 1 if n_seqs else 0
+    cu = lengths_to_cu(lengths)
+    T = int(cu[-1])
+    rng = np.random.Generator(np.random.PCG64(seed))
+    A = (-np.exp(rng.uniform(0.0, a_log_hi, size=H))).astype(np.float32)
+    dt = rng.uniform(dt_lo, dt_hi, size=(T, H)).astype(np.float32)
+    x = rng.standard_normal((T, H, P), dtype=np.float32)
+    B = rng.standard_normal((T, G, N), dtype=np.float32)
+    C = rng.standard_normal((T, G, N), dtype=np.float32)
+    state = rng.standard_normal((n_slots, H, P, N), dtype=np.float32)
+    state *= np.float32(state_std)
+    if sentinel_unused:
+        used = np.zeros(n_slots, dtype=bool)
+        used[slots] = True
+        for k in np.nonzero(~used)[0]:
+            state[k] = np.float32(1000.0 + k)
+    if poison_fresh:
+        for s in range(n_seqs):
+            if fresh[s]:
+                state[slots[s]] = np.nan
+    return ScanCase(H=H, P=P, N=N, G=G, lengths=lengths, cu_seqlens=cu, slot=slots,
+                    fresh=fresh, x=x, dt=dt, A=A, B=B, C=C, state=state, seed=seed,
+                    name=name)
+
+
+# The five workloads.  Seeds: the tiny scan's seed 0 is given; the others are
+# this project's choice (1..4), fixed here.
+def _tiny(seed=0):
+    return make_case(4, 16, 16, 1, [64], [1], seed, name="tiny_T64_H4_P16_N16_G1")
+
+
+def _decode16(seed=1, sets=1):
+    n = 16
+    return make_case(64, 64, 128, 8, [1] * n, [0] * n, seed, n_slots=n * sets,
+                     name="decode_16x1_H64_P64_N128_G8")
+
+
+def _prefill4096(seed=2):
+    return make_case(64, 64, 128, 8, [4096], [1], seed,
+                     name="prefill_1x4096_H64_P64_N128_G8")
+
+
+def _mixed(seed=3):
+    lengths = [1, 7, 25, 26, 64, 100, 150, 150]
+    fresh = [1 - (i % 2) for i in range(8)]          # odd indices resume
+    rng = np.random.Generator(np.random.PCG64(seed + 1000))
+    slots = rng.permutation(10)[:8].astype(np.int32)  # 2 of 10 slots unused
+    return make_case(16, 96, 100, 4, lengths, fresh, seed, slots=slots, n_slots=10,
+                     poison_fresh=True, sentinel_unused=True,
+                     name="mixed_8seq_H16_P96_N100_G4")
+
+
+def _decode256(seed=4):
+    n = 256
+    return make_case(64, 64, 128, 8, [1] * n, [0] * n, seed,
+                     name="decode_256x1_H64_P64_N128_G8")
+
+
+WORKLOADS = {
+    "tiny": _tiny,
+    "decode16": _decode16,
+    "prefill4096": _prefill4096,
+    "mixed": _mixed,
+    "decode256": _decode256,
+}
+
+
+def workload(name: str, **kw) -> ScanCase:
+    return WORKLOADS[name](**kw)
