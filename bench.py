@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X Mamba2 selective-state scan (one layer's scan).
+
+Headline: decode, 16 sequences x 1 token at H=64, P=64, N=128, G=8, fp32,
+resuming state.  A step is one ssm_scan_decode call.  Consecutive steps use
+16 disjoint slot sets of a 256-slot state (537 MB), so each step's 33.5 MB of
+state comes from HBM, not from the 256 MB Infinity Cache.  The 16 steps of one
+rotation are captured once in a HIP graph and replayed, so host launch
+overhead does not pad the step time.  Also measured and reported beside it:
+the 1 x 4096-token prefill at the same geometry (fresh state), eager launches.
+
+Prints one JSON line.  Times come from HIP events on the stream the kernels run
+on; the roofline objects use algorithmic bytes (decode, HBM-bound) and
+algorithmic flops (prefill, FP32 VALU-bound).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP32_VALU_PEAK_TFLOPS = 157.3  # 256 CU x 2.4 GHz x 256 flop/clk (packed FMA)
+FP32_VALU_UNPACKED_TFLOPS = 78.6
+H, P, N, G = 64, 64, 128, 8
+DECODE_SEQS, SLOT_SETS = 16, 16
+PREFILL_T = 4096
+
+
+def decode_bytes(n_seqs=DECODE_SEQS):
+    """Algorithmic bytes of one decode launch: resumed state read + written,
+    x, y, B, C, dt, A, slot, fresh -- each moved once."""
+    state = n_seqs * H * P * N * 4
+    return 2 * state + 2 * n_seqs * H * P * 4 + 2 * n_seqs * G * N * 4 + n_seqs * H * 4 \
+        + H * 4 + n_seqs * 4 + n_seqs
+
+
+def prefill_bytes(T=PREFILL_T):
+    """x and y, B and C, dt, A, cu_seqlens/slot/fresh, final state write."""
+    return 2 * T * H * P * 4 + 2 * T * G * N * 4 + T * H * 4 + H * 4 + 8 + 4 + 1 + H * P * N * 4
+
+
+def prefill_flops(T=PREFILL_T):
+    """5 flops per (token, head, row, state element): 2 multiplies and an add
+    for the update, a multiply and an add for y."""
+    return 5 * T * H * P * N
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in ("mamba2_selective_scan_amd/csrc/scan_kernel.hpp",
+                "mamba2_selective_scan_amd/csrc/ssm_scan.hip",
+                "mamba2_selective_scan_amd/build.py", "include/ssm_scan.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name):
+    """Measured HBM bytes per launch from a committed counter run, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_decode(case, seconds):
+    """The fp32 oracle on the same decode step, repeated for ~``seconds``."""
+    import oracle
+    threads = min(16, host_cores())
+    orc = oracle.default()
+    orc.scan_case(case, threads=threads)               # page in
+    n, t0 = 0, time.perf_counter()
+    while True:
+        orc.scan_case(case, threads=threads)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(el / n * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle",
+            "sample": f"{n} repetitions of the full decode 16x1 step (16 seqs x 64 heads x 64 "
+                      f"rows x 128 state, fp32, resuming), {el:.1f} s of CPU time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=320, help="timed decode steps")
+    ap.add_argument("--warmup", type=int, default=32, help="untimed decode steps")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the scan needs no collective and this build runs "
+              "on a single MI355X (see the sharding notes); run it with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mamba2_selective_scan_amd as ssm
+    import ssm_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------- decode 16x1, 16 rotating slot sets
+    case = ssm_inputs.workload("decode16", sets=SLOT_SETS)
+    d = ssm.to_device(case, dev)
+    slot_sets = [torch.arange(k * DECODE_SEQS, (k + 1) * DECODE_SEQS, dtype=torch.int32,
+                              device=dev) for k in range(SLOT_SETS)]
+    y = torch.empty((DECODE_SEQS, H, P), dtype=torch.float32, device=dev)
+
+    def decode_step(k):
+        ssm.decode(d["x"], d["dt"], d["A"], d["B"], d["C"], d["state"], slot_sets[k],
+                   d["fresh"], y=y)
+
+    for k in range(SLOT_SETS):                          # eager warm-up, sets the kernels up
+        decode_step(k)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(SLOT_SETS):
+            decode_step(k)
+    torch.cuda.synchronize()
+    replays_w = max(1, -(-args.warmup // SLOT_SETS))
+    replays = max(1, -(-args.steps // SLOT_SETS))
+    steps = replays * SLOT_SETS
+    for _ in range(replays_w):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_us = ev0.elapsed_time(ev1) * 1e3 / steps        # average step (= launch) duration
+    dec_gbs = decode_bytes() / (dec_us * 1e-6) / 1e9
+    traffic = load_traffic("decode16")
+
+    result = {
+        "metric": "scan time per layer (ms prefill 1x4096, us decode 16x1); % HBM/VALU roofline",
+        "value": round(dec_us, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": replays_w * SLOT_SETS,
+        "ms_per_step": round(dec_us / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; x,B,C ~ N(0,1), dt ~ U[0.001,0.1], A = -exp(U[0,ln16]), "
+                "state ~ 0.5 N(0,1))",
+        "config": {"workload": "decode 16 seqs x 1 token, resuming", "H": H, "P": P, "N": N,
+                   "G": G, "slot_sets_rotated": SLOT_SETS,
+                   "state_bytes_rotated": int(case.state.nbytes),
+                   "launch": "HIP graph of 16 steps, replayed",
+                   "geometry": ssm.geometry(H, P, N, G, DECODE_SEQS, decode=True)},
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": decode_bytes()},
+        "wall_s_timed": round(wall, 4),
+    }
+
+    # ---------------- prefill 1x4096, fresh
+    if not args.no_prefill:
+        pc = ssm_inputs.workload("prefill4096")
+        pd = ssm.to_device(pc, dev)
+        py = torch.empty((PREFILL_T, H, P), dtype=torch.float32, device=dev)
+
+        def prefill_once():
+            ssm.prefill(pd["x"], pd["dt"], pd["A"], pd["B"], pd["C"], pd["state"],
+                        pd["cu_seqlens"], pd["slot"], pd["fresh"], y=py)
+
+        for _ in range(args.prefill_warmup):
+            prefill_once()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(args.prefill_steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            prefill_once()
+            b.record(stream)
+            times.append((a, b))
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in times]
+        pf_ms = float(np.mean(ms))
+        tflops = prefill_flops() / (pf_ms * 1e-3) / 1e12
+        result["prefill"] = {
+            "workload": "prefill 1 seq x 4096 tokens, fresh", "ms": round(pf_ms, 4),
+            "ms_min": round(min(ms), 4), "ms_max": round(max(ms), 4),
+            "iterations": args.prefill_steps,
+            "geometry": ssm.geometry(H, P, N, G, 1),
+            "roofline": {"bound": "alu", "achieved": round(tflops, 3),
+                         "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / FP32_VALU_PEAK_TFLOPS, 4),
+                         "frac_of_unpacked_fp32": round(tflops / FP32_VALU_UNPACKED_TFLOPS, 4),
+                         "traffic": load_traffic("prefill4096"),
+                         "algorithmic_flops_per_launch": prefill_flops(),
+                         "algorithmic_bytes_per_launch": prefill_bytes(),
+                         "achieved_GBs": round(prefill_bytes() / (pf_ms * 1e-3) / 1e9, 1)},
+        }
+
+    if not args.no_cpu_baseline:
+        one_set = ssm_inputs.workload("decode16")
+        result["cpu_baseline"] = cpu_baseline_decode(one_set, args.cpu_seconds)
+    result["device"] = torch.cuda.get_device_name(dev)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

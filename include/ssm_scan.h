@@ -1,0 +1,156 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) Mamba2 selective-state scan.
+ *
+ * The operation.  For every sequence s of a packed token batch, every head h,
+ * head-dim row p and state index n, tokens strictly in order:
+ *
+ *     dA       = exp(dt[t][h] * A[h])
+ *     st[p][n] = st[p][n] * dA + B[t][g][n] * (x[t][h][p] * dt[t][h])
+ *     y[t][h][p] = sum over n of st[p][n] * C[t][g][n]    (after the update)
+ *
+ * with g = h / (n_heads / n_groups): heads share B and C by contiguous group.
+ * This is the recurrence of ggml's CPU scan and of its rewritten Mamba2 group
+ * kernel ("the-llama-journey", Day 12 operand table and loop nest, Day 14
+ * kernel), over a batch that mixes sequences starting from zero with
+ * sequences resuming from their state slot ("perf(cuda): keep the Mamba2 scan
+ * state in registers, stage tokens by chunk #90", What changes and Testing).
+ * dt is used as given (no softplus is applied) and B enters as dt*B.
+ *
+ * Conventions shared by every entry point:
+ *  - All array pointers are DEVICE pointers, dense and row-major in the
+ *    layouts written beside each argument, owned by the caller.  float arrays
+ *    are fp32 and must be 4-byte aligned; 16-byte alignment together with
+ *    d_state % 4 == 0 and head_dim % 4 == 0 selects the vector (float4) path.
+ *  - The library allocates nothing and never synchronizes.  Work is enqueued
+ *    on `stream` (a hipStream_t; NULL = the null stream) and the call returns
+ *    as soon as it is enqueued.
+ *  - Return value: SSM_OK (0) or a negative SSM_ERR_* code.  Argument errors
+ *    are detected on the host before anything is enqueued; then nothing on the
+ *    device has been touched.  No C++ exception crosses the ABI.
+ *  - The state slots named by `slot` are updated in place: read when the
+ *    sequence resumes (fresh[s] == 0), never read when it is fresh, and always
+ *    written with the state after the sequence's last token.  A zero-length
+ *    resuming sequence leaves its slot unchanged; a zero-length fresh one
+ *    zeroes it.  Slots no sequence names are not touched.
+ *  - y must not alias any input or the state.  Inputs may alias each other.
+ *  - Preconditions on device-array CONTENTS are not checked on the hot path:
+ *    cu_seqlens[0] == 0, non-decreasing, cu_seqlens[n_seqs] == n_tokens; slots
+ *    distinct and in [0, n_slots).  Breaking them is undefined behaviour (two
+ *    sequences writing one slot race); ssm_scan_check_metadata() checks them.
+ *  - The library holds no state; calls on different streams may run
+ *    concurrently if they touch disjoint slots and outputs.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_SCAN_ABI_VERSION 1
+#define SSM_SCAN_MAX_D_STATE 1024
+
+enum ssm_scan_status {
+    SSM_OK = 0,
+    SSM_ERR_NULL = -1,        /* a required pointer is NULL                        */
+    SSM_ERR_DIMS = -2,        /* a size is <= 0 (or < 0 where 0 is allowed), or
+                                 n_heads % n_groups != 0                            */
+    SSM_ERR_UNSUPPORTED = -3, /* d_state > SSM_SCAN_MAX_D_STATE or the grid would
+                                 exceed the launch limits                           */
+    SSM_ERR_ALIGN = -4,       /* a float or int array is not 4-byte aligned         */
+    SSM_ERR_LAUNCH = -5,      /* the HIP runtime refused the launch                 */
+    SSM_ERR_METADATA = -6     /* ssm_scan_check_metadata found a violation          */
+};
+
+/* H, P, N, G: heads, head-dim rows per head, state size, B/C groups. */
+typedef struct ssm_scan_dims {
+    int32_t n_heads;
+    int32_t head_dim;
+    int32_t d_state;
+    int32_t n_groups;
+} ssm_scan_dims;
+
+/*
+ * Prefill: scan a packed batch of n_seqs sequences, n_tokens tokens in all.
+ *   cu_seqlens [n_seqs+1] int32  token offsets; sequence s owns tokens
+ *                                 cu_seqlens[s] .. cu_seqlens[s+1]-1
+ *   slot       [n_seqs]   int32  state slot of each sequence
+ *   fresh      [n_seqs]   uint8  1 = start from the zero state (slot not read)
+ *   x          [n_tokens][H][P]  input
+ *   dt         [n_tokens][H]     step size (final; no softplus)
+ *   A          [H]               one decay rate per head (normally < 0)
+ *   B, C       [n_tokens][G][N]  input and output projections
+ *   state      [n_slots][H][P][N] read (resume) and written in place
+ *   y          [n_tokens][H][P]  output, fully overwritten
+ * n_seqs == 0 is a no-op returning SSM_OK.  With n_tokens == 0 the token
+ * arrays (x, dt, B, C, y) may be NULL.
+ */
+int ssm_scan_prefill(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens,
+                     const int32_t *cu_seqlens, const int32_t *slot,
+                     const uint8_t *fresh, const float *x, const float *dt,
+                     const float *A, const float *B, const float *C, float *state,
+                     int32_t n_slots, float *y, void *stream);
+
+/*
+ * Decode: one token for each of n_seqs sequences (token s belongs to sequence
+ * s).  Identical in meaning to ssm_scan_prefill with every length equal to 1;
+ * it exists so a decode step needs no cu_seqlens.
+ *   x [n_seqs][H][P], dt [n_seqs][H], B and C [n_seqs][G][N], y [n_seqs][H][P];
+ *   slot, fresh, A, state as for prefill.
+ */
+int ssm_scan_decode(const ssm_scan_dims *dims, int32_t n_seqs, const int32_t *slot,
+                    const uint8_t *fresh, const float *x, const float *dt,
+                    const float *A, const float *B, const float *C, float *state,
+                    int32_t n_slots, float *y, void *stream);
+
+/* Static text for a status code (never NULL). */
+const char *ssm_scan_strerror(int code);
+
+/* SSM_SCAN_ABI_VERSION of the built library. */
+int ssm_scan_version(void);
+
+/*
+ * The hipError_t of the last HIP runtime call that failed inside this library
+ * on the calling thread (0 if none has), and the runtime's text for it.  Lets
+ * a caller that got SSM_ERR_LAUNCH see why.  The text pointer is static.
+ */
+int ssm_scan_last_hip_error(void);
+const char *ssm_scan_last_hip_error_string(void);
+
+/*
+ * Debug / test helper on HOST arrays (copy them from the device first):
+ * checks cu_seqlens[0] == 0, non-decreasing, cu_seqlens[n_seqs] == n_tokens,
+ * every slot in [0, n_slots) and no slot named twice.  Returns SSM_OK,
+ * SSM_ERR_NULL, SSM_ERR_DIMS or SSM_ERR_METADATA.  cu_seqlens may be NULL to
+ * check the slots of a decode batch only.  Touches no device.
+ */
+int ssm_scan_check_metadata(int32_t n_seqs, int32_t n_tokens, const int32_t *cu_seqlens,
+                            const int32_t *slot, int32_t n_slots);
+
+/* The launch shape the library picks for a call (for logs and tests). */
+typedef struct ssm_scan_geometry {
+    int32_t lanes_per_row;     /* R: adjacent wavefront lanes that share one row   */
+    int32_t elems_per_lane;    /* E: state elements each lane keeps in registers  */
+    int32_t rows_per_block;    /* RB: head-dim rows one workgroup covers           */
+    int32_t chunk_tokens;      /* CT: tokens staged in LDS per chunk               */
+    int32_t threads_per_block;
+    int32_t lds_bytes;         /* dynamic LDS per workgroup                         */
+    int64_t blocks;            /* workgroups in the grid                            */
+    int32_t vector_path;       /* 1 = float4 loads and stores; 0 = scalar + LDS tile */
+} ssm_scan_geometry;
+
+/*
+ * Fill *out with the geometry a prefill (decode == 0) or decode (decode != 0)
+ * call with these sizes would launch.  `aligned` says whether the caller's
+ * pointers are all 16-byte aligned.  Touches no device.
+ */
+int ssm_scan_query_geometry(const ssm_scan_dims *dims, int32_t n_seqs, int32_t decode,
+                            int32_t aligned, ssm_scan_geometry *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

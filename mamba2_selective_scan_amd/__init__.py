@@ -1,0 +1,251 @@
+"""Python binding of the MI355X Mamba2 selective-state scan library.
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+``libssmscan.so`` (built from ``csrc/`` by ``build.py``), reached through its C
+ABI (``include/ssm_scan.h``).  torch supplies device memory and the current
+stream; tensors are passed as raw device pointers.  There is no CPU fallback:
+if the library is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libssmscan.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "ssm_scan.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+        "or `python mamba2_selective_scan_amd/build.py` first")
+
+# torch ships its own HIP runtime under the same soname (libamdhip64.so.7).
+# Importing torch first makes the library bind to that runtime, so torch's
+# device pointers and stream handles are valid in our calls.  Loading the
+# library first would bring in a second runtime and every launch would fail.
+import torch  # noqa: E402,F401  (load order matters, see above)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+def hip_runtimes_loaded() -> list:
+    """Paths of the HIP runtime libraries mapped into this process (Linux)."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+if len(hip_runtimes_loaded()) > 1:
+    raise ImportError("two HIP runtimes are loaded in this process "
+                      f"({hip_runtimes_loaded()}); import torch before anything that "
+                      "links /opt/rocm's libamdhip64, and before this package")
+
+SSM_OK = 0
+SSM_ERR_NULL = -1
+SSM_ERR_DIMS = -2
+SSM_ERR_UNSUPPORTED = -3
+SSM_ERR_ALIGN = -4
+SSM_ERR_LAUNCH = -5
+SSM_ERR_METADATA = -6
+MAX_D_STATE = 1024
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("d_state", ctypes.c_int32), ("n_groups", ctypes.c_int32)]
+
+
+class Geometry(ctypes.Structure):
+    _fields_ = [("lanes_per_row", ctypes.c_int32), ("elems_per_lane", ctypes.c_int32),
+                ("rows_per_block", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
+                ("threads_per_block", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("blocks", ctypes.c_int64), ("vector_path", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_lib.ssm_scan_prefill.argtypes = [ctypes.POINTER(Dims), _i32, _i32] + [_vp] * 9 + [_i32, _vp, _vp]
+_lib.ssm_scan_prefill.restype = ctypes.c_int
+_lib.ssm_scan_decode.argtypes = [ctypes.POINTER(Dims), _i32] + [_vp] * 8 + [_i32, _vp, _vp]
+_lib.ssm_scan_decode.restype = ctypes.c_int
+_lib.ssm_scan_strerror.argtypes = [ctypes.c_int]
+_lib.ssm_scan_strerror.restype = ctypes.c_char_p
+_lib.ssm_scan_version.argtypes = []
+_lib.ssm_scan_version.restype = ctypes.c_int
+_lib.ssm_scan_last_hip_error.argtypes = []
+_lib.ssm_scan_last_hip_error.restype = ctypes.c_int
+_lib.ssm_scan_last_hip_error_string.argtypes = []
+_lib.ssm_scan_last_hip_error_string.restype = ctypes.c_char_p
+_lib.ssm_scan_check_metadata.argtypes = [_i32, _i32, _vp, _vp, _i32]
+_lib.ssm_scan_check_metadata.restype = ctypes.c_int
+_lib.ssm_scan_query_geometry.argtypes = [ctypes.POINTER(Dims), _i32, _i32, _i32,
+                                         ctypes.POINTER(Geometry)]
+_lib.ssm_scan_query_geometry.restype = ctypes.c_int
+
+
+class ScanError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = f"{where}: {strerror(code)} (status {code})"
+        if code == SSM_ERR_LAUNCH:
+            self.hip_error = int(_lib.ssm_scan_last_hip_error())
+            msg += (f"; HIP error {self.hip_error}: "
+                    f"{_lib.ssm_scan_last_hip_error_string().decode()}")
+        super().__init__(msg)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (for callers that want the raw ABI)."""
+    return _lib
+
+
+def header_symbols() -> list:
+    """Names of the functions include/ssm_scan.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ssm_scan_\w+)\s*\(", text, re.M)))
+
+
+def strerror(code: int) -> str:
+    return _lib.ssm_scan_strerror(int(code)).decode()
+
+
+def version() -> int:
+    return int(_lib.ssm_scan_version())
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != SSM_OK:
+        raise ScanError(rc, where)
+
+
+def geometry(H, P, N, G, n_seqs, decode=False, aligned=True) -> dict:
+    out = Geometry()
+    _check(_lib.ssm_scan_query_geometry(ctypes.byref(Dims(H, P, N, G)), int(n_seqs),
+                                        int(bool(decode)), int(bool(aligned)),
+                                        ctypes.byref(out)), "ssm_scan_query_geometry")
+    return out.as_dict()
+
+
+def check_metadata(cu_seqlens, slot, n_tokens: int, n_slots: int) -> int:
+    """Check metadata given as host arrays (numpy/torch CPU int32) or None for
+    cu_seqlens; returns the status code (SSM_OK or SSM_ERR_*)."""
+    import numpy as np
+    slot_h = np.ascontiguousarray(_to_host(slot), dtype=np.int32)
+    cu_h = None if cu_seqlens is None else np.ascontiguousarray(_to_host(cu_seqlens),
+                                                                 dtype=np.int32)
+    return int(_lib.ssm_scan_check_metadata(
+        int(slot_h.shape[0]), int(n_tokens),
+        None if cu_h is None else cu_h.ctypes.data, slot_h.ctypes.data, int(n_slots)))
+
+
+def _to_host(a):
+    if hasattr(a, "detach"):
+        return a.detach().cpu().numpy()
+    return a
+
+
+# ------------------------------------------------------------------ torch side
+def _dev_ptr(t, dtype, name, device):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def prefill(x, dt, A, B, C, state, cu_seqlens, slot, fresh, y=None, stream=None):
+    """Scan a packed batch on the GPU (``ssm_scan_prefill``).
+
+    x [T, H, P], dt [T, H], A [H], B and C [T, G, N] fp32; state
+    [n_slots, H, P, N] fp32 (updated in place); cu_seqlens [n_seqs+1] and
+    slot [n_seqs] int32; fresh [n_seqs] uint8.  Returns y [T, H, P] (``y`` if
+    given).  Enqueued on ``stream`` (default: the current stream), no sync.
+    """
+    import torch
+    n_slots, H, P, N = (int(v) for v in state.shape)
+    T = int(x.shape[0])
+    G = int(B.shape[1])
+    n_seqs = int(slot.shape[0])
+    if tuple(x.shape) != (T, H, P) or tuple(dt.shape) != (T, H) or tuple(A.shape) != (H,):
+        raise ValueError("x, dt or A has the wrong shape")
+    if tuple(B.shape) != (T, G, N) or tuple(C.shape) != (T, G, N):
+        raise ValueError("B or C has the wrong shape")
+    if tuple(cu_seqlens.shape) != (n_seqs + 1,) or tuple(fresh.shape) != (n_seqs,):
+        raise ValueError("cu_seqlens or fresh has the wrong shape")
+    dev = state.device
+    if y is None:
+        y = torch.empty((T, H, P), dtype=torch.float32, device=dev)
+    elif tuple(y.shape) != (T, H, P):
+        raise ValueError("y has the wrong shape")
+    f32, i32 = torch.float32, torch.int32
+    rc = _lib.ssm_scan_prefill(
+        ctypes.byref(Dims(H, P, N, G)), n_seqs, T,
+        _dev_ptr(cu_seqlens, i32, "cu_seqlens", dev), _dev_ptr(slot, i32, "slot", dev),
+        _dev_ptr(fresh, torch.uint8, "fresh", dev), _dev_ptr(x, f32, "x", dev),
+        _dev_ptr(dt, f32, "dt", dev), _dev_ptr(A, f32, "A", dev), _dev_ptr(B, f32, "B", dev),
+        _dev_ptr(C, f32, "C", dev), _dev_ptr(state, f32, "state", dev), n_slots,
+        _dev_ptr(y, f32, "y", dev), _stream_handle(stream, dev))
+    _check(rc, "ssm_scan_prefill")
+    return y
+
+
+def decode(x, dt, A, B, C, state, slot, fresh, y=None, stream=None):
+    """One token per sequence on the GPU (``ssm_scan_decode``).
+
+    x [S, H, P], dt [S, H], A [H], B and C [S, G, N]; state as for prefill;
+    slot [S] int32, fresh [S] uint8.  Returns y [S, H, P].
+    """
+    import torch
+    n_slots, H, P, N = (int(v) for v in state.shape)
+    S = int(slot.shape[0])
+    G = int(B.shape[1])
+    if tuple(x.shape) != (S, H, P) or tuple(dt.shape) != (S, H) or tuple(A.shape) != (H,):
+        raise ValueError("x, dt or A has the wrong shape")
+    if tuple(B.shape) != (S, G, N) or tuple(C.shape) != (S, G, N):
+        raise ValueError("B or C has the wrong shape")
+    if tuple(fresh.shape) != (S,):
+        raise ValueError("fresh has the wrong shape")
+    dev = state.device
+    if y is None:
+        y = torch.empty((S, H, P), dtype=torch.float32, device=dev)
+    elif tuple(y.shape) != (S, H, P):
+        raise ValueError("y has the wrong shape")
+    f32 = torch.float32
+    rc = _lib.ssm_scan_decode(
+        ctypes.byref(Dims(H, P, N, G)), S, _dev_ptr(slot, torch.int32, "slot", dev),
+        _dev_ptr(fresh, torch.uint8, "fresh", dev), _dev_ptr(x, f32, "x", dev),
+        _dev_ptr(dt, f32, "dt", dev), _dev_ptr(A, f32, "A", dev), _dev_ptr(B, f32, "B", dev),
+        _dev_ptr(C, f32, "C", dev), _dev_ptr(state, f32, "state", dev), n_slots,
+        _dev_ptr(y, f32, "y", dev), _stream_handle(stream, dev))
+    _check(rc, "ssm_scan_decode")
+    return y
+
+
+def to_device(case, device="cuda:0"):
+    """Copy an ``ssm_inputs.ScanCase``'s arrays to ``device`` as torch tensors."""
+    import torch
+    d = {}
+    for f in ("x", "dt", "A", "B", "C", "state", "cu_seqlens", "slot", "fresh"):
+        d[f] = torch.from_numpy(getattr(case, f)).to(device)
+    return d

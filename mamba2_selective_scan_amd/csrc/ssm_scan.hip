@@ -1,0 +1,280 @@
+// ssm_scan.hip -- the C ABI (include/ssm_scan.h) over the gfx950 scan kernel.
+//
+// Host side only: validate sizes and pointers, pick the compiled kernel shape
+// for the state size, and enqueue one launch on the caller's stream.  Nothing
+// here allocates device memory or synchronizes.
+#include "ssm_scan.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "scan_kernel.hpp"
+
+namespace {
+
+using ssm::kThreads;
+using ssm::ScanArgs;
+using ssm::Shape;
+
+// One row of the shape table: state sizes up to n_max use R lanes per row,
+// J float4 groups per lane and CT tokens per prefill chunk.  R lanes hold
+// 4*R*J >= N elements; the table keeps E = 4J at 4..16 registers and the
+// double-buffered staging under ~80 KB of the 160 KB LDS.
+struct ShapeRow {
+    int n_max, R, J, CT;
+};
+constexpr ShapeRow kShapes[] = {
+    {16, 4, 1, 32},
+    {32, 8, 1, 32},
+    {64, 16, 1, 32},
+    {128, 16, 2, 32},
+    {256, 16, 4, 16},
+    {512, 32, 4, 8},
+    {1024, 64, 4, 4},
+};
+static_assert(kShapes[sizeof(kShapes) / sizeof(kShapes[0]) - 1].n_max == SSM_SCAN_MAX_D_STATE,
+              "the table must cover every supported state size");
+
+const ShapeRow *shape_for(int N) {
+    for (const ShapeRow &row : kShapes)
+        if (N <= row.n_max) return &row;
+    return nullptr;
+}
+
+constexpr int kMaxDevices = 64;
+
+thread_local hipError_t t_last_hip_error = hipSuccess;
+
+int hip_fail(hipError_t err, int code) {
+    t_last_hip_error = err;
+    return code;
+}
+
+template <class S, bool VEC, bool DECODE>
+int launch(const ScanArgs &a, hipStream_t stream) {
+    const void *kern = reinterpret_cast<const void *>(&ssm::scan_kernel<S, VEC, DECODE>);
+    const int lds_bytes = S::lds_floats(DECODE, VEC) * int(sizeof(float));
+    if (lds_bytes > 64 * 1024) {
+        // Opt in to more than 64 KB of dynamic LDS, once per device.
+        static std::atomic<uint8_t> opted[kMaxDevices];
+        int dev = 0;
+        const hipError_t derr = hipGetDevice(&dev);
+        if (derr != hipSuccess) return hip_fail(derr, SSM_ERR_LAUNCH);
+        if (dev < 0 || dev >= kMaxDevices) return SSM_ERR_UNSUPPORTED;
+        if (!opted[dev].load(std::memory_order_acquire)) {
+            const hipError_t aerr =
+                hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+            if (aerr != hipSuccess) return hip_fail(aerr, SSM_ERR_LAUNCH);
+            opted[dev].store(1, std::memory_order_release);
+        }
+    }
+    ScanArgs args = a;
+    void *params[] = {&args};
+    const hipError_t err = hipLaunchKernel(kern, dim3(unsigned(a.n_blocks)), dim3(kThreads), params,
+                                           size_t(lds_bytes), stream);
+    return err == hipSuccess ? SSM_OK : hip_fail(err, SSM_ERR_LAUNCH);
+}
+
+// Calls f.template run<R, J, CT>() for the table row (the row's compile-time shape).
+template <class F>
+int with_row(const ShapeRow &row, F &&f) {
+    switch (row.n_max) {
+    case 16: return f.template run<4, 1, 32>();
+    case 32: return f.template run<8, 1, 32>();
+    case 64: return f.template run<16, 1, 32>();
+    case 128: return f.template run<16, 2, 32>();
+    case 256: return f.template run<16, 4, 16>();
+    case 512: return f.template run<32, 4, 8>();
+    case 1024: return f.template run<64, 4, 4>();
+    default: return SSM_ERR_UNSUPPORTED;
+    }
+}
+
+struct Launch {
+    const ScanArgs &a;
+    bool vec, decode;
+    hipStream_t stream;
+    template <int R, int J, int CT>
+    int run() const {
+        if (decode)
+            return vec ? launch<Shape<R, J, 1>, true, true>(a, stream)
+                       : launch<Shape<R, J, 1>, false, true>(a, stream);
+        return vec ? launch<Shape<R, J, CT>, true, false>(a, stream)
+                   : launch<Shape<R, J, CT>, false, false>(a, stream);
+    }
+};
+
+struct LdsBytes {
+    bool vec, decode;
+    template <int R, int J, int CT>
+    int run() const {
+        return int(sizeof(float)) * (decode ? Shape<R, J, 1>::lds_floats(true, vec)
+                                            : Shape<R, J, CT>::lds_floats(false, vec));
+    }
+};
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_dims(const ssm_scan_dims *d) {
+    if (!d) return SSM_ERR_NULL;
+    if (d->n_heads <= 0 || d->head_dim <= 0 || d->d_state <= 0 || d->n_groups <= 0)
+        return SSM_ERR_DIMS;
+    if (d->n_heads % d->n_groups != 0) return SSM_ERR_DIMS;
+    if (d->d_state > SSM_SCAN_MAX_D_STATE) return SSM_ERR_UNSUPPORTED;
+    return SSM_OK;
+}
+
+// Shared body of prefill and decode once the arguments are known valid.
+int scan_common(const ssm_scan_dims *d, int32_t n_seqs, const int32_t *cu_seqlens,
+                const int32_t *slot, const uint8_t *fresh, const float *x, const float *dt,
+                const float *A, const float *B, const float *C, float *state, float *y,
+                bool decode, void *stream) {
+    const ShapeRow *row = shape_for(d->d_state);
+    if (!row) return SSM_ERR_UNSUPPORTED;
+    const int RB = ssm::kWaves * (64 / row->R);
+    const int64_t n_row_blocks = (int64_t(d->head_dim) + RB - 1) / RB;
+    const int64_t n_blocks = int64_t(n_seqs) * d->n_heads * n_row_blocks;
+    if (n_blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+
+    const void *fptrs[] = {x, dt, A, B, C, state, y};
+    bool vec = (d->d_state % 4 == 0) && (d->head_dim % 4 == 0);
+    for (const void *p : fptrs) {
+        if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+        if (p && !aligned(p, 16)) vec = false;
+    }
+    if (!aligned(slot, 4) || (cu_seqlens && !aligned(cu_seqlens, 4))) return SSM_ERR_ALIGN;
+
+    ScanArgs a{};
+    a.cu_seqlens = cu_seqlens;
+    a.slot = slot;
+    a.fresh = fresh;
+    a.x = x;
+    a.dt = dt;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.state = state;
+    a.y = y;
+    a.H = d->n_heads;
+    a.P = d->head_dim;
+    a.N = d->d_state;
+    a.G = d->n_groups;
+    a.heads_per_group = d->n_heads / d->n_groups;
+    a.n_row_blocks = int32_t(n_row_blocks);
+    a.n_blocks = int32_t(n_blocks);
+    return with_row(*row, Launch{a, vec, decode, static_cast<hipStream_t>(stream)});
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_prefill(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens,
+                     const int32_t *cu_seqlens, const int32_t *slot, const uint8_t *fresh,
+                     const float *x, const float *dt, const float *A, const float *B,
+                     const float *C, float *state, int32_t n_slots, float *y, void *stream) {
+    const int rc = check_dims(dims);
+    if (rc != SSM_OK) return rc;
+    if (n_seqs < 0 || n_tokens < 0 || n_slots < 0) return SSM_ERR_DIMS;
+    if (n_seqs == 0) return SSM_OK;
+    if (n_slots == 0) return SSM_ERR_DIMS;
+    if (!cu_seqlens || !slot || !fresh || !A || !state) return SSM_ERR_NULL;
+    if (n_tokens > 0 && (!x || !dt || !B || !C || !y)) return SSM_ERR_NULL;
+    return scan_common(dims, n_seqs, cu_seqlens, slot, fresh, x, dt, A, B, C, state, y,
+                       /*decode=*/false, stream);
+}
+
+int ssm_scan_decode(const ssm_scan_dims *dims, int32_t n_seqs, const int32_t *slot,
+                    const uint8_t *fresh, const float *x, const float *dt, const float *A,
+                    const float *B, const float *C, float *state, int32_t n_slots, float *y,
+                    void *stream) {
+    const int rc = check_dims(dims);
+    if (rc != SSM_OK) return rc;
+    if (n_seqs < 0 || n_slots < 0) return SSM_ERR_DIMS;
+    if (n_seqs == 0) return SSM_OK;
+    if (n_slots == 0) return SSM_ERR_DIMS;
+    if (!slot || !fresh || !A || !state || !x || !dt || !B || !C || !y) return SSM_ERR_NULL;
+    return scan_common(dims, n_seqs, nullptr, slot, fresh, x, dt, A, B, C, state, y,
+                       /*decode=*/true, stream);
+}
+
+const char *ssm_scan_strerror(int code) {
+    switch (code) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL: return "a required pointer is NULL";
+    case SSM_ERR_DIMS: return "invalid size (non-positive dimension, negative count, or n_heads % n_groups != 0)";
+    case SSM_ERR_UNSUPPORTED: return "unsupported size (d_state above the maximum, or the grid is too large)";
+    case SSM_ERR_ALIGN: return "an array is not 4-byte aligned";
+    case SSM_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+    case SSM_ERR_METADATA: return "invalid metadata (cu_seqlens not monotone from 0 to n_tokens, or a slot out of range or repeated)";
+    default: return "unknown status code";
+    }
+}
+
+int ssm_scan_version(void) { return SSM_SCAN_ABI_VERSION; }
+
+int ssm_scan_last_hip_error(void) { return int(t_last_hip_error); }
+
+const char *ssm_scan_last_hip_error_string(void) {
+    return t_last_hip_error == hipSuccess ? "no error" : hipGetErrorString(t_last_hip_error);
+}
+
+int ssm_scan_check_metadata(int32_t n_seqs, int32_t n_tokens, const int32_t *cu_seqlens,
+                            const int32_t *slot, int32_t n_slots) {
+    if (n_seqs < 0 || n_tokens < 0 || n_slots < 0) return SSM_ERR_DIMS;
+    if (n_seqs == 0) return SSM_OK;
+    if (!slot) return SSM_ERR_NULL;
+    if (cu_seqlens) {
+        if (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] != n_tokens) return SSM_ERR_METADATA;
+        for (int32_t s = 0; s < n_seqs; ++s)
+            if (cu_seqlens[s + 1] < cu_seqlens[s]) return SSM_ERR_METADATA;
+    }
+    for (int32_t s = 0; s < n_seqs; ++s)
+        if (slot[s] < 0 || slot[s] >= n_slots) return SSM_ERR_METADATA;
+    // distinct slots: sort-free check with a bitmap over [0, n_slots)
+    const int64_t words = (int64_t(n_slots) + 63) / 64;
+    uint64_t small[64];
+    uint64_t *seen = small;
+    uint64_t *heap = nullptr;
+    if (words > 64) {
+        heap = new (std::nothrow) uint64_t[size_t(words)];
+        if (!heap) return SSM_ERR_UNSUPPORTED;
+        seen = heap;
+    }
+    std::memset(seen, 0, size_t(words) * sizeof(uint64_t));
+    int rc = SSM_OK;
+    for (int32_t s = 0; s < n_seqs && rc == SSM_OK; ++s) {
+        const uint64_t bit = uint64_t(1) << (slot[s] % 64);
+        uint64_t &w = seen[slot[s] / 64];
+        if (w & bit) rc = SSM_ERR_METADATA;
+        w |= bit;
+    }
+    delete[] heap;
+    return rc;
+}
+
+int ssm_scan_query_geometry(const ssm_scan_dims *dims, int32_t n_seqs, int32_t decode,
+                            int32_t aligned16, ssm_scan_geometry *out) {
+    const int rc = check_dims(dims);
+    if (rc != SSM_OK) return rc;
+    if (!out) return SSM_ERR_NULL;
+    if (n_seqs < 0) return SSM_ERR_DIMS;
+    const ShapeRow *row = shape_for(dims->d_state);
+    if (!row) return SSM_ERR_UNSUPPORTED;
+    const bool vec = aligned16 && dims->d_state % 4 == 0 && dims->head_dim % 4 == 0;
+    const int RB = ssm::kWaves * (64 / row->R);
+    out->lanes_per_row = row->R;
+    out->elems_per_lane = 4 * row->J;
+    out->rows_per_block = RB;
+    out->chunk_tokens = decode ? 1 : row->CT;
+    out->threads_per_block = kThreads;
+    out->lds_bytes = with_row(*row, LdsBytes{vec, decode != 0});
+    out->blocks = int64_t(n_seqs) * dims->n_heads * ((int64_t(dims->head_dim) + RB - 1) / RB);
+    out->vector_path = vec ? 1 : 0;
+    return SSM_OK;
+}
+
+}  // extern "C"

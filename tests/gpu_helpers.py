@@ -1,0 +1,84 @@
+"""Helpers shared by the GPU tests: run a case through the C ABI on cuda:0 and
+compare with the oracle.  Every input comes from ssm_inputs (seeded); every
+expected value from the oracle or from closed forms -- never from the GPU."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import ssm_inputs
+
+TOL = 1e-4          # max |gpu - ref| / (1 + |ref|) on y and on the final state
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(a, ref):
+    a = np.asarray(a, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if a.size == 0:
+        return 0.0
+    return float(np.max(np.abs(a - ref) / (1.0 + np.abs(ref))))
+
+
+def run_gpu(case, mode="prefill", device="cuda:0", offset_floats=0):
+    """Run ``case`` on the GPU; returns (y, state) as numpy.  ``mode`` is
+    "prefill" or "decode" (every length must be 1).  ``offset_floats`` > 0
+    places every float array at that element offset inside a larger buffer,
+    which breaks 16-byte alignment and forces the scalar path."""
+    import torch
+    import mamba2_selective_scan_amd as ssm
+
+    def put(arr):
+        t = torch.from_numpy(np.ascontiguousarray(arr))
+        if offset_floats and t.dtype == torch.float32:
+            flat = torch.empty(t.numel() + offset_floats, dtype=t.dtype, device=device)
+            view = flat[offset_floats:].view(t.shape)
+            view.copy_(t.to(device))
+            return view
+        return t.to(device)
+
+    x, dt, A, B, C = (put(getattr(case, f)) for f in ("x", "dt", "A", "B", "C"))
+    state = put(case.state)
+    slot = put(case.slot)
+    fresh = put(case.fresh)
+    y = put(np.zeros((case.n_tokens, case.H, case.P), np.float32))
+    if mode == "prefill":
+        cu = put(case.cu_seqlens)
+        ssm.prefill(x, dt, A, B, C, state, cu, slot, fresh, y=y)
+    elif mode == "decode":
+        assert np.all(case.lengths == 1)
+        ssm.decode(x, dt, A, B, C, state, slot, fresh, y=y)
+    else:
+        raise ValueError(mode)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), state.cpu().numpy()
+
+
+def assert_parity(case, y_gpu, st_gpu, y_ref, st_ref, tol=TOL, label=""):
+    used = np.unique(case.slot)
+    e_y = rel_err(y_gpu, y_ref)
+    e_s = rel_err(st_gpu[used], st_ref[used]) if used.size else 0.0
+    say(f"  {label or case.name}: max rel err y={e_y:.3e} state={e_s:.3e}")
+    assert np.all(np.isfinite(y_gpu)), "non-finite y"
+    assert e_y <= tol, f"y error {e_y} > {tol}"
+    assert e_s <= tol, f"state error {e_s} > {tol}"
+    unused = np.setdiff1d(np.arange(case.n_slots), used)
+    for k in unused:
+        assert np.array_equal(st_gpu[k], case.state[k], equal_nan=True), f"unused slot {k} changed"
+
+
+def sub_case(case, seqs):
+    """The sequences ``seqs`` of a packed case, repacked (same slots)."""
+    parts = [(int(case.cu_seqlens[s]), int(case.cu_seqlens[s + 1])) for s in seqs]
+    idx = np.concatenate([np.arange(a, b) for a, b in parts]) if parts else np.zeros(0, int)
+    lengths = np.array([b - a for a, b in parts], np.int32)
+    return ssm_inputs.ScanCase(H=case.H, P=case.P, N=case.N, G=case.G, lengths=lengths,
+                               cu_seqlens=ssm_inputs.lengths_to_cu(lengths),
+                               slot=case.slot[list(seqs)], fresh=case.fresh[list(seqs)],
+                               x=case.x[idx], dt=case.dt[idx], A=case.A, B=case.B[idx],
+                               C=case.C[idx], state=case.state, name=case.name + f"[{seqs}]")

@@ -1,0 +1,122 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every function
+include/ssm_scan.h declares, rejects bad arguments with the documented codes
+before touching any device, and reports launch geometry; every compiled
+kernel keeps its state in registers (no scratch)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mamba2_selective_scan_amd as m
+
+D = m.Dims
+
+
+def test_exports_every_declared_symbol():
+    names = m.header_symbols()
+    assert set(names) == {"ssm_scan_prefill", "ssm_scan_decode", "ssm_scan_strerror",
+                          "ssm_scan_version", "ssm_scan_check_metadata",
+                          "ssm_scan_query_geometry", "ssm_scan_last_hip_error",
+                          "ssm_scan_last_hip_error_string"}
+    for n in names:
+        assert hasattr(m.lib(), n), n
+
+
+def test_version_and_strerror():
+    assert m.version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert m.strerror(code) and "unknown" not in m.strerror(code)
+    assert "unknown" in m.strerror(-99)
+    assert m.lib().ssm_scan_last_hip_error() == 0
+    assert m.lib().ssm_scan_last_hip_error_string() == b"no error"
+
+
+FAKE = 0x10000          # never dereferenced: argument checks fail before any launch
+
+
+def _prefill(dims, n_seqs=1, n_tokens=4, ptrs=None, n_slots=1, fake=FAKE):
+    p = dict(cu=fake, slot=fake, fresh=fake, x=fake, dt=fake, A=fake, B=fake, C=fake,
+             state=fake, y=fake)
+    p.update(ptrs or {})
+    return m.lib().ssm_scan_prefill(None if dims is None else ctypes.byref(dims), n_seqs,
+                                    n_tokens, p["cu"], p["slot"], p["fresh"], p["x"], p["dt"],
+                                    p["A"], p["B"], p["C"], p["state"], n_slots, p["y"], None)
+
+
+def _decode(dims, n_seqs=1, ptrs=None, n_slots=1, fake=FAKE):
+    p = dict(slot=fake, fresh=fake, x=fake, dt=fake, A=fake, B=fake, C=fake, state=fake, y=fake)
+    p.update(ptrs or {})
+    return m.lib().ssm_scan_decode(None if dims is None else ctypes.byref(dims), n_seqs,
+                                   p["slot"], p["fresh"], p["x"], p["dt"], p["A"], p["B"],
+                                   p["C"], p["state"], n_slots, p["y"], None)
+
+
+@pytest.mark.parametrize("call", [_prefill, _decode])
+def test_argument_errors(call):
+    ok = D(4, 8, 16, 2)
+    assert call(None) == m.SSM_ERR_NULL
+    for bad in (D(0, 8, 16, 2), D(4, 0, 16, 2), D(4, 8, 0, 2), D(4, 8, 16, 0), D(4, 8, 16, 3),
+                D(-4, 8, 16, 2)):
+        assert call(bad) == m.SSM_ERR_DIMS
+    assert call(D(4, 8, 1025, 2)) == m.SSM_ERR_UNSUPPORTED
+    assert call(ok, n_seqs=-1) == m.SSM_ERR_DIMS
+    assert call(ok, n_seqs=0) == m.SSM_OK                # no-op, nothing launched
+    assert call(ok, n_slots=0) == m.SSM_ERR_DIMS
+    assert call(ok, n_slots=-2) == m.SSM_ERR_DIMS
+    for name in ("slot", "fresh", "A", "state", "x", "y"):
+        assert call(ok, ptrs={name: None}) == m.SSM_ERR_NULL, name
+    for name in ("x", "dt", "A", "B", "C", "state", "y", "slot"):
+        assert call(ok, ptrs={name: FAKE + 2}) == m.SSM_ERR_ALIGN, name
+
+
+def test_prefill_specific_errors():
+    ok = D(4, 8, 16, 2)
+    assert _prefill(ok, n_tokens=-1) == m.SSM_ERR_DIMS
+    assert _prefill(ok, ptrs={"cu": None}) == m.SSM_ERR_NULL
+    assert _prefill(ok, ptrs={"cu": FAKE + 1}) == m.SSM_ERR_ALIGN
+
+
+def test_check_metadata():
+    cu = np.array([0, 3, 3, 5], np.int32)
+    assert m.check_metadata(cu, np.array([2, 0, 1]), 5, 3) == m.SSM_OK
+    assert m.check_metadata(cu, np.array([2, 0, 2]), 5, 3) == m.SSM_ERR_METADATA   # repeated
+    assert m.check_metadata(cu, np.array([2, 0, 3]), 5, 3) == m.SSM_ERR_METADATA   # range
+    assert m.check_metadata(cu, np.array([2, 0, -1]), 5, 3) == m.SSM_ERR_METADATA
+    assert m.check_metadata(cu, np.array([2, 0, 1]), 6, 3) == m.SSM_ERR_METADATA   # total
+    assert m.check_metadata(np.array([1, 3, 3, 5]), np.array([2, 0, 1]), 5, 3) == m.SSM_ERR_METADATA
+    assert m.check_metadata(np.array([0, 3, 2, 5]), np.array([2, 0, 1]), 5, 3) == m.SSM_ERR_METADATA
+    assert m.check_metadata(None, np.arange(300)[::-1], 0, 300) == m.SSM_OK       # decode, big
+    assert m.check_metadata(None, np.r_[np.arange(200), 7], 0, 300) == m.SSM_ERR_METADATA
+    assert m.lib().ssm_scan_check_metadata(2, 0, None, None, 4) == m.SSM_ERR_NULL
+
+
+@pytest.mark.parametrize("N", [1, 15, 16, 17, 64, 100, 128, 129, 256, 300, 512, 513, 1024])
+@pytest.mark.parametrize("decode", [False, True])
+def test_geometry(N, decode):
+    for aligned in (True, False):
+        g = m.geometry(64, 96, N, 8, 3, decode=decode, aligned=aligned)
+        R, E = g["lanes_per_row"], g["elems_per_lane"]
+        assert R * E >= N and 64 % R == 0
+        assert g["rows_per_block"] == 4 * 64 // R
+        assert g["blocks"] == 3 * 64 * -(-96 // g["rows_per_block"])
+        assert g["lds_bytes"] <= 160 * 1024
+        assert g["chunk_tokens"] == (1 if decode else g["chunk_tokens"])
+        assert g["vector_path"] == int(aligned and N % 4 == 0)
+
+
+def test_no_kernel_uses_scratch():
+    """Each lane's state array must stay in VGPRs: every kernel in the build's
+    resource report has ScratchSize 0."""
+    report = os.path.join(os.path.dirname(m.LIB_PATH), "libssmscan.resources.txt")
+    text = open(report).read()
+    names = re.findall(r"Function Name: (\S+)", text)
+    scratch = [int(v) for v in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
+    assert len(names) == 28 and len(scratch) == len(names)
+    assert all(v == 0 for v in scratch), dict(zip(names, scratch))
+
+
+def test_single_hip_runtime():
+    """The library shares torch's HIP runtime (one libamdhip64 mapped)."""
+    assert len(m.hip_runtimes_loaded()) == 1, m.hip_runtimes_loaded()
