@@ -101,6 +101,65 @@ def cpu_baseline_decode(case, seconds):
                       f"rows x 128 state, fp32, resuming), {el:.1f} s of CPU time"}
 
 
+def _timed(fn, n, stream):
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def profile_mode(args, dev, stream):
+    """One kernel kind, eager launches, for counter runs: every dispatch of the
+    named kernel is the workload of the headline (decode) or of the prefill."""
+    import torch
+
+    import mamba2_selective_scan_amd as ssm
+    import ssm_inputs
+    out = {"mode": args.mode}
+    if args.mode == "copy":
+        n = 256 * 1024 * 1024 // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        ms = _timed(lambda i: dst.copy_(src), args.steps, stream)
+        out.update(bytes_read=4 * n, bytes_written=4 * n, ms=ms,
+                   GBs=2 * 4 * n / (ms * 1e-3) / 1e9)
+    elif args.mode == "decode":
+        case = ssm_inputs.workload("decode16", sets=SLOT_SETS)
+        d = ssm.to_device(case, dev)
+        sets = [torch.arange(k * DECODE_SEQS, (k + 1) * DECODE_SEQS, dtype=torch.int32,
+                             device=dev) for k in range(SLOT_SETS)]
+        y = torch.empty((DECODE_SEQS, H, P), dtype=torch.float32, device=dev)
+
+        def step(i):
+            ssm.decode(d["x"], d["dt"], d["A"], d["B"], d["C"], d["state"],
+                       sets[i % SLOT_SETS], d["fresh"], y=y)
+        for i in range(args.warmup):
+            step(i)
+        ms = _timed(step, args.steps, stream)
+        out.update(algorithmic_bytes=decode_bytes(), ms_per_launch_eager=ms)
+    else:
+        pc = ssm_inputs.workload("prefill4096")
+        pd = ssm.to_device(pc, dev)
+        py = torch.empty((PREFILL_T, H, P), dtype=torch.float32, device=dev)
+
+        def once(i):
+            ssm.prefill(pd["x"], pd["dt"], pd["A"], pd["B"], pd["C"], pd["state"],
+                        pd["cu_seqlens"], pd["slot"], pd["fresh"], y=py)
+        for i in range(args.warmup):
+            once(i)
+        ms = _timed(once, args.steps, stream)
+        out.update(algorithmic_bytes=prefill_bytes(), algorithmic_flops=prefill_flops(),
+                   ms_per_launch=ms)
+    out["kernel_hash"] = kernel_source_hash()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +170,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--mode", choices=("all", "decode", "prefill", "copy"), default="all",
+                    help="decode/prefill: launch only that kernel, eagerly, and print its "
+                         "timing (for counter runs); copy: a plain 256 MiB device copy, the "
+                         "reference for scaling HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -128,6 +191,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+
+    if args.mode != "all":
+        profile_mode(args, dev, stream)
+        return
 
     # ---------------- decode 16x1, 16 rotating slot sets
     case = ssm_inputs.workload("decode16", sets=SLOT_SETS)

@@ -93,32 +93,30 @@ struct Shape {
     static_assert(RB % 4 == 0, "rows per block must be a multiple of 4");
 
     static constexpr int lds_floats(bool decode, bool vec) {
-        const int staging = (decode ? 1 : 2) * BUF;
+        const int staging = decode ? 0 : 2 * BUF;   // decode reads its one token from global
         return (!vec && TILE > staging) ? TILE : staging;
     }
 };
 
-__device__ __forceinline__ float dpp_quad_xor1(float v) {   // quad_perm [1,0,3,2]
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+// DPP lane permutations within a 16-lane row.  `old` = 0 is the identity of
+// the add that consumes them, which lets the backend fuse each into v_add_f32_dpp.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float dpp_quad_xor2(float v) {   // quad_perm [2,3,0,1]
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_half_mirror(float v) { // lane l <- lane 7-l within 8
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_mirror(float v) {      // lane l <- lane 15-l within 16
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
-}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;   // lane l <- lane 7-l within 8
+constexpr int kMirror = 0x140;       // lane l <- lane 15-l within 16
 
 // Sum over the R adjacent lanes that hold one row.  Every step adds a value
 // and its partner's (commutative), so all R lanes end with identical bits.
 template <int R>
 __device__ __forceinline__ float row_allreduce(float v) {
-    v += dpp_quad_xor1(v);
-    v += dpp_quad_xor2(v);
-    if constexpr (R >= 8) v += dpp_half_mirror(v);
-    if constexpr (R >= 16) v += dpp_mirror(v);
+    v += dpp<kQuadXor1>(v);
+    v += dpp<kQuadXor2>(v);
+    if constexpr (R >= 8) v += dpp<kHalfMirror>(v);
+    if constexpr (R >= 16) v += dpp<kMirror>(v);
     if constexpr (R >= 32) v += __shfl_xor(v, 16, 64);
     if constexpr (R >= 64) v += __shfl_xor(v, 32, 64);
     return v;
@@ -140,6 +138,36 @@ __device__ __forceinline__ f4 load4(const float *p, int n_valid) {
 }
 
 __device__ __forceinline__ int clamp4(int v) { return v < 0 ? 0 : (v > 4 ? 4 : v); }
+
+// One token of the recurrence for the lane's E = 4J state elements, given the
+// lane's J 4-groups of B and C for the token.  Returns the lane's partial y.
+// Prefill and decode both go through here, so their arithmetic is identical.
+template <int J>
+__device__ __forceinline__ float update_token(float (&h)[4 * J], const f4 (&b)[J], const f4 (&c)[J],
+                                              float dA, float x_dt) {
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        float *hj = h + 4 * j;
+        hj[0] = hj[0] * dA + b[j].x * x_dt;
+        hj[1] = hj[1] * dA + b[j].y * x_dt;
+        hj[2] = hj[2] * dA + b[j].z * x_dt;
+        hj[3] = hj[3] * dA + b[j].w * x_dt;
+        acc0 += hj[0] * c[j].x;
+        acc1 += hj[1] * c[j].y;
+        acc0 += hj[2] * c[j].z;
+        acc1 += hj[3] * c[j].w;
+    }
+    return acc0 + acc1;
+}
+
+// The lane's J 4-groups of one token's B (or C) row in LDS; p points at the
+// lane's first group, groups are 4*R floats apart.
+template <int R, int J>
+__device__ __forceinline__ void lds_groups(f4 (&v)[J], const float *p) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) v[j] = *reinterpret_cast<const f4 *>(p + 4 * R * j);
+}
 
 template <class S, bool VEC, bool DECODE>
 __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
@@ -209,134 +237,169 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                 h[4 * j + 2] = nv > 2 ? v.z : 0.f;
                 h[4 * j + 3] = nv > 3 ? v.w : 0.f;
             }
-            __syncthreads();                        // the tile area is reused for staging
+            __syncthreads();                        // the tile area is reused below
         }
     }
 
-    // ---- chunk staging: global -> registers -> LDS
-    f4 pb[S::U_BC], pc[S::U_BC], px[S::U_X];
-    float pdt = 0.f;
+    if constexpr (DECODE) {
+        // One token: read the lane's slices of B and C, its row's x and the
+        // head's dt straight into registers; no LDS and no barrier.
+        const int64_t bc = (int64_t(s) * G + g) * N;
+        f4 bl[J], cl[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int n0 = 4 * (j * R + r);
+            const int nv = clamp4(N - n0);
+            bl[j] = load4<VEC>(a.B + bc + n0, nv);
+            cl[j] = load4<VEC>(a.C + bc + n0, nv);
+        }
+        const float dt = a.dt[int64_t(s) * H + hd];
+        const float x = row_ok ? a.x[(int64_t(s) * H + hd) * P + p0 + i] : 0.f;
+        const float dA = expf(dt * A_h);
+        const float yv = row_allreduce<R>(update_token<J>(h, bl, cl, dA, x * dt));
+        if (r == 0 && row_ok) a.y[(int64_t(s) * H + hd) * P + p0 + i] = yv;
+    } else {
+        // All state loads are complete before the chunk pipeline starts, so the
+        // token loop never waits on the next chunk's prefetch.
+        __builtin_amdgcn_s_waitcnt(0);
 
-    auto issue_loads = [&](int t0, int nt) {
-#pragma unroll
-        for (int u = 0; u < S::U_BC; ++u) {
-            const int q = u * kThreads + tid;                 // unit = (token, 4-group)
-            const int tt = q / (NP / 4);
-            const int n0 = 4 * (q - tt * (NP / 4));
-            const bool ok = (q < CT * NP / 4) && (tt < nt);
-            const int64_t off = (int64_t(t0 + tt) * G + g) * N + n0;
-            const int nv = ok ? clamp4(N - n0) : 0;
-            pb[u] = load4<VEC>(a.B + off, nv);
-            pc[u] = load4<VEC>(a.C + off, nv);
-        }
-#pragma unroll
-        for (int u = 0; u < S::U_X; ++u) {
-            const int q = u * kThreads + tid;                 // unit = (token, 4 rows)
-            const int tt = q / (RB / 4);
-            const int pi = 4 * (q - tt * (RB / 4));
-            const bool ok = (q < CT * RB / 4) && (tt < nt);
-            const int nv = ok ? clamp4(rows_valid - pi) : 0;
-            px[u] = load4<VEC>(a.x + (int64_t(t0 + tt) * H + hd) * P + p0 + pi, nv);
-        }
-        pdt = (tid < nt) ? a.dt[int64_t(t0 + tid) * H + hd] : 0.f;
-    };
+        // ---- chunk staging: global -> registers -> LDS
+        f4 pb[S::U_BC], pc[S::U_BC], px[S::U_X];
+        float pdt = 0.f;
 
-    auto commit = [&](int buf) {
-        float *base = lds + buf * S::BUF;
-        f4 *Bs4 = reinterpret_cast<f4 *>(base + S::OFF_B);
-        f4 *Cs4 = reinterpret_cast<f4 *>(base + S::OFF_C);
-        f4 *Xs4 = reinterpret_cast<f4 *>(base + S::OFF_X);
+        auto issue_loads = [&](int t0, int nt) {
 #pragma unroll
-        for (int u = 0; u < S::U_BC; ++u) {
-            const int q = u * kThreads + tid;
-            if (q < CT * NP / 4) { Bs4[q] = pb[u]; Cs4[q] = pc[u]; }
-        }
-#pragma unroll
-        for (int u = 0; u < S::U_X; ++u) {
-            const int q = u * kThreads + tid;
-            if (q < CT * RB / 4) Xs4[q] = px[u];
-        }
-        if (tid < CT) {
-            base[S::OFF_DT + tid] = pdt;
-            base[S::OFF_DA + tid] = expf(pdt * A_h);
-        }
-    };
-
-    auto compute = [&](int buf, int nt) {
-        const float *base = lds + buf * S::BUF;
-        const float *Bs = base + S::OFF_B;
-        const float *Cs = base + S::OFF_C;
-        const float *Xs = base + S::OFF_X;
-        float *Ys = lds + buf * S::BUF + S::OFF_Y;
-        // Lane r of a row keeps y of every token tt with tt % R == r and writes
-        // them out once per R tokens: one LDS store per R tokens, distinct
-        // addresses, no per-token lane masking.
-        float y_keep = 0.f;
-        for (int tt = 0; tt < nt; ++tt) {
-            const float dA = base[S::OFF_DA + tt];
-            const float x_dt = Xs[tt * RB + i] * base[S::OFF_DT + tt];
-            float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const int n0 = 4 * (j * R + r);
-                const f4 b = *reinterpret_cast<const f4 *>(Bs + tt * NP + n0);
-                const f4 c = *reinterpret_cast<const f4 *>(Cs + tt * NP + n0);
-                float *hj = h + 4 * j;
-                hj[0] = hj[0] * dA + b.x * x_dt;
-                hj[1] = hj[1] * dA + b.y * x_dt;
-                hj[2] = hj[2] * dA + b.z * x_dt;
-                hj[3] = hj[3] * dA + b.w * x_dt;
-                acc0 += hj[0] * c.x;
-                acc1 += hj[1] * c.y;
-                acc0 += hj[2] * c.z;
-                acc1 += hj[3] * c.w;
+            for (int u = 0; u < S::U_BC; ++u) {
+                const int q = u * kThreads + tid;                 // unit = (token, 4-group)
+                const int tt = q / (NP / 4);
+                const int n0 = 4 * (q - tt * (NP / 4));
+                const bool ok = (q < CT * NP / 4) && (tt < nt);
+                const int64_t off = (int64_t(t0 + tt) * G + g) * N + n0;
+                const int nv = ok ? clamp4(N - n0) : 0;
+                pb[u] = load4<VEC>(a.B + off, nv);
+                pc[u] = load4<VEC>(a.C + off, nv);
             }
-            const float yv = row_allreduce<R>(acc0 + acc1);
-            const int slot_r = tt % R;
-            y_keep = (r == slot_r) ? yv : y_keep;
-            if (slot_r == R - 1 || tt == nt - 1) {
-                const int tok = tt - slot_r + r;
-                if (tok <= tt) Ys[tok * RB + i] = y_keep;
-            }
-        }
-    };
-
-    auto flush_y = [&](int buf, int t0, int nt) {
-        const float *Ys = lds + buf * S::BUF + S::OFF_Y;
-        if constexpr (VEC) {
-            for (int q = tid; q < nt * (RB / 4); q += kThreads) {
+#pragma unroll
+            for (int u = 0; u < S::U_X; ++u) {
+                const int q = u * kThreads + tid;                 // unit = (token, 4 rows)
                 const int tt = q / (RB / 4);
                 const int pi = 4 * (q - tt * (RB / 4));
-                if (pi < rows_valid)
-                    *reinterpret_cast<f4 *>(a.y + (int64_t(t0 + tt) * H + hd) * P + p0 + pi) =
-                        *reinterpret_cast<const f4 *>(Ys + tt * RB + pi);
+                const bool ok = (q < CT * RB / 4) && (tt < nt);
+                const int nv = ok ? clamp4(rows_valid - pi) : 0;
+                px[u] = load4<VEC>(a.x + (int64_t(t0 + tt) * H + hd) * P + p0 + pi, nv);
             }
-        } else {
-            for (int q = tid; q < nt * RB; q += kThreads) {
-                const int tt = q / RB;
-                const int pi = q - tt * RB;
-                if (pi < rows_valid) a.y[(int64_t(t0 + tt) * H + hd) * P + p0 + pi] = Ys[tt * RB + pi];
-            }
-        }
-    };
+            pdt = (tid < nt) ? a.dt[int64_t(t0 + tid) * H + hd] : 0.f;
+        };
 
-    // ---- token loop, chunk by chunk
-    const int n_chunks = (n_tok + CT - 1) / CT;
-    if (n_chunks > 0) {
-        issue_loads(t_begin, min(CT, n_tok));
-        commit(0);
-    }
-    __syncthreads();
-    for (int c = 0; c < n_chunks; ++c) {
-        const int buf = DECODE ? 0 : (c & 1);
-        const int t0 = t_begin + c * CT;
-        const int nt = min(CT, t_end - t0);
-        const bool has_next = !DECODE && (c + 1 < n_chunks);
-        if (has_next) issue_loads(t0 + CT, min(CT, t_end - t0 - CT));
-        compute(buf, nt);
-        if (has_next) commit(buf ^ 1);
+        auto commit = [&](int buf) {
+            float *base = lds + buf * S::BUF;
+            f4 *Bs4 = reinterpret_cast<f4 *>(base + S::OFF_B);
+            f4 *Cs4 = reinterpret_cast<f4 *>(base + S::OFF_C);
+            f4 *Xs4 = reinterpret_cast<f4 *>(base + S::OFF_X);
+#pragma unroll
+            for (int u = 0; u < S::U_BC; ++u) {
+                const int q = u * kThreads + tid;
+                if (q < CT * NP / 4) { Bs4[q] = pb[u]; Cs4[q] = pc[u]; }
+            }
+#pragma unroll
+            for (int u = 0; u < S::U_X; ++u) {
+                const int q = u * kThreads + tid;
+                if (q < CT * RB / 4) Xs4[q] = px[u];
+            }
+            if (tid < CT) {
+                base[S::OFF_DT + tid] = pdt;
+                base[S::OFF_DA + tid] = expf(pdt * A_h);
+            }
+        };
+
+        // Tokens go in groups of KY.  Every lane of a row ends a token with the
+        // row's y; lane r keeps the y of the group's token r % KY and stores it
+        // once per group, so the per-token cost is one select.  Inside a group
+        // the token index is a compile-time constant: LDS offsets fold into the
+        // instructions and the keep-select needs no runtime compare.
+        constexpr int KY = R < 16 ? R : 16;
+        const int rk = r % KY;
+        auto compute = [&](int buf, int nt) {
+            const float *base = lds + buf * S::BUF;
+            const float *Bl = base + S::OFF_B + 4 * r;
+            const float *Cl = base + S::OFF_C + 4 * r;
+            const float *Xl = base + S::OFF_X + i;
+            const float *Dt = base + S::OFF_DT;
+            const float *Da = base + S::OFF_DA;
+            float *Ys = lds + buf * S::BUF + S::OFF_Y + i;
+            float y_keep = 0.f;
+            int t0 = 0;
+            for (; t0 + KY <= nt; t0 += KY) {
+#pragma unroll
+                for (int kk = 0; kk < KY; ++kk) {
+                    const int tt = t0 + kk;
+                    f4 bv[J], cv[J];
+                    lds_groups<R, J>(bv, Bl + tt * NP);
+                    lds_groups<R, J>(cv, Cl + tt * NP);
+                    const float yv =
+                        row_allreduce<R>(update_token<J>(h, bv, cv, Da[tt], Xl[tt * RB] * Dt[tt]));
+                    y_keep = (rk == kk) ? yv : y_keep;
+                }
+                Ys[(t0 + rk) * RB] = y_keep;
+            }
+            if (t0 < nt) {
+                for (int tt = t0; tt < nt; ++tt) {
+                    f4 bv[J], cv[J];
+                    lds_groups<R, J>(bv, Bl + tt * NP);
+                    lds_groups<R, J>(cv, Cl + tt * NP);
+                    const float yv =
+                        row_allreduce<R>(update_token<J>(h, bv, cv, Da[tt], Xl[tt * RB] * Dt[tt]));
+                    y_keep = (rk == tt - t0) ? yv : y_keep;
+                }
+                if (rk < nt - t0) Ys[(t0 + rk) * RB] = y_keep;
+            }
+        };
+
+        auto flush_y = [&](int buf, int t0, int nt) {
+            const float *Ys = lds + buf * S::BUF + S::OFF_Y;
+            if constexpr (VEC) {
+                for (int q = tid; q < nt * (RB / 4); q += kThreads) {
+                    const int tt = q / (RB / 4);
+                    const int pi = 4 * (q - tt * (RB / 4));
+                    if (pi < rows_valid)
+                        *reinterpret_cast<f4 *>(a.y + (int64_t(t0 + tt) * H + hd) * P + p0 + pi) =
+                            *reinterpret_cast<const f4 *>(Ys + tt * RB + pi);
+                }
+            } else {
+                for (int q = tid; q < nt * RB; q += kThreads) {
+                    const int tt = q / RB;
+                    const int pi = q - tt * RB;
+                    if (pi < rows_valid) a.y[(int64_t(t0 + tt) * H + hd) * P + p0 + pi] = Ys[tt * RB + pi];
+                }
+            }
+        };
+
+        // ---- token loop, chunk by chunk, double-buffered.  Chunk c's y tile is
+        // written out during chunk c+1, after that chunk's prefetch is issued and
+        // before its token loop: the stores then drain under the compute, and
+        // the registers that carried them are free again by the time they are
+        // reused (vector-memory counters on this chip count stores too).
+        const int n_chunks = (n_tok + CT - 1) / CT;
+        if (n_chunks > 0) {
+            issue_loads(t_begin, min(CT, n_tok));
+            commit(0);
+        }
         __syncthreads();
-        flush_y(buf, t0, nt);
+        for (int c = 0; c < n_chunks; ++c) {
+            const int buf = c & 1;
+            const int t0 = t_begin + c * CT;
+            const int nt = min(CT, t_end - t0);
+            const bool has_next = c + 1 < n_chunks;
+            if (has_next) issue_loads(t0 + CT, min(CT, t_end - t0 - CT));
+            if (c > 0) flush_y(buf ^ 1, t0 - CT, CT);    // previous chunk, always full
+            compute(buf, nt);
+            if (has_next) commit(buf ^ 1);
+            __syncthreads();
+        }
+        if (n_chunks > 0) {
+            const int c = n_chunks - 1;
+            flush_y(c & 1, t_begin + c * CT, n_tok - c * CT);
+        }
     }
 
     // ---- registers -> state slot
@@ -350,7 +413,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
             }
         }
     } else {
-        __syncthreads();                             // last chunk's y tile may overlap the state tile
+        __syncthreads();                             // the last y tile may overlap the state tile
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int n0 = 4 * (j * R + r);
