@@ -53,12 +53,22 @@ def prefill_flops(T=PREFILL_T):
 
 
 def kernel_source_hash():
+    """Hash of what determines the kernels' machine code: the HIP sources and
+    the C header with comments and whitespace removed, and the hipcc flags.
+    Counter results are tied to it, so they stop counting once the code
+    changes, but not when only a comment does."""
+    import re
     h = hashlib.sha256()
     for rel in ("mamba2_selective_scan_amd/csrc/scan_kernel.hpp",
-                "mamba2_selective_scan_amd/csrc/ssm_scan.hip",
-                "mamba2_selective_scan_amd/build.py", "include/ssm_scan.h"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+                "mamba2_selective_scan_amd/csrc/ssm_scan.hip", "include/ssm_scan.h"):
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    with open(os.path.join(ROOT, "mamba2_selective_scan_amd", "build.py")) as f:
+        flags = re.search(r"FLAGS = \[(.*?)\]", f.read(), re.S).group(1)
+    h.update(" ".join(flags.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -129,6 +139,24 @@ def profile_mode(args, dev, stream):
         ms = _timed(lambda i: dst.copy_(src), args.steps, stream)
         out.update(bytes_read=4 * n, bytes_written=4 * n, ms=ms,
                    GBs=2 * 4 * n / (ms * 1e-3) / 1e9)
+    elif args.mode == "copy16":
+        n = DECODE_SEQS * H * P * N
+        src = [torch.randn(n, device=dev) for _ in range(SLOT_SETS)]
+        dst = [torch.empty_like(src[0]) for _ in range(SLOT_SETS)]
+
+        def rot():
+            for k in range(SLOT_SETS):
+                dst[k].copy_(src[k])
+        rot()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            rot()
+        for _ in range(2):
+            graph.replay()
+        ms = _timed(lambda i: graph.replay(), max(1, args.steps // SLOT_SETS), stream) / SLOT_SETS
+        out.update(bytes_per_copy=2 * 4 * n, us_per_copy=ms * 1e3,
+                   GBs=2 * 4 * n / (ms * 1e-3) / 1e9)
     elif args.mode == "decode":
         case = ssm_inputs.workload("decode16", sets=SLOT_SETS)
         d = ssm.to_device(case, dev)
@@ -170,10 +198,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--mode", choices=("all", "decode", "prefill", "copy"), default="all",
+    ap.add_argument("--mode", choices=("all", "decode", "prefill", "copy", "copy16"),
+                    default="all",
                     help="decode/prefill: launch only that kernel, eagerly, and print its "
                          "timing (for counter runs); copy: a plain 256 MiB device copy, the "
-                         "reference for scaling HBM byte counters")
+                         "reference for scaling HBM byte counters; copy16: device copies of "
+                         "one decode step's state size over 16 rotating buffers, replayed "
+                         "from a HIP graph like the decode bench (achievable-bandwidth "
+                         "reference)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -10,7 +10,7 @@
  *
  * with g = h / (n_heads / n_groups): heads share B and C by contiguous group.
  * This is the recurrence of ggml's CPU scan and of its rewritten Mamba2 group
- * kernel ("the-llama-journey", Day 12 operand table and loop nest, Day 14
+ * kernel ("The llama journey", Day 12 operand table and loop nest, Day 14
  * kernel), over a batch that mixes sequences starting from zero with
  * sequences resuming from their state slot ("perf(cuda): keep the Mamba2 scan
  * state in registers, stage tokens by chunk #90", What changes and Testing).

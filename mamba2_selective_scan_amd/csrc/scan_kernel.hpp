@@ -4,7 +4,7 @@
 // (four 64-wide wavefronts) owns one (sequence, head, run of RB head-dim rows)
 // and walks that sequence's tokens in order.  Per token and row it computes
 //     dA = exp(dt*A[h]);  st[n] = st[n]*dA + B[n]*(x*dt);  y = sum_n st[n]*C[n]
-// -- the recurrence of ggml's Mamba2 group kernel ("the-llama-journey", Day 14)
+// -- the recurrence of ggml's Mamba2 group kernel ("The llama journey", Day 14)
 // with the state kept in registers and a row split over adjacent lanes, as in
 // "perf(cuda): keep the Mamba2 scan state in registers, stage tokens by chunk
 // #90" (What changes).  Where this layout departs from that page's CUDA one:
@@ -25,13 +25,16 @@
 //    (quad_perm, row_half_mirror, row_mirror; a lane shuffle only past 16
 //    lanes).  Every lane of the row ends with the same sum, so no barrier and
 //    no atomic is needed per token.
-//  * B, C, x and dt of CT tokens are staged in LDS per chunk, double-buffered:
+//  * Prefill: B, C, x and dt of CT tokens are staged in LDS per chunk, double-buffered:
 //    the next chunk's global loads are issued into registers before the
 //    current chunk is computed and written to the other buffer after it, so
 //    there is one barrier per chunk.  dA = exp(dt*A) is computed once per
 //    token at staging time, not per lane.  y of the chunk is collected in an
 //    LDS tile (each lane keeps the y of every R-th token in a register and
-//    stores it once per R tokens) and written out coalesced after the barrier.
+//    stores it once per group of tokens) and written out coalesced during the
+//    next chunk.
+//  * Decode (one token per sequence) reads the lane's B/C groups, x and dt
+//    straight into registers: no LDS, no barrier.
 //  * The grid is one-dimensional.  Workgroup ids are remapped so that the
 //    blocks the hardware sends to one XCD (id % 8) are consecutive in
 //    (sequence, head, row-block) order: heads of one B/C group share an L2.

@@ -20,20 +20,24 @@ using ssm::ScanArgs;
 using ssm::Shape;
 
 // One row of the shape table: state sizes up to n_max use R lanes per row,
-// J float4 groups per lane and CT tokens per prefill chunk.  R lanes hold
-// 4*R*J >= N elements; the table keeps E = 4J at 4..16 registers and the
-// double-buffered staging under ~80 KB of the 160 KB LDS.
+// J float4 groups per lane and CT tokens per chunk for prefill, and DR lanes
+// with DJ groups per lane for decode.  R lanes hold 4*R*J >= N elements.
+// Prefill keeps E = 4J at 4..16 registers and the double-buffered staging
+// under ~80 KB of the 160 KB LDS.  Decode is one pass over the state, so it
+// favours more float4 loads in flight per lane (measured on MI355X at
+// N = 128: 8 lanes x 16 elements beat 16 x 8 by 3%, 32 x 4 and 4 x 32 lost
+// 12-17%).
 struct ShapeRow {
-    int n_max, R, J, CT;
+    int n_max, R, J, CT, DR, DJ;
 };
 constexpr ShapeRow kShapes[] = {
-    {16, 4, 1, 32},
-    {32, 8, 1, 32},
-    {64, 16, 1, 32},
-    {128, 16, 2, 32},
-    {256, 16, 4, 16},
-    {512, 32, 4, 8},
-    {1024, 64, 4, 4},
+    {16, 4, 1, 32, 4, 1},
+    {32, 8, 1, 32, 8, 1},
+    {64, 16, 1, 32, 16, 1},
+    {128, 16, 2, 32, 8, 4},
+    {256, 16, 4, 16, 16, 4},
+    {512, 32, 4, 8, 32, 4},
+    {1024, 64, 4, 4, 64, 4},
 };
 static_assert(kShapes[sizeof(kShapes) / sizeof(kShapes[0]) - 1].n_max == SSM_SCAN_MAX_D_STATE,
               "the table must cover every supported state size");
@@ -78,17 +82,17 @@ int launch(const ScanArgs &a, hipStream_t stream) {
     return err == hipSuccess ? SSM_OK : hip_fail(err, SSM_ERR_LAUNCH);
 }
 
-// Calls f.template run<R, J, CT>() for the table row (the row's compile-time shape).
+// Calls f.template run<R, J, CT, DR, DJ>() for the table row (its compile-time shapes).
 template <class F>
 int with_row(const ShapeRow &row, F &&f) {
     switch (row.n_max) {
-    case 16: return f.template run<4, 1, 32>();
-    case 32: return f.template run<8, 1, 32>();
-    case 64: return f.template run<16, 1, 32>();
-    case 128: return f.template run<16, 2, 32>();
-    case 256: return f.template run<16, 4, 16>();
-    case 512: return f.template run<32, 4, 8>();
-    case 1024: return f.template run<64, 4, 4>();
+    case 16: return f.template run<4, 1, 32, 4, 1>();
+    case 32: return f.template run<8, 1, 32, 8, 1>();
+    case 64: return f.template run<16, 1, 32, 16, 1>();
+    case 128: return f.template run<16, 2, 32, 8, 4>();
+    case 256: return f.template run<16, 4, 16, 16, 4>();
+    case 512: return f.template run<32, 4, 8, 32, 4>();
+    case 1024: return f.template run<64, 4, 4, 64, 4>();
     default: return SSM_ERR_UNSUPPORTED;
     }
 }
@@ -97,11 +101,11 @@ struct Launch {
     const ScanArgs &a;
     bool vec, decode;
     hipStream_t stream;
-    template <int R, int J, int CT>
+    template <int R, int J, int CT, int DR, int DJ>
     int run() const {
         if (decode)
-            return vec ? launch<Shape<R, J, 1>, true, true>(a, stream)
-                       : launch<Shape<R, J, 1>, false, true>(a, stream);
+            return vec ? launch<Shape<DR, DJ, 1>, true, true>(a, stream)
+                       : launch<Shape<DR, DJ, 1>, false, true>(a, stream);
         return vec ? launch<Shape<R, J, CT>, true, false>(a, stream)
                    : launch<Shape<R, J, CT>, false, false>(a, stream);
     }
@@ -109,12 +113,22 @@ struct Launch {
 
 struct LdsBytes {
     bool vec, decode;
-    template <int R, int J, int CT>
+    template <int R, int J, int CT, int DR, int DJ>
     int run() const {
-        return int(sizeof(float)) * (decode ? Shape<R, J, 1>::lds_floats(true, vec)
+        return int(sizeof(float)) * (decode ? Shape<DR, DJ, 1>::lds_floats(true, vec)
                                             : Shape<R, J, CT>::lds_floats(false, vec));
     }
 };
+
+// Lanes per row, elements per lane and rows per workgroup of a call.
+struct Geo {
+    int R, E, RB, CT;
+};
+Geo geo_for(const ShapeRow &row, bool decode) {
+    const int R = decode ? row.DR : row.R;
+    const int J = decode ? row.DJ : row.J;
+    return Geo{R, 4 * J, ssm::kWaves * (64 / R), decode ? 1 : row.CT};
+}
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -134,7 +148,7 @@ int scan_common(const ssm_scan_dims *d, int32_t n_seqs, const int32_t *cu_seqlen
                 bool decode, void *stream) {
     const ShapeRow *row = shape_for(d->d_state);
     if (!row) return SSM_ERR_UNSUPPORTED;
-    const int RB = ssm::kWaves * (64 / row->R);
+    const int RB = geo_for(*row, decode).RB;
     const int64_t n_row_blocks = (int64_t(d->head_dim) + RB - 1) / RB;
     const int64_t n_blocks = int64_t(n_seqs) * d->n_heads * n_row_blocks;
     if (n_blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
@@ -265,14 +279,14 @@ int ssm_scan_query_geometry(const ssm_scan_dims *dims, int32_t n_seqs, int32_t d
     const ShapeRow *row = shape_for(dims->d_state);
     if (!row) return SSM_ERR_UNSUPPORTED;
     const bool vec = aligned16 && dims->d_state % 4 == 0 && dims->head_dim % 4 == 0;
-    const int RB = ssm::kWaves * (64 / row->R);
-    out->lanes_per_row = row->R;
-    out->elems_per_lane = 4 * row->J;
-    out->rows_per_block = RB;
-    out->chunk_tokens = decode ? 1 : row->CT;
+    const Geo geo = geo_for(*row, decode != 0);
+    out->lanes_per_row = geo.R;
+    out->elems_per_lane = geo.E;
+    out->rows_per_block = geo.RB;
+    out->chunk_tokens = geo.CT;
     out->threads_per_block = kThreads;
     out->lds_bytes = with_row(*row, LdsBytes{vec, decode != 0});
-    out->blocks = int64_t(n_seqs) * dims->n_heads * ((int64_t(dims->head_dim) + RB - 1) / RB);
+    out->blocks = int64_t(n_seqs) * dims->n_heads * ((int64_t(dims->head_dim) + geo.RB - 1) / geo.RB);
     out->vector_path = vec ? 1 : 0;
     return SSM_OK;
 }

@@ -7,10 +7,10 @@
  * library and the GPU library never calls it.
  *
  * What it computes (the definition, written out):
- *   "the-llama-journey", Day 12: ggml's CPU reference loops over sequences,
+ *   "The llama journey", Day 12: ggml's CPU reference loops over sequences,
  *   then tokens, then heads, then head-dim rows, then state elements, updates
  *   each state element and reads y out as the row's dot product with C.
- *   "the-llama-journey", Day 14 (the rewritten group kernel): per token the
+ *   "The llama journey", Day 14 (the rewritten group kernel): per token the
  *   decay is exp(dt * A[head]) with one scalar A per head, x is scaled by dt,
  *   each state element becomes state * dA + B * (x * dt), y sums state * C
  *   over the state index using the state *after* the update, and heads map to

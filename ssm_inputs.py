@@ -6,7 +6,7 @@ scan's arithmetic.  Both the CPU oracle (through the tests) and the GPU path
 here, so the two sides see identical input bits.
 
 Shapes follow the operand table of ggml's CPU scan as transcribed on
-"the-llama-journey" (Day 12, the src0..src6 table): state [slot][head][row][n],
+"The llama journey" (Day 12, the src0..src6 table): state [slot][head][row][n],
 x [token][head][row], dt [token][head], A [head] (one scalar per head for
 Mamba2), B and C [token][group][n].  Tokens of all sequences are packed one
 after another; ``cu_seqlens`` gives where each sequence starts.

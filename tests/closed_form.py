@@ -2,7 +2,7 @@
 
 None of this calls the oracle or the GPU library.  The brute-force form is the
 recurrence unrolled, which the benchmark spec of the scan and the
-recurrence on "the-llama-journey" (Day 14) imply: for one (sequence, head),
+recurrence on "The llama journey" (Day 14) imply: for one (sequence, head),
 with a_k = exp(dt_k * A), u_k = dt_k * x_k and tokens k = 1..t,
 
     h_t = (prod_{r=1..t} a_r) h_0 + sum_{j=1..t} (prod_{r=j+1..t} a_r) u_j (x) B_j

@@ -51,8 +51,11 @@ def test_workload_decode_entry(ssm, orc, name):
     y32, st32 = orc.scan_case(case, precision="f32")
     assert_parity(case, y, st, y32, st32, label=f"{name} decode entry")
     yp, stp = run_gpu(case, "prefill")
-    assert np.array_equal(y, yp) and np.array_equal(st, stp), \
-        "decode and one-token prefill differ"
+    # The state update is elementwise and identical in both entry points; y
+    # may differ in the last bits because decode splits a row over fewer lanes
+    # (a different summation tree).
+    assert np.array_equal(st, stp), "decode and one-token prefill states differ"
+    assert rel_err(y, yp) <= TOL
 
 
 def test_decode_bench_launch_configuration(ssm, orc):
