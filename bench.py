@@ -175,10 +175,17 @@ def profile_mode(args, dev, stream):
         pc = ssm_inputs.workload("prefill4096")
         pd = ssm.to_device(pc, dev)
         py = torch.empty((PREFILL_T, H, P), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, ssm.workspace_size(H, P, N, G, 1, PREFILL_T, PREFILL_T)),
+                         dtype=torch.uint8, device=dev)
 
         def once(i):
-            ssm.prefill(pd["x"], pd["dt"], pd["A"], pd["B"], pd["C"], pd["state"],
-                        pd["cu_seqlens"], pd["slot"], pd["fresh"], y=py)
+            if args.mode == "prefill":
+                ssm.prefill_ws(pd["x"], pd["dt"], pd["A"], pd["B"], pd["C"], pd["state"],
+                               pd["cu_seqlens"], pd["slot"], pd["fresh"], PREFILL_T,
+                               workspace=ws, y=py)
+            else:
+                ssm.prefill(pd["x"], pd["dt"], pd["A"], pd["B"], pd["C"], pd["state"],
+                            pd["cu_seqlens"], pd["slot"], pd["fresh"], y=py)
         for i in range(args.warmup):
             once(i)
         ms = _timed(once, args.steps, stream)
@@ -198,9 +205,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--mode", choices=("all", "decode", "prefill", "copy", "copy16"),
+    ap.add_argument("--mode", choices=("all", "decode", "prefill", "prefill1", "copy", "copy16"),
                     default="all",
-                    help="decode/prefill: launch only that kernel, eagerly, and print its "
+                    help="decode/prefill: launch only that path (prefill: the time-split path; "
+                         "prefill1: the unsplit single kernel), eagerly, and print its "
                          "timing (for counter runs); copy: a plain 256 MiB device copy, the "
                          "reference for scaling HBM byte counters; copy16: device copies of "
                          "one decode step's state size over 16 rotating buffers, replayed "
@@ -291,35 +299,52 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
 
-    # ---------------- prefill 1x4096, fresh
+    # ---------------- prefill 1x4096, fresh.  One sequence fills only a quarter
+    # of the SIMDs, so the library splits it over time (ssm_scan_prefill_ws,
+    # automatic plan); the unsplit single-pass time is reported beside it.
     if not args.no_prefill:
         pc = ssm_inputs.workload("prefill4096")
         pd = ssm.to_device(pc, dev)
         py = torch.empty((PREFILL_T, H, P), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, ssm.workspace_size(H, P, N, G, 1, PREFILL_T, PREFILL_T)),
+                         dtype=torch.uint8, device=dev)
 
-        def prefill_once():
+        def prefill_split():
+            ssm.prefill_ws(pd["x"], pd["dt"], pd["A"], pd["B"], pd["C"], pd["state"],
+                           pd["cu_seqlens"], pd["slot"], pd["fresh"], PREFILL_T,
+                           workspace=ws, y=py)
+
+        def prefill_unsplit():
             ssm.prefill(pd["x"], pd["dt"], pd["A"], pd["B"], pd["C"], pd["state"],
                         pd["cu_seqlens"], pd["slot"], pd["fresh"], y=py)
 
-        for _ in range(args.prefill_warmup):
-            prefill_once()
-        torch.cuda.synchronize()
-        times = []
-        for _ in range(args.prefill_steps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            prefill_once()
-            b.record(stream)
-            times.append((a, b))
-        torch.cuda.synchronize()
-        ms = [a.elapsed_time(b) for a, b in times]
+        def event_times(fn):
+            for _ in range(args.prefill_warmup):
+                fn()
+            torch.cuda.synchronize()
+            pairs = []
+            for _ in range(args.prefill_steps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                pairs.append((a, b))
+            torch.cuda.synchronize()
+            return [a.elapsed_time(b) for a, b in pairs]
+
+        ms = event_times(prefill_split)
+        ms_unsplit = event_times(prefill_unsplit)
         pf_ms = float(np.mean(ms))
         tflops = prefill_flops() / (pf_ms * 1e-3) / 1e12
         result["prefill"] = {
             "workload": "prefill 1 seq x 4096 tokens, fresh", "ms": round(pf_ms, 4),
             "ms_min": round(min(ms), 4), "ms_max": round(max(ms), 4),
             "iterations": args.prefill_steps,
-            "geometry": ssm.geometry(H, P, N, G, 1),
+            "path": "ssm_scan_prefill_ws, automatic time split: segment scans + combine + "
+                    "corrections (3 kernels)",
+            "plan": ssm.prefill_plan(H, P, N, G, 1, PREFILL_T),
+            "ms_unsplit": round(float(np.mean(ms_unsplit)), 4),
+            "geometry_unsplit": ssm.geometry(H, P, N, G, 1),
             "roofline": {"bound": "alu", "achieved": round(tflops, 3),
                          "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / FP32_VALU_PEAK_TFLOPS, 4),

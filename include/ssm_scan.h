@@ -43,6 +43,7 @@
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -94,6 +95,42 @@ int ssm_scan_prefill(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens
                      int32_t n_slots, float *y, void *stream);
 
 /*
+ * Prefill that may split long sequences over time, for batches too small to
+ * fill the GPU (few sequences, long prompts).  Same arguments and meaning as
+ * ssm_scan_prefill, plus:
+ *   max_seqlen      host-side upper bound on every sequence's length (a longer
+ *                   sequence is still scanned correctly, its last segment just
+ *                   runs to its end)
+ *   n_segments      0 = let the library decide, 1 = never split, k > 1 = cut
+ *                   each sequence into about k segments
+ *   workspace       device scratch of at least the size that
+ *                   ssm_scan_prefill_workspace_size() reports for the same
+ *                   arguments; owned by the caller, contents need no
+ *                   initialisation and are garbage afterwards.  With NULL or
+ *                   too small a workspace the call runs unsplit.
+ * A split sequence is scanned as segments in parallel (segment 0 from the true
+ * start state, later ones from zero); a second kernel chains the segments' end
+ * states, carry <- prod(dA over the segment) * carry + end, and writes the
+ * final state to the slot; a third adds each later segment's carried-in state
+ * to its y: y[t] += prod(dA from the segment start through t) * (C_t . carry).
+ * Real arithmetic equals the sequential recurrence exactly; in floating point
+ * only the association changes (the time-split form of the scan that "perf(cuda):
+ * keep the Mamba2 scan state in registers ... #90" leaves for later).
+ * Three kernels are enqueued on `stream`; no allocation, no synchronization.
+ */
+int ssm_scan_prefill_ws(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens,
+                        int32_t max_seqlen, int32_t n_segments, const int32_t *cu_seqlens,
+                        const int32_t *slot, const uint8_t *fresh, const float *x,
+                        const float *dt, const float *A, const float *B, const float *C,
+                        float *state, int32_t n_slots, float *y, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Workspace bytes ssm_scan_prefill_ws needs for these sizes (0 if it would not
+ * split).  Touches no device. */
+int ssm_scan_prefill_workspace_size(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens,
+                                    int32_t max_seqlen, int32_t n_segments, size_t *bytes);
+
+/*
  * Decode: one token for each of n_seqs sequences (token s belongs to sequence
  * s).  Identical in meaning to ssm_scan_prefill with every length equal to 1;
  * it exists so a decode step needs no cu_seqlens.
@@ -139,6 +176,8 @@ typedef struct ssm_scan_geometry {
     int32_t lds_bytes;         /* dynamic LDS per workgroup                         */
     int64_t blocks;            /* workgroups in the grid                            */
     int32_t vector_path;       /* 1 = float4 loads and stores; 0 = scalar + LDS tile */
+    int32_t segments;          /* time segments per sequence (1 = not split)        */
+    int32_t segment_tokens;    /* tokens per segment when split                      */
 } ssm_scan_geometry;
 
 /*
@@ -148,6 +187,11 @@ typedef struct ssm_scan_geometry {
  */
 int ssm_scan_query_geometry(const ssm_scan_dims *dims, int32_t n_seqs, int32_t decode,
                             int32_t aligned, ssm_scan_geometry *out);
+
+/* The geometry of the segment-scan kernel ssm_scan_prefill_ws would launch
+ * (segments = 1: it would run unsplit).  Touches no device. */
+int ssm_scan_query_prefill_plan(const ssm_scan_dims *dims, int32_t n_seqs, int32_t max_seqlen,
+                                int32_t n_segments, int32_t aligned, ssm_scan_geometry *out);
 
 #ifdef __cplusplus
 }

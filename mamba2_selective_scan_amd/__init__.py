@@ -63,7 +63,8 @@ class Geometry(ctypes.Structure):
     _fields_ = [("lanes_per_row", ctypes.c_int32), ("elems_per_lane", ctypes.c_int32),
                 ("rows_per_block", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
                 ("threads_per_block", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
-                ("blocks", ctypes.c_int64), ("vector_path", ctypes.c_int32)]
+                ("blocks", ctypes.c_int64), ("vector_path", ctypes.c_int32),
+                ("segments", ctypes.c_int32), ("segment_tokens", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -88,6 +89,15 @@ _lib.ssm_scan_check_metadata.restype = ctypes.c_int
 _lib.ssm_scan_query_geometry.argtypes = [ctypes.POINTER(Dims), _i32, _i32, _i32,
                                          ctypes.POINTER(Geometry)]
 _lib.ssm_scan_query_geometry.restype = ctypes.c_int
+_lib.ssm_scan_query_prefill_plan.argtypes = [ctypes.POINTER(Dims), _i32, _i32, _i32, _i32,
+                                             ctypes.POINTER(Geometry)]
+_lib.ssm_scan_query_prefill_plan.restype = ctypes.c_int
+_lib.ssm_scan_prefill_workspace_size.argtypes = [ctypes.POINTER(Dims), _i32, _i32, _i32, _i32,
+                                                 ctypes.POINTER(ctypes.c_size_t)]
+_lib.ssm_scan_prefill_workspace_size.restype = ctypes.c_int
+_lib.ssm_scan_prefill_ws.argtypes = ([ctypes.POINTER(Dims), _i32, _i32, _i32, _i32] + [_vp] * 9
+                                     + [_i32, _vp, _vp, ctypes.c_size_t, _vp])
+_lib.ssm_scan_prefill_ws.restype = ctypes.c_int
 
 
 class ScanError(RuntimeError):
@@ -131,6 +141,25 @@ def geometry(H, P, N, G, n_seqs, decode=False, aligned=True) -> dict:
                                         int(bool(decode)), int(bool(aligned)),
                                         ctypes.byref(out)), "ssm_scan_query_geometry")
     return out.as_dict()
+
+
+def prefill_plan(H, P, N, G, n_seqs, max_seqlen, segments=0, aligned=True) -> dict:
+    """Geometry of the segment scan ``prefill_ws`` would launch (segments == 1:
+    it would not split)."""
+    out = Geometry()
+    _check(_lib.ssm_scan_query_prefill_plan(ctypes.byref(Dims(H, P, N, G)), int(n_seqs),
+                                            int(max_seqlen), int(segments), int(bool(aligned)),
+                                            ctypes.byref(out)), "ssm_scan_query_prefill_plan")
+    return out.as_dict()
+
+
+def workspace_size(H, P, N, G, n_seqs, n_tokens, max_seqlen, segments=0) -> int:
+    """Bytes of device workspace ``prefill_ws`` needs (0: it would not split)."""
+    b = ctypes.c_size_t()
+    _check(_lib.ssm_scan_prefill_workspace_size(ctypes.byref(Dims(H, P, N, G)), int(n_seqs),
+                                                int(n_tokens), int(max_seqlen), int(segments),
+                                                ctypes.byref(b)), "ssm_scan_prefill_workspace_size")
+    return int(b.value)
 
 
 def check_metadata(cu_seqlens, slot, n_tokens: int, n_slots: int) -> int:
@@ -207,6 +236,47 @@ def prefill(x, dt, A, B, C, state, cu_seqlens, slot, fresh, y=None, stream=None)
         _dev_ptr(C, f32, "C", dev), _dev_ptr(state, f32, "state", dev), n_slots,
         _dev_ptr(y, f32, "y", dev), _stream_handle(stream, dev))
     _check(rc, "ssm_scan_prefill")
+    return y
+
+
+def prefill_ws(x, dt, A, B, C, state, cu_seqlens, slot, fresh, max_seqlen, segments=0,
+               workspace=None, y=None, stream=None):
+    """``ssm_scan_prefill_ws``: like ``prefill``, but long sequences may be
+    split over time when the batch is too small to fill the GPU.
+    ``max_seqlen`` (host int) bounds the sequence lengths; ``segments`` 0 =
+    automatic, 1 = never split, k = about k segments.  ``workspace`` (a uint8
+    CUDA tensor of at least ``workspace_size(...)`` bytes) is allocated here
+    when not given."""
+    import torch
+    n_slots, H, P, N = (int(v) for v in state.shape)
+    T = int(x.shape[0])
+    G = int(B.shape[1])
+    n_seqs = int(slot.shape[0])
+    if tuple(x.shape) != (T, H, P) or tuple(dt.shape) != (T, H) or tuple(A.shape) != (H,):
+        raise ValueError("x, dt or A has the wrong shape")
+    if tuple(B.shape) != (T, G, N) or tuple(C.shape) != (T, G, N):
+        raise ValueError("B or C has the wrong shape")
+    if tuple(cu_seqlens.shape) != (n_seqs + 1,) or tuple(fresh.shape) != (n_seqs,):
+        raise ValueError("cu_seqlens or fresh has the wrong shape")
+    dev = state.device
+    if y is None:
+        y = torch.empty((T, H, P), dtype=torch.float32, device=dev)
+    elif tuple(y.shape) != (T, H, P):
+        raise ValueError("y has the wrong shape")
+    need = workspace_size(H, P, N, G, n_seqs, T, max_seqlen, segments)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = _dev_ptr(workspace, torch.uint8, "workspace", dev) if workspace is not None else None
+    ws_bytes = int(workspace.numel()) if workspace is not None else 0
+    f32, i32 = torch.float32, torch.int32
+    rc = _lib.ssm_scan_prefill_ws(
+        ctypes.byref(Dims(H, P, N, G)), n_seqs, T, int(max_seqlen), int(segments),
+        _dev_ptr(cu_seqlens, i32, "cu_seqlens", dev), _dev_ptr(slot, i32, "slot", dev),
+        _dev_ptr(fresh, torch.uint8, "fresh", dev), _dev_ptr(x, f32, "x", dev),
+        _dev_ptr(dt, f32, "dt", dev), _dev_ptr(A, f32, "A", dev), _dev_ptr(B, f32, "B", dev),
+        _dev_ptr(C, f32, "C", dev), _dev_ptr(state, f32, "state", dev), n_slots,
+        _dev_ptr(y, f32, "y", dev), ws_ptr, ws_bytes, _stream_handle(stream, dev))
+    _check(rc, "ssm_scan_prefill_ws")
     return y
 
 

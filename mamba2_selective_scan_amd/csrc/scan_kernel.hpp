@@ -65,8 +65,17 @@ struct ScanArgs {
     int32_t H, P, N, G;
     int32_t heads_per_group;
     int32_t n_row_blocks;        // ceil(P / RB)
-    int32_t n_blocks;            // n_seqs * H * n_row_blocks
+    int32_t n_blocks;            // n_seqs * n_segs * H * n_row_blocks
+    // Time-parallel prefill (n_segs > 1): each sequence is cut into segments
+    // of seg_len tokens (the last one runs to the sequence end).
+    int32_t n_segs;              // segments per sequence in the grid (1 = none)
+    int32_t seg_len;
+    float *ws_state;             // [n_seqs][n_segs][H][P][N] segment end / carried-in states
+    float *ws_dtot;              // [n_seqs][n_segs][H] product of dA over each segment
+    float *ws_dcum;              // [T][H] product of dA from the segment start through t
 };
+
+enum class Mode { kPrefill, kSegScan, kDecode, kCorrect };
 
 // Compile-time shape of one kernel instance.
 template <int R_, int J_, int CT_>
@@ -95,8 +104,8 @@ struct Shape {
     static_assert(CT <= kThreads, "one thread stages each token's dt");
     static_assert(RB % 4 == 0, "rows per block must be a multiple of 4");
 
-    static constexpr int lds_floats(bool decode, bool vec) {
-        const int staging = decode ? 0 : 2 * BUF;   // decode reads its one token from global
+    static constexpr int lds_floats(Mode mode, bool vec) {
+        const int staging = mode == Mode::kDecode ? 0 : 2 * BUF;   // decode reads from global
         return (!vec && TILE > staging) ? TILE : staging;
     }
 };
@@ -122,6 +131,21 @@ __device__ __forceinline__ float row_allreduce(float v) {
     if constexpr (R >= 16) v += dpp<kMirror>(v);
     if constexpr (R >= 32) v += __shfl_xor(v, 16, 64);
     if constexpr (R >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Inclusive running product over the 16 lanes of each DPP row (lanes past a
+// row's start multiply by 1).  Used on one token's dA per lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_or_one(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(v), CTRL,
+                                                      0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_prefix_product(float v) {
+    v *= dpp_or_one<0x111>(v);     // row_shr:1
+    v *= dpp_or_one<0x112>(v);     // row_shr:2
+    v *= dpp_or_one<0x114>(v);     // row_shr:4
+    v *= dpp_or_one<0x118>(v);     // row_shr:8
     return v;
 }
 
@@ -172,30 +196,73 @@ __device__ __forceinline__ void lds_groups(f4 (&v)[J], const float *p) {
     for (int j = 0; j < J; ++j) v[j] = *reinterpret_cast<const f4 *>(p + 4 * R * j);
 }
 
-template <class S, bool VEC, bool DECODE>
+// The tokens [t_begin, t_end) that time segment k of sequence s covers, and
+// how many segments the sequence really has.  With n_segs == 1 the segment is
+// the whole sequence.
+struct SegRange {
+    int t_begin, t_end, n_real;
+};
+__device__ __forceinline__ SegRange segment_range(const ScanArgs &a, int s, int k) {
+    const int c0 = a.cu_seqlens[s], c1 = a.cu_seqlens[s + 1];
+    if (a.n_segs == 1) return SegRange{c0, c1, 1};
+    const int len = c1 - c0;
+    int n_real = (len + a.seg_len - 1) / a.seg_len;
+    n_real = n_real < 1 ? 1 : (n_real > a.n_segs ? a.n_segs : n_real);
+    const int tb = c0 + k * a.seg_len;
+    return SegRange{tb, k == n_real - 1 ? c1 : tb + a.seg_len, n_real};
+}
+
+// MODE kPrefill: scan whole sequences and write y and the end state (slot).
+// MODE kSegScan: scan one time segment of a sequence cut into n_segs pieces
+//   (segment 0 from the true start state, later ones from zero) and write y;
+//   the end state goes to ws_state (to the slot if the sequence was too short
+//   to be cut), with the segment's running and total decay products.
+// MODE kDecode: one token per sequence, B/C/x/dt read straight into registers.
+// MODE kCorrect: for a time segment k >= 1, add the carried-in state's
+//   contribution dcum[t] * (C_t . carry) to the y the segment scan wrote.
+template <class S, bool VEC, Mode MODE>
 __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     extern __shared__ float4 lds_raw[];
     float *const lds = reinterpret_cast<float *>(lds_raw);
 
     constexpr int R = S::R, J = S::J, E = S::E, CT = S::CT, NP = S::NP, RB = S::RB;
+    constexpr bool DECODE = MODE == Mode::kDecode;
+    constexpr bool CORRECT = MODE == Mode::kCorrect;
+    constexpr bool SEGMENTED = MODE == Mode::kSegScan || CORRECT;   // grid has a segment axis
 
-    // ---- workgroup -> (sequence, head, row block); XCD-contiguous order
+    // ---- workgroup -> (sequence, segment, head, row block); XCD-contiguous order
     const int bid = blockIdx.x;
     const int nb = a.n_blocks;
     const int per = nb / kXcds, rem = nb % kXcds;
-    const int xcd = bid % kXcds, k = bid / kXcds;
-    const int L = (xcd < rem) ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
+    const int xcd = bid % kXcds, kx = bid / kXcds;
+    const int L = (xcd < rem) ? xcd * (per + 1) + kx : rem * (per + 1) + (xcd - rem) * per + kx;
     const int rb = L % a.n_row_blocks;
     const int hd = (L / a.n_row_blocks) % a.H;
-    const int s = L / (a.n_row_blocks * a.H);
+    const int seg = SEGMENTED ? (L / (a.n_row_blocks * a.H)) % a.n_segs : 0;
+    const int s = L / (a.n_row_blocks * a.H * (SEGMENTED ? a.n_segs : 1));
 
     const int H = a.H, P = a.P, N = a.N, G = a.G;
     const int g = hd / a.heads_per_group;
-    const int t_begin = DECODE ? s : a.cu_seqlens[s];
-    const int t_end = DECODE ? s + 1 : a.cu_seqlens[s + 1];
+    int t_begin, t_end, n_real = 1;
+    if constexpr (DECODE) {
+        t_begin = s;
+        t_end = s + 1;
+    } else if constexpr (!SEGMENTED) {
+        t_begin = a.cu_seqlens[s];
+        t_end = a.cu_seqlens[s + 1];
+    } else {
+        const SegRange sr = segment_range(a, s, seg);
+        t_begin = sr.t_begin;
+        t_end = sr.t_end;
+        n_real = sr.n_real;
+    }
+    if (seg >= n_real) return;                       // the sequence is shorter
+    if (CORRECT && seg == 0) return;                 // segment 0 started from the true state
     const int n_tok = t_end - t_begin;
-    const bool fresh = a.fresh[s] != 0;
-    if (!fresh && n_tok <= 0) return;               // resume with no tokens: slot unchanged
+    const bool split = SEGMENTED && n_real > 1;
+    // Only the first segment of a sequence sees the slot; later ones start at 0.
+    const bool fresh = CORRECT ? false : (seg > 0 || a.fresh[s] != 0);
+    if (!CORRECT && !split && !fresh && n_tok <= 0) return;   // empty resume: slot unchanged
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -204,7 +271,15 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     const int p0 = rb * RB;
     const int rows_valid = min(RB, P - p0);
     const bool row_ok = i < rows_valid;
+    const int64_t hpn = int64_t(H) * P * N;
+    // rows p0.. of this head in the slot, and in this segment's workspace entry
     float *const st_block = a.state + ((int64_t(a.slot[s]) * H + hd) * P + p0) * int64_t(N);
+    float *const ws_block = SEGMENTED
+        ? a.ws_state + (int64_t(s) * a.n_segs + seg) * hpn + (int64_t(hd) * P + p0) * N
+        : nullptr;
+    // where the state comes from: the slot; for a correction, the state carried
+    // into this segment (the combine pass left it in the previous entry)
+    float *const src_block = CORRECT ? ws_block - hpn : st_block;
     const float A_h = a.A[hd];
 
     // ---- state -> registers
@@ -218,7 +293,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                 const int n0 = 4 * (j * R + r);
                 if (row_ok && n0 < N) {
                     const f4 v = __builtin_nontemporal_load(
-                        reinterpret_cast<const f4 *>(st_block + int64_t(i) * N + n0));
+                        reinterpret_cast<const f4 *>(src_block + int64_t(i) * N + n0));
                     h[4 * j + 0] = v.x; h[4 * j + 1] = v.y; h[4 * j + 2] = v.z; h[4 * j + 3] = v.w;
                 }
             }
@@ -227,7 +302,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
             const int total = rows_valid * N;
             for (int q = tid; q < total; q += kThreads) {
                 const int row = q / N;
-                lds[row * S::NPT + (q - row * N)] = st_block[q];
+                lds[row * S::NPT + (q - row * N)] = src_block[q];
             }
             __syncthreads();
 #pragma unroll
@@ -266,9 +341,15 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         // token loop never waits on the next chunk's prefetch.
         __builtin_amdgcn_s_waitcnt(0);
 
-        // ---- chunk staging: global -> registers -> LDS
+        // ---- chunk staging: global -> registers -> LDS.  The x slot carries x
+        // (prefill) or the segment scan's y (correction); the dt slot carries dt
+        // (prefill) or, for a correction, the running product of dA from the
+        // segment start through each token.  Time segments keep that running
+        // product in wave 0 (`run`), chunk after chunk: a 16-lane DPP prefix
+        // product per chunk (chunks of a segmented launch are <= 16 tokens).
         f4 pb[S::U_BC], pc[S::U_BC], px[S::U_X];
         float pdt = 0.f;
+        const float *xsrc = CORRECT ? a.y : a.x;
 
         auto issue_loads = [&](int t0, int nt) {
 #pragma unroll
@@ -279,7 +360,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                 const bool ok = (q < CT * NP / 4) && (tt < nt);
                 const int64_t off = (int64_t(t0 + tt) * G + g) * N + n0;
                 const int nv = ok ? clamp4(N - n0) : 0;
-                pb[u] = load4<VEC>(a.B + off, nv);
+                if constexpr (!CORRECT) pb[u] = load4<VEC>(a.B + off, nv);
                 pc[u] = load4<VEC>(a.C + off, nv);
             }
 #pragma unroll
@@ -289,12 +370,13 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                 const int pi = 4 * (q - tt * (RB / 4));
                 const bool ok = (q < CT * RB / 4) && (tt < nt);
                 const int nv = ok ? clamp4(rows_valid - pi) : 0;
-                px[u] = load4<VEC>(a.x + (int64_t(t0 + tt) * H + hd) * P + p0 + pi, nv);
+                px[u] = load4<VEC>(xsrc + (int64_t(t0 + tt) * H + hd) * P + p0 + pi, nv);
             }
             pdt = (tid < nt) ? a.dt[int64_t(t0 + tid) * H + hd] : 0.f;
         };
 
-        auto commit = [&](int buf) {
+        float run = 1.f;                                    // wave 0: dA product so far
+        auto commit = [&](int buf, int t0, int nt) {
             float *base = lds + buf * S::BUF;
             f4 *Bs4 = reinterpret_cast<f4 *>(base + S::OFF_B);
             f4 *Cs4 = reinterpret_cast<f4 *>(base + S::OFF_C);
@@ -302,16 +384,36 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
 #pragma unroll
             for (int u = 0; u < S::U_BC; ++u) {
                 const int q = u * kThreads + tid;
-                if (q < CT * NP / 4) { Bs4[q] = pb[u]; Cs4[q] = pc[u]; }
+                if (q < CT * NP / 4) {
+                    if constexpr (!CORRECT) Bs4[q] = pb[u];
+                    Cs4[q] = pc[u];
+                }
             }
 #pragma unroll
             for (int u = 0; u < S::U_X; ++u) {
                 const int q = u * kThreads + tid;
                 if (q < CT * RB / 4) Xs4[q] = px[u];
             }
-            if (tid < CT) {
-                base[S::OFF_DT + tid] = pdt;
-                base[S::OFF_DA + tid] = expf(pdt * A_h);
+            if constexpr (SEGMENTED) {
+                static_assert(!SEGMENTED || CT <= 16, "segment chunks fit one DPP row");
+                if (tid < 64) {                              // wave 0, all lanes active
+                    const float dA = (tid < nt) ? expf(pdt * A_h) : 1.f;
+                    const float cum = run * row_prefix_product(dA);
+                    run = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), 15));
+                    if (tid < CT) {
+                        base[S::OFF_DT + tid] = CORRECT ? cum : pdt;
+                        base[S::OFF_DA + tid] = dA;
+                    }
+                    // a split sequence's segment scan also leaves the running
+                    // product for the matrix-core correction (one row block per head)
+                    if (MODE == Mode::kSegScan && split && rb == 0 && tid < nt)
+                        a.ws_dcum[int64_t(t0 + tid) * H + hd] = cum;
+                }
+            } else {
+                if (tid < CT) {
+                    base[S::OFF_DT + tid] = pdt;
+                    base[S::OFF_DA + tid] = expf(pdt * A_h);
+                }
             }
         };
 
@@ -322,36 +424,44 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         // instructions and the keep-select needs no runtime compare.
         constexpr int KY = R < 16 ? R : 16;
         const int rk = r % KY;
+        auto token_y = [&](const float *base, int tt) -> float {
+            f4 cv[J];
+            lds_groups<R, J>(cv, base + S::OFF_C + 4 * r + tt * NP);
+            if constexpr (CORRECT) {
+                // y += dcum[t] * (C_t . carry): the carry decayed to token t
+                float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    acc0 += h[4 * j + 0] * cv[j].x;
+                    acc1 += h[4 * j + 1] * cv[j].y;
+                    acc0 += h[4 * j + 2] * cv[j].z;
+                    acc1 += h[4 * j + 3] * cv[j].w;
+                }
+                const float yc = row_allreduce<R>(acc0 + acc1);
+                return base[S::OFF_X + tt * RB + i] + base[S::OFF_DT + tt] * yc;
+            } else {
+                f4 bv[J];
+                lds_groups<R, J>(bv, base + S::OFF_B + 4 * r + tt * NP);
+                return row_allreduce<R>(update_token<J>(
+                    h, bv, cv, base[S::OFF_DA + tt], base[S::OFF_X + tt * RB + i] * base[S::OFF_DT + tt]));
+            }
+        };
         auto compute = [&](int buf, int nt) {
             const float *base = lds + buf * S::BUF;
-            const float *Bl = base + S::OFF_B + 4 * r;
-            const float *Cl = base + S::OFF_C + 4 * r;
-            const float *Xl = base + S::OFF_X + i;
-            const float *Dt = base + S::OFF_DT;
-            const float *Da = base + S::OFF_DA;
             float *Ys = lds + buf * S::BUF + S::OFF_Y + i;
             float y_keep = 0.f;
             int t0 = 0;
             for (; t0 + KY <= nt; t0 += KY) {
 #pragma unroll
                 for (int kk = 0; kk < KY; ++kk) {
-                    const int tt = t0 + kk;
-                    f4 bv[J], cv[J];
-                    lds_groups<R, J>(bv, Bl + tt * NP);
-                    lds_groups<R, J>(cv, Cl + tt * NP);
-                    const float yv =
-                        row_allreduce<R>(update_token<J>(h, bv, cv, Da[tt], Xl[tt * RB] * Dt[tt]));
+                    const float yv = token_y(base, t0 + kk);
                     y_keep = (rk == kk) ? yv : y_keep;
                 }
                 Ys[(t0 + rk) * RB] = y_keep;
             }
             if (t0 < nt) {
                 for (int tt = t0; tt < nt; ++tt) {
-                    f4 bv[J], cv[J];
-                    lds_groups<R, J>(bv, Bl + tt * NP);
-                    lds_groups<R, J>(cv, Cl + tt * NP);
-                    const float yv =
-                        row_allreduce<R>(update_token<J>(h, bv, cv, Da[tt], Xl[tt * RB] * Dt[tt]));
+                    const float yv = token_y(base, tt);
                     y_keep = (rk == tt - t0) ? yv : y_keep;
                 }
                 if (rk < nt - t0) Ys[(t0 + rk) * RB] = y_keep;
@@ -385,7 +495,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         const int n_chunks = (n_tok + CT - 1) / CT;
         if (n_chunks > 0) {
             issue_loads(t_begin, min(CT, n_tok));
-            commit(0);
+            commit(0, t_begin, min(CT, n_tok));
         }
         __syncthreads();
         for (int c = 0; c < n_chunks; ++c) {
@@ -396,23 +506,29 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
             if (has_next) issue_loads(t0 + CT, min(CT, t_end - t0 - CT));
             if (c > 0) flush_y(buf ^ 1, t0 - CT, CT);    // previous chunk, always full
             compute(buf, nt);
-            if (has_next) commit(buf ^ 1);
+            if (has_next) commit(buf ^ 1, t0 + CT, min(CT, t_end - t0 - CT));
             __syncthreads();
         }
         if (n_chunks > 0) {
             const int c = n_chunks - 1;
             flush_y(c & 1, t_begin + c * CT, n_tok - c * CT);
         }
+        // a split sequence's segment records its total decay once per head
+        if constexpr (MODE == Mode::kSegScan)
+            if (split && rb == 0 && tid == 0) a.ws_dtot[(int64_t(s) * a.n_segs + seg) * H + hd] = run;
     }
 
-    // ---- registers -> state slot
+    if constexpr (CORRECT) return;                   // the state is not changed here
+
+    // ---- registers -> state slot (or this segment's workspace entry)
+    float *const dst_block = (SEGMENTED && split) ? ws_block : st_block;
     if constexpr (VEC) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int n0 = 4 * (j * R + r);
             if (row_ok && n0 < N) {
                 const f4 v = {h[4 * j + 0], h[4 * j + 1], h[4 * j + 2], h[4 * j + 3]};
-                __builtin_nontemporal_store(v, reinterpret_cast<f4 *>(st_block + int64_t(i) * N + n0));
+                __builtin_nontemporal_store(v, reinterpret_cast<f4 *>(dst_block + int64_t(i) * N + n0));
             }
         }
     } else {
@@ -427,8 +543,48 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         const int total = rows_valid * N;
         for (int q = tid; q < total; q += kThreads) {
             const int row = q / N;
-            st_block[q] = lds[row * S::NPT + (q - row * N)];
+            dst_block[q] = lds[row * S::NPT + (q - row * N)];
         }
+    }
+}
+
+// Combine pass of the time-parallel prefill, one thread per 4 (VEC) or 1 state
+// elements of one (sequence, head, row): walk the sequence's segments in order,
+//     carry <- dtot[k] * carry + local_end[k]
+// starting from segment 0's (true) end state; leave the state carried INTO
+// segment k in entry k-1 for the correction pass, and write the final carry to
+// the sequence's slot.
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) combine_kernel(ScanArgs a, int64_t n_units) {
+    const int64_t u = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    if (u >= n_units) return;
+    constexpr int W = VEC ? 4 : 1;
+    const int64_t per_seq = int64_t(a.H) * a.P * a.N / W;
+    const int s = int(u / per_seq);
+    const int64_t e = (u - int64_t(s) * per_seq) * W;          // element within [H][P][N]
+    const int hd = int(e / (int64_t(a.P) * a.N));
+    const SegRange sr = segment_range(a, s, 0);
+    if (sr.n_real == 1) return;                                // not split: the scan wrote the slot
+    const int64_t hpn = int64_t(a.H) * a.P * a.N;
+    float *w = a.ws_state + int64_t(s) * a.n_segs * hpn + e;
+    float *dst = a.state + int64_t(a.slot[s]) * hpn + e;
+    if constexpr (VEC) {
+        f4 carry = *reinterpret_cast<const f4 *>(w);
+        for (int k = 1; k < sr.n_real; ++k) {
+            if (k > 1) *reinterpret_cast<f4 *>(w + (k - 1) * hpn) = carry;
+            const float d = a.ws_dtot[(int64_t(s) * a.n_segs + k) * a.H + hd];
+            const f4 loc = *reinterpret_cast<const f4 *>(w + k * hpn);
+            carry = d * carry + loc;
+        }
+        __builtin_nontemporal_store(carry, reinterpret_cast<f4 *>(dst));
+    } else {
+        float carry = w[0];
+        for (int k = 1; k < sr.n_real; ++k) {
+            if (k > 1) w[(k - 1) * hpn] = carry;
+            const float d = a.ws_dtot[(int64_t(s) * a.n_segs + k) * a.H + hd];
+            carry = d * carry + w[k * hpn];
+        }
+        dst[0] = carry;
     }
 }
 

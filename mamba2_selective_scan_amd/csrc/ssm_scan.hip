@@ -7,16 +7,19 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
 
+#include "correct_mfma.hpp"
 #include "scan_kernel.hpp"
 
 namespace {
 
 using ssm::kThreads;
 using ssm::ScanArgs;
+using ssm::Mode;
 using ssm::Shape;
 
 // One row of the shape table: state sizes up to n_max use R lanes per row,
@@ -26,7 +29,8 @@ using ssm::Shape;
 // under ~80 KB of the 160 KB LDS.  Decode is one pass over the state, so it
 // favours more float4 loads in flight per lane (measured on MI355X at
 // N = 128: 8 lanes x 16 elements beat 16 x 8 by 3%, 32 x 4 and 4 x 32 lost
-// 12-17%).
+// 12-17%).  The two halves of a time-split prefill run with half the chunk
+// (SCT = CT / 2), so four workgroups fit in one CU's LDS.
 struct ShapeRow {
     int n_max, R, J, CT, DR, DJ;
 };
@@ -57,10 +61,10 @@ int hip_fail(hipError_t err, int code) {
     return code;
 }
 
-template <class S, bool VEC, bool DECODE>
+template <class S, bool VEC, Mode MODE>
 int launch(const ScanArgs &a, hipStream_t stream) {
-    const void *kern = reinterpret_cast<const void *>(&ssm::scan_kernel<S, VEC, DECODE>);
-    const int lds_bytes = S::lds_floats(DECODE, VEC) * int(sizeof(float));
+    const void *kern = reinterpret_cast<const void *>(&ssm::scan_kernel<S, VEC, MODE>);
+    const int lds_bytes = S::lds_floats(MODE, VEC) * int(sizeof(float));
     if (lds_bytes > 64 * 1024) {
         // Opt in to more than 64 KB of dynamic LDS, once per device.
         static std::atomic<uint8_t> opted[kMaxDevices];
@@ -97,37 +101,65 @@ int with_row(const ShapeRow &row, F &&f) {
     }
 }
 
+// What a launch computes: a whole-sequence prefill, a decode step, or one of
+// the two kernel halves of a time-split prefill (segment scans, corrections).
+enum class Kind { kPrefill, kDecode, kSegScan, kCorrect };
+
+constexpr int seg_chunk(int CT) { return CT / 2 > 2 ? CT / 2 : 2; }
+
 struct Launch {
     const ScanArgs &a;
-    bool vec, decode;
+    bool vec;
+    Kind kind;
     hipStream_t stream;
     template <int R, int J, int CT, int DR, int DJ>
     int run() const {
-        if (decode)
-            return vec ? launch<Shape<DR, DJ, 1>, true, true>(a, stream)
-                       : launch<Shape<DR, DJ, 1>, false, true>(a, stream);
-        return vec ? launch<Shape<R, J, CT>, true, false>(a, stream)
-                   : launch<Shape<R, J, CT>, false, false>(a, stream);
+        constexpr int SCT = seg_chunk(CT);
+        switch (kind) {
+        case Kind::kDecode:
+            return vec ? launch<Shape<DR, DJ, 1>, true, Mode::kDecode>(a, stream)
+                       : launch<Shape<DR, DJ, 1>, false, Mode::kDecode>(a, stream);
+        case Kind::kPrefill:
+            return vec ? launch<Shape<R, J, CT>, true, Mode::kPrefill>(a, stream)
+                       : launch<Shape<R, J, CT>, false, Mode::kPrefill>(a, stream);
+        case Kind::kSegScan:
+            return vec ? launch<Shape<R, J, SCT>, true, Mode::kSegScan>(a, stream)
+                       : launch<Shape<R, J, SCT>, false, Mode::kSegScan>(a, stream);
+        case Kind::kCorrect:
+            return vec ? launch<Shape<R, J, SCT>, true, Mode::kCorrect>(a, stream)
+                       : launch<Shape<R, J, SCT>, false, Mode::kCorrect>(a, stream);
+        }
+        return SSM_ERR_UNSUPPORTED;
     }
 };
 
 struct LdsBytes {
-    bool vec, decode;
+    bool vec;
+    Kind kind;
     template <int R, int J, int CT, int DR, int DJ>
     int run() const {
-        return int(sizeof(float)) * (decode ? Shape<DR, DJ, 1>::lds_floats(true, vec)
-                                            : Shape<R, J, CT>::lds_floats(false, vec));
+        constexpr int SCT = seg_chunk(CT);
+        int floats = 0;
+        switch (kind) {
+        case Kind::kDecode: floats = Shape<DR, DJ, 1>::lds_floats(Mode::kDecode, vec); break;
+        case Kind::kPrefill: floats = Shape<R, J, CT>::lds_floats(Mode::kPrefill, vec); break;
+        case Kind::kSegScan: floats = Shape<R, J, SCT>::lds_floats(Mode::kSegScan, vec); break;
+        case Kind::kCorrect: floats = Shape<R, J, SCT>::lds_floats(Mode::kCorrect, vec); break;
+        }
+        return int(sizeof(float)) * floats;
     }
 };
 
-// Lanes per row, elements per lane and rows per workgroup of a call.
+// Lanes per row, elements per lane, rows per workgroup and chunk of a launch.
 struct Geo {
     int R, E, RB, CT;
 };
-Geo geo_for(const ShapeRow &row, bool decode) {
+Geo geo_for(const ShapeRow &row, Kind kind) {
+    const bool decode = kind == Kind::kDecode;
     const int R = decode ? row.DR : row.R;
     const int J = decode ? row.DJ : row.J;
-    return Geo{R, 4 * J, ssm::kWaves * (64 / R), decode ? 1 : row.CT};
+    const int CT = decode ? 1 : (kind == Kind::kPrefill ? row.CT : seg_chunk(row.CT));
+    return Geo{R, 4 * J, ssm::kWaves * (64 / R), CT};
 }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -141,16 +173,71 @@ int check_dims(const ssm_scan_dims *d) {
     return SSM_OK;
 }
 
-// Shared body of prefill and decode once the arguments are known valid.
-int scan_common(const ssm_scan_dims *d, int32_t n_seqs, const int32_t *cu_seqlens,
-                const int32_t *slot, const uint8_t *fresh, const float *x, const float *dt,
-                const float *A, const float *B, const float *C, float *state, float *y,
-                bool decode, void *stream) {
+// How a prefill is cut over time.  A single long sequence exposes only
+// H * P rows, one wavefront per SIMD at the headline geometry; cutting it into
+// n_segs segments multiplies the wavefronts by n_segs.  Auto mode cuts when
+// the whole-sequence launch would give fewer than 2 wavefronts per SIMD
+// (1024 SIMDs), aiming at 4, with segments of at least 256 tokens.
+struct SegPlan {
+    int n_segs, seg_len;
+};
+constexpr int64_t kTargetWaves = 4096;
+constexpr int kMinSegTokens = 256;
+
+SegPlan plan_segments(const ssm_scan_dims *d, const ShapeRow &row, int32_t n_seqs,
+                      int32_t max_seqlen, int32_t requested) {
+    const int sct = seg_chunk(row.CT);
+    if (requested == 1 || max_seqlen <= sct || n_seqs <= 0) return SegPlan{1, 0};
+    int64_t K;
+    if (requested > 1) {
+        K = requested;
+    } else {
+        const int RB = ssm::kWaves * (64 / row.R);
+        const int64_t waves = int64_t(n_seqs) * d->n_heads * ((d->head_dim + RB - 1) / RB) * ssm::kWaves;
+        if (2 * waves >= kTargetWaves) return SegPlan{1, 0};
+        K = (kTargetWaves + waves - 1) / waves;
+        K = std::min<int64_t>(K, max_seqlen / kMinSegTokens);
+    }
+    K = std::min<int64_t>(K, (int64_t(max_seqlen) + sct - 1) / sct);
+    if (K < 2) return SegPlan{1, 0};
+    const int64_t per = (max_seqlen + K - 1) / K;
+    // whole chunks per segment, unless rounding up would lose a segment
+    int seg_len = int((per + sct - 1) / sct * sct);
+    if ((int64_t(max_seqlen) + seg_len - 1) / seg_len < K) seg_len = int(per);
+    const int n_segs = int((int64_t(max_seqlen) + seg_len - 1) / seg_len);
+    return n_segs < 2 ? SegPlan{1, 0} : SegPlan{n_segs, seg_len};
+}
+
+// Workspace carve-up for a split prefill: 256-byte aligned pieces.
+struct WsLayout {
+    size_t state, dtot, dcum, total;
+};
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+WsLayout ws_layout(const ssm_scan_dims *d, int32_t n_seqs, int32_t n_tokens, int n_segs) {
+    WsLayout w{};
+    const size_t seg_entries = size_t(n_seqs) * size_t(n_segs) * size_t(d->n_heads);
+    w.state = 0;
+    w.dtot = round256(seg_entries * size_t(d->head_dim) * size_t(d->d_state) * sizeof(float));
+    w.dcum = w.dtot + round256(seg_entries * sizeof(float));
+    w.total = w.dcum + round256(size_t(n_tokens) * size_t(d->n_heads) * sizeof(float)) + 256;
+    return w;
+}
+
+// Shared body of every scan once the arguments are known valid.  With
+// plan.n_segs > 1, `ws` (256-byte aligned, ws_layout() bytes) receives the
+// segment end states, their total and running decays, and three kernels run:
+// segment scans, the combine pass and the corrections.
+int scan_common(const ssm_scan_dims *d, int32_t n_seqs, int32_t n_tokens,
+                const int32_t *cu_seqlens, const int32_t *slot, const uint8_t *fresh,
+                const float *x, const float *dt, const float *A, const float *B, const float *C,
+                float *state, float *y, bool decode, SegPlan plan, char *ws, void *stream_ptr) {
     const ShapeRow *row = shape_for(d->d_state);
     if (!row) return SSM_ERR_UNSUPPORTED;
-    const int RB = geo_for(*row, decode).RB;
+    const bool split = !decode && plan.n_segs > 1;
+    const Kind kind = decode ? Kind::kDecode : (split ? Kind::kSegScan : Kind::kPrefill);
+    const int RB = geo_for(*row, kind).RB;
     const int64_t n_row_blocks = (int64_t(d->head_dim) + RB - 1) / RB;
-    const int64_t n_blocks = int64_t(n_seqs) * d->n_heads * n_row_blocks;
+    const int64_t n_blocks = int64_t(n_seqs) * (split ? plan.n_segs : 1) * d->n_heads * n_row_blocks;
     if (n_blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
 
     const void *fptrs[] = {x, dt, A, B, C, state, y};
@@ -179,7 +266,48 @@ int scan_common(const ssm_scan_dims *d, int32_t n_seqs, const int32_t *cu_seqlen
     a.heads_per_group = d->n_heads / d->n_groups;
     a.n_row_blocks = int32_t(n_row_blocks);
     a.n_blocks = int32_t(n_blocks);
-    return with_row(*row, Launch{a, vec, decode, static_cast<hipStream_t>(stream)});
+    a.n_segs = split ? plan.n_segs : 1;
+    a.seg_len = split ? plan.seg_len : 0;
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    if (!split) return with_row(*row, Launch{a, vec, kind, stream});
+
+    const WsLayout w = ws_layout(d, n_seqs, n_tokens, plan.n_segs);
+    a.ws_state = reinterpret_cast<float *>(ws + w.state);
+    a.ws_dtot = reinterpret_cast<float *>(ws + w.dtot);
+    a.ws_dcum = reinterpret_cast<float *>(ws + w.dcum);
+    int rc = with_row(*row, Launch{a, vec, Kind::kSegScan, stream});
+    if (rc != SSM_OK) return rc;
+    {
+        const int64_t units = int64_t(n_seqs) * d->n_heads * d->head_dim * d->d_state / (vec ? 4 : 1);
+        const int64_t grid = (units + kThreads - 1) / kThreads;
+        if (grid > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+        const void *kern = vec ? reinterpret_cast<const void *>(&ssm::combine_kernel<true>)
+                               : reinterpret_cast<const void *>(&ssm::combine_kernel<false>);
+        ScanArgs args = a;
+        int64_t n_units = units;
+        void *params[] = {&args, &n_units};
+        const hipError_t err =
+            hipLaunchKernel(kern, dim3(unsigned(grid)), dim3(kThreads), params, 0, stream);
+        if (err != hipSuccess) return hip_fail(err, SSM_ERR_LAUNCH);
+    }
+    // Corrections: a dense contraction per segment, on the matrix cores when
+    // the state rows split into float4 halves (N % 8 == 0, N <= 128).
+    if (vec && d->d_state % 8 == 0 && d->d_state <= 128) {
+        const int n_tblocks = (plan.seg_len + 127) / 128;
+        const int64_t grid = int64_t(n_seqs) * plan.n_segs * d->n_heads * n_tblocks;
+        if (grid > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+        const int nh = d->d_state / 2;
+        const void *kern = nh <= 16 ? reinterpret_cast<const void *>(&ssm::correct_mfma_kernel<16>)
+                         : nh <= 32 ? reinterpret_cast<const void *>(&ssm::correct_mfma_kernel<32>)
+                                    : reinterpret_cast<const void *>(&ssm::correct_mfma_kernel<64>);
+        ScanArgs args = a;
+        int tblocks = n_tblocks;
+        void *params[] = {&args, &tblocks};
+        const hipError_t err =
+            hipLaunchKernel(kern, dim3(unsigned(grid)), dim3(kThreads), params, 0, stream);
+        return err == hipSuccess ? SSM_OK : hip_fail(err, SSM_ERR_LAUNCH);
+    }
+    return with_row(*row, Launch{a, vec, Kind::kCorrect, stream});
 }
 
 }  // namespace
@@ -197,8 +325,50 @@ int ssm_scan_prefill(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens
     if (n_slots == 0) return SSM_ERR_DIMS;
     if (!cu_seqlens || !slot || !fresh || !A || !state) return SSM_ERR_NULL;
     if (n_tokens > 0 && (!x || !dt || !B || !C || !y)) return SSM_ERR_NULL;
-    return scan_common(dims, n_seqs, cu_seqlens, slot, fresh, x, dt, A, B, C, state, y,
-                       /*decode=*/false, stream);
+    return scan_common(dims, n_seqs, n_tokens, cu_seqlens, slot, fresh, x, dt, A, B, C, state,
+                       y, /*decode=*/false, SegPlan{1, 0}, nullptr, stream);
+}
+
+int ssm_scan_prefill_workspace_size(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens,
+                                    int32_t max_seqlen, int32_t n_segments, size_t *bytes) {
+    const int rc = check_dims(dims);
+    if (rc != SSM_OK) return rc;
+    if (!bytes) return SSM_ERR_NULL;
+    if (n_seqs < 0 || n_tokens < 0 || max_seqlen < 0 || n_segments < 0) return SSM_ERR_DIMS;
+    const ShapeRow *row = shape_for(dims->d_state);
+    const SegPlan plan = plan_segments(dims, *row, n_seqs, max_seqlen, n_segments);
+    *bytes = plan.n_segs > 1 ? ws_layout(dims, n_seqs, n_tokens, plan.n_segs).total : 0;
+    return SSM_OK;
+}
+
+int ssm_scan_prefill_ws(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens,
+                        int32_t max_seqlen, int32_t n_segments, const int32_t *cu_seqlens,
+                        const int32_t *slot, const uint8_t *fresh, const float *x,
+                        const float *dt, const float *A, const float *B, const float *C,
+                        float *state, int32_t n_slots, float *y, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    const int rc = check_dims(dims);
+    if (rc != SSM_OK) return rc;
+    if (n_seqs < 0 || n_tokens < 0 || n_slots < 0 || max_seqlen < 0 || n_segments < 0)
+        return SSM_ERR_DIMS;
+    if (n_seqs == 0) return SSM_OK;
+    if (n_slots == 0) return SSM_ERR_DIMS;
+    if (!cu_seqlens || !slot || !fresh || !A || !state) return SSM_ERR_NULL;
+    if (n_tokens > 0 && (!x || !dt || !B || !C || !y)) return SSM_ERR_NULL;
+    const ShapeRow *row = shape_for(dims->d_state);
+    SegPlan plan = plan_segments(dims, *row, n_seqs, max_seqlen, n_segments);
+    char *ws = nullptr;
+    if (plan.n_segs > 1) {
+        const size_t need = ws_layout(dims, n_seqs, n_tokens, plan.n_segs).total;
+        if (!workspace || workspace_bytes < need) {
+            plan = SegPlan{1, 0};                    // not enough room: one pass per sequence
+        } else {
+            const uintptr_t p = reinterpret_cast<uintptr_t>(workspace);
+            ws = reinterpret_cast<char *>((p + 255) / 256 * 256);
+        }
+    }
+    return scan_common(dims, n_seqs, n_tokens, cu_seqlens, slot, fresh, x, dt, A, B, C, state,
+                       y, /*decode=*/false, plan, ws, stream);
 }
 
 int ssm_scan_decode(const ssm_scan_dims *dims, int32_t n_seqs, const int32_t *slot,
@@ -211,8 +381,8 @@ int ssm_scan_decode(const ssm_scan_dims *dims, int32_t n_seqs, const int32_t *sl
     if (n_seqs == 0) return SSM_OK;
     if (n_slots == 0) return SSM_ERR_DIMS;
     if (!slot || !fresh || !A || !state || !x || !dt || !B || !C || !y) return SSM_ERR_NULL;
-    return scan_common(dims, n_seqs, nullptr, slot, fresh, x, dt, A, B, C, state, y,
-                       /*decode=*/true, stream);
+    return scan_common(dims, n_seqs, n_seqs, nullptr, slot, fresh, x, dt, A, B, C, state, y,
+                       /*decode=*/true, SegPlan{1, 0}, nullptr, stream);
 }
 
 const char *ssm_scan_strerror(int code) {
@@ -279,15 +449,37 @@ int ssm_scan_query_geometry(const ssm_scan_dims *dims, int32_t n_seqs, int32_t d
     const ShapeRow *row = shape_for(dims->d_state);
     if (!row) return SSM_ERR_UNSUPPORTED;
     const bool vec = aligned16 && dims->d_state % 4 == 0 && dims->head_dim % 4 == 0;
-    const Geo geo = geo_for(*row, decode != 0);
+    const Kind kind = decode ? Kind::kDecode : Kind::kPrefill;
+    const Geo geo = geo_for(*row, kind);
     out->lanes_per_row = geo.R;
     out->elems_per_lane = geo.E;
     out->rows_per_block = geo.RB;
     out->chunk_tokens = geo.CT;
     out->threads_per_block = kThreads;
-    out->lds_bytes = with_row(*row, LdsBytes{vec, decode != 0});
+    out->lds_bytes = with_row(*row, LdsBytes{vec, kind});
     out->blocks = int64_t(n_seqs) * dims->n_heads * ((int64_t(dims->head_dim) + geo.RB - 1) / geo.RB);
     out->vector_path = vec ? 1 : 0;
+    out->segments = 1;
+    out->segment_tokens = 0;
+    return SSM_OK;
+}
+
+int ssm_scan_query_prefill_plan(const ssm_scan_dims *dims, int32_t n_seqs, int32_t max_seqlen,
+                                int32_t n_segments, int32_t aligned16, ssm_scan_geometry *out) {
+    const int rc = ssm_scan_query_geometry(dims, n_seqs, 0, aligned16, out);
+    if (rc != SSM_OK) return rc;
+    if (max_seqlen < 0 || n_segments < 0) return SSM_ERR_DIMS;
+    const ShapeRow *row = shape_for(dims->d_state);
+    const SegPlan plan = plan_segments(dims, *row, n_seqs, max_seqlen, n_segments);
+    if (plan.n_segs > 1) {
+        const bool vec = out->vector_path != 0;
+        const Geo geo = geo_for(*row, Kind::kSegScan);
+        out->chunk_tokens = geo.CT;
+        out->lds_bytes = with_row(*row, LdsBytes{vec, Kind::kSegScan});
+        out->blocks *= plan.n_segs;
+        out->segments = plan.n_segs;
+        out->segment_tokens = plan.seg_len;
+    }
     return SSM_OK;
 }
 

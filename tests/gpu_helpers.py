@@ -25,11 +25,15 @@ def rel_err(a, ref):
     return float(np.max(np.abs(a - ref) / (1.0 + np.abs(ref))))
 
 
-def run_gpu(case, mode="prefill", device="cuda:0", offset_floats=0):
+def run_gpu(case, mode="prefill", device="cuda:0", offset_floats=0, max_seqlen=None,
+            segments=0, workspace_bytes=None):
     """Run ``case`` on the GPU; returns (y, state) as numpy.  ``mode`` is
     "prefill" or "decode" (every length must be 1).  ``offset_floats`` > 0
     places every float array at that element offset inside a larger buffer,
-    which breaks 16-byte alignment and forces the scalar path."""
+    which breaks 16-byte alignment and forces the scalar path.  Mode
+    "prefill_ws" calls ssm_scan_prefill_ws with ``max_seqlen`` (default: the
+    longest length) and ``segments``; ``workspace_bytes`` overrides the
+    workspace size the library asks for."""
     import torch
     import mamba2_selective_scan_amd as ssm
 
@@ -50,6 +54,15 @@ def run_gpu(case, mode="prefill", device="cuda:0", offset_floats=0):
     if mode == "prefill":
         cu = put(case.cu_seqlens)
         ssm.prefill(x, dt, A, B, C, state, cu, slot, fresh, y=y)
+    elif mode == "prefill_ws":
+        cu = put(case.cu_seqlens)
+        ms = int(case.lengths.max()) if max_seqlen is None and case.n_seqs else int(max_seqlen or 0)
+        need = ssm.workspace_size(case.H, case.P, case.N, case.G, case.n_seqs, case.n_tokens,
+                                  ms, segments)
+        nbytes = need if workspace_bytes is None else workspace_bytes
+        ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device=device)  # garbage
+        ssm.prefill_ws(x, dt, A, B, C, state, cu, slot, fresh, ms, segments=segments,
+                       workspace=ws[:nbytes] if nbytes else None, y=y)
     elif mode == "decode":
         assert np.all(case.lengths == 1)
         ssm.decode(x, dt, A, B, C, state, slot, fresh, y=y)

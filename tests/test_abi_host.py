@@ -19,7 +19,8 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"ssm_scan_prefill", "ssm_scan_decode", "ssm_scan_strerror",
                           "ssm_scan_version", "ssm_scan_check_metadata",
                           "ssm_scan_query_geometry", "ssm_scan_last_hip_error",
-                          "ssm_scan_last_hip_error_string"}
+                          "ssm_scan_last_hip_error_string", "ssm_scan_prefill_ws",
+                          "ssm_scan_prefill_workspace_size", "ssm_scan_query_prefill_plan"}
     for n in names:
         assert hasattr(m.lib(), n), n
 
@@ -113,10 +114,40 @@ def test_no_kernel_uses_scratch():
     text = open(report).read()
     names = re.findall(r"Function Name: (\S+)", text)
     scratch = [int(v) for v in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
-    assert len(names) == 28 and len(scratch) == len(names)
+    # 7 state-size classes x (prefill, segment scan, correction, decode) x (vector, scalar)
+    # + 2 combine kernels + 3 matrix-core corrections
+    assert len(names) == 61 and len(scratch) == len(names)
     assert all(v == 0 for v in scratch), dict(zip(names, scratch))
 
 
 def test_single_hip_runtime():
     """The library shares torch's HIP runtime (one libamdhip64 mapped)."""
     assert len(m.hip_runtimes_loaded()) == 1, m.hip_runtimes_loaded()
+
+
+def test_prefill_plan_and_workspace():
+    """The headline prefill (1 x 4096 at H64 P64 N128 G8) fills only 1024
+    wavefronts, so automatic planning cuts it into 4 segments of 1024 tokens;
+    a batch that already fills the GPU is not cut; forcing works; the
+    workspace holds one [H][P][N] state per segment plus the decay arrays."""
+    g = m.prefill_plan(64, 64, 128, 8, 1, 4096)
+    assert g["segments"] == 4 and g["segment_tokens"] == 1024 and g["blocks"] == 4 * 256
+    assert g["chunk_tokens"] == 16 and g["lds_bytes"] <= 160 * 1024 // 4
+    ws = m.workspace_size(64, 64, 128, 8, 1, 4096, 4096)
+    assert 4 * 64 * 64 * 128 * 4 + 4096 * 64 * 4 <= ws <= 4 * 64 * 64 * 128 * 4 + 4096 * 64 * 4 + 4096
+    assert m.prefill_plan(64, 64, 128, 8, 16, 4096)["segments"] == 1     # 16 seqs fill it
+    assert m.workspace_size(64, 64, 128, 8, 16, 65536, 4096) == 0
+    assert m.prefill_plan(64, 64, 128, 8, 1, 200)["segments"] == 1        # too short
+    f = m.prefill_plan(4, 16, 16, 1, 1, 64, segments=3)
+    assert f["segments"] == 3 and f["segment_tokens"] == 22     # whole 16-token chunks would give 2
+    assert m.prefill_plan(64, 64, 128, 8, 1, 4096, segments=1)["segments"] == 1
+
+
+@pytest.mark.parametrize("bad", [dict(max_seqlen=-1), dict(n_segments=-2)])
+def test_prefill_ws_errors(bad):
+    kw = dict(max_seqlen=8, n_segments=0)
+    kw.update(bad)
+    rc = m.lib().ssm_scan_prefill_ws(ctypes.byref(D(4, 8, 16, 2)), 1, 4, kw["max_seqlen"],
+                                     kw["n_segments"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, 1, FAKE, None, 0, None)
+    assert rc == m.SSM_ERR_DIMS

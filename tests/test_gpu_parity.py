@@ -243,3 +243,67 @@ def test_graph_replay_matches_eager(ssm):
         torch.cuda.synchronize()
         assert torch.equal(yg, ye), rep
         assert torch.equal(g_in["state"], e_in["state"]), rep
+
+
+# ---------------------------------------------------------------- time-split prefill
+def test_split_prefill_headline(ssm, orc):
+    """1 x 4096 at H64 P64 N128 G8: the automatic plan cuts it into 4
+    segments; fresh and resuming start states."""
+    for fresh in (1, 0):
+        case = ssm_inputs.workload("prefill4096")
+        if not fresh:
+            case = ssm_inputs.make_case(64, 64, 128, 8, [4096], [0], seed=12)
+        plan = ssm.prefill_plan(case.H, case.P, case.N, case.G, 1, 4096)
+        say(f"split prefill 1x4096 fresh={fresh}: plan {plan}")
+        assert plan["segments"] == 4
+        y, st = run_gpu(case, "prefill_ws")
+        y32, st32 = orc.scan_case(case, precision="f32")
+        assert_parity(case, y, st, y32, st32, label=f"split 1x4096 fresh={fresh} vs fp32")
+        y64, st64 = orc.scan_case(case, precision="f64")
+        assert_parity(case, y, st, y64, st64, label=f"split 1x4096 fresh={fresh} vs fp64")
+
+
+@pytest.mark.parametrize("segments", [2, 3, 7])
+@pytest.mark.parametrize("max_seqlen", [150, 40])
+def test_split_prefill_mixed_batch(ssm, orc, segments, max_seqlen):
+    """The mixed edge batch (varlen, fresh/resume, NaN-poisoned fresh slots,
+    unused slots) cut into forced segments; max_seqlen 40 understates the
+    longest sequences (150), whose last segment then runs to the end."""
+    case = ssm_inputs.workload("mixed")
+    say(f"mixed split segments={segments} max_seqlen={max_seqlen}: "
+        f"{ssm.prefill_plan(case.H, case.P, case.N, case.G, 8, max_seqlen, segments)}")
+    y, st = run_gpu(case, "prefill_ws", max_seqlen=max_seqlen, segments=segments)
+    y32, st32 = orc.scan_case(case, precision="f32")
+    assert_parity(case, y, st, y32, st32)
+
+
+@pytest.mark.parametrize("N,P", [(1, 5), (8, 16), (32, 16), (33, 5), (64, 96), (100, 96), (128, 16), (128, 40), (1024, 16)])
+def test_split_prefill_shapes(ssm, orc, N, P):
+    lengths = [0, 1, 77, 200, 31]
+    case = ssm_inputs.make_case(4, P, N, 2, lengths, [1, 0, 0, 1, 0], seed=300 + N + P,
+                                slots=[6, 0, 2, 5, 3], n_slots=8, poison_fresh=True,
+                                sentinel_unused=True, name=f"split_N{N}_P{P}")
+    say(f"split shape N={N} P={P}")
+    y, st = run_gpu(case, "prefill_ws", segments=4)
+    y32, st32 = orc.scan_case(case, precision="f32")
+    assert_parity(case, y, st, y32, st32)
+    assert not np.any(st[6])
+
+
+def test_split_prefill_scalar_path(ssm, orc):
+    case = ssm_inputs.workload("mixed")
+    y, st = run_gpu(case, "prefill_ws", offset_floats=1, segments=3)
+    y32, st32 = orc.scan_case(case, precision="f32")
+    assert_parity(case, y, st, y32, st32, label="split scalar path")
+
+
+def test_split_prefill_small_workspace_falls_back(ssm, orc):
+    """Too small a workspace: the call runs unsplit and is still correct
+    (bitwise the plain prefill)."""
+    case = ssm_inputs.workload("tiny")
+    y, st = run_gpu(case, "prefill_ws", segments=3, workspace_bytes=64)
+    yp, stp = run_gpu(case, "prefill")
+    assert np.array_equal(y, yp) and np.array_equal(st, stp)
+    ys, sts = run_gpu(case, "prefill_ws", segments=3)
+    y32, st32 = orc.scan_case(case, precision="f32")
+    assert_parity(case, ys, sts, y32, st32, label="tiny split 3")
