@@ -39,18 +39,26 @@ class Oracle:
         self.path = path
         self.lib = ctypes.CDLL(path)
         common = [ctypes.c_int32] * 5 + [_i32p, _i32p, _u8p] + [_f32p] * 5
-        self.lib.ssm_oracle_scan_f32.argtypes = common + [_f32p, _f32p, ctypes.c_int32]
-        self.lib.ssm_oracle_scan_f32.restype = ctypes.c_int
-        self.lib.ssm_oracle_scan_f64.argtypes = common + [_f64p, _f64p, ctypes.c_int32]
-        self.lib.ssm_oracle_scan_f64.restype = ctypes.c_int
+        opts = [_f32p, ctypes.c_int32, ctypes.c_int32]
+        self.lib.ssm_oracle_scan_opt_f32.argtypes = (common + [_f32p, _f32p, ctypes.c_int32]
+                                                     + opts + [_f32p])
+        self.lib.ssm_oracle_scan_opt_f32.restype = ctypes.c_int
+        self.lib.ssm_oracle_scan_opt_f64.argtypes = (common + [_f64p, _f64p, ctypes.c_int32]
+                                                     + opts + [_f64p])
+        self.lib.ssm_oracle_scan_opt_f64.restype = ctypes.c_int
 
     def scan(self, H, P, N, G, cu_seqlens, slot, fresh, x, dt, A, B, C, state,
-             precision="f32", threads=None):
+             precision="f32", threads=None, dt_bias=None, dt_softplus=False,
+             A_per_state=False, snapshots=False):
         """Run the scan on a packed batch.
 
-        Returns ``(y, state_out)``; the input ``state`` is not modified.
-        precision "f32": fp32 arithmetic; "f64": double arithmetic on the same
-        fp32 inputs (y and state_out are float64 then).
+        Returns ``(y, state_out)``, or ``(y, state_out, snapshots)`` with
+        ``snapshots=True``; the input ``state`` is not modified.  precision
+        "f32": fp32 arithmetic; "f64": double arithmetic on the same fp32
+        inputs (outputs are float64 then).  Options: ``dt_bias`` [H] is added
+        to dt, ``dt_softplus`` applies softplus (identity above 20),
+        ``A_per_state`` takes A as [H][N], ``snapshots`` returns the state
+        after every token, [T][H][P][N].
         """
         cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
         slot = np.ascontiguousarray(slot, dtype=np.int32)
@@ -63,34 +71,39 @@ class Oracle:
         n_seqs = slot.shape[0]
         T = int(cu[-1]) if cu.shape[0] else 0
         assert cu.shape[0] == n_seqs + 1
-        assert x.shape == (T, H, P) and dt.shape == (T, H) and A.shape == (H,)
+        assert x.shape == (T, H, P) and dt.shape == (T, H)
+        assert A.shape == ((H, N) if A_per_state else (H,))
         assert B.shape == (T, G, N) and C.shape == (T, G, N)
         assert state.ndim == 4 and state.shape[1:] == (H, P, N)
+        bias = None
+        if dt_bias is not None:
+            bias = np.ascontiguousarray(dt_bias, dtype=np.float32)
+            assert bias.shape == (H,)
         if threads is None:
             threads = os.cpu_count() or 1
         if precision == "f32":
-            st = np.array(state, dtype=np.float32, copy=True, order="C")
-            y = np.zeros((T, H, P), dtype=np.float32)
-            fn, fp = self.lib.ssm_oracle_scan_f32, _f32p
+            dtype, fn, fp = np.float32, self.lib.ssm_oracle_scan_opt_f32, _f32p
         elif precision == "f64":
-            st = np.array(state, dtype=np.float64, copy=True, order="C")
-            y = np.zeros((T, H, P), dtype=np.float64)
-            fn, fp = self.lib.ssm_oracle_scan_f64, _f64p
+            dtype, fn, fp = np.float64, self.lib.ssm_oracle_scan_opt_f64, _f64p
         else:
             raise ValueError(precision)
+        st = np.array(state, dtype=dtype, copy=True, order="C")
+        y = np.zeros((T, H, P), dtype=dtype)
+        snaps = np.zeros((T, H, P, N), dtype=dtype) if snapshots else None
         rc = fn(H, P, N, G, n_seqs, _ptr(cu, _i32p), _ptr(slot, _i32p),
                 _ptr(fresh, _u8p), _ptr(x, _f32p), _ptr(dt, _f32p), _ptr(A, _f32p),
-                _ptr(B, _f32p), _ptr(C, _f32p), _ptr(st, fp), _ptr(y, fp),
-                int(threads))
+                _ptr(B, _f32p), _ptr(C, _f32p), _ptr(st, fp), _ptr(y, fp), int(threads),
+                None if bias is None else _ptr(bias, _f32p), int(bool(dt_softplus)),
+                int(bool(A_per_state)), None if snaps is None else _ptr(snaps, fp))
         if rc != 0:
             raise ValueError(f"oracle rejected the dimensions (rc={rc})")
-        return y, st
+        return (y, st, snaps) if snapshots else (y, st)
 
-    def scan_case(self, case, precision="f32", threads=None):
-        """``scan`` on an ``ssm_inputs.ScanCase``."""
+    def scan_case(self, case, precision="f32", threads=None, **options):
+        """``scan`` on an ``ssm_inputs.ScanCase`` (options as for ``scan``)."""
         return self.scan(case.H, case.P, case.N, case.G, case.cu_seqlens, case.slot,
                          case.fresh, case.x, case.dt, case.A, case.B, case.C,
-                         case.state, precision=precision, threads=threads)
+                         case.state, precision=precision, threads=threads, **options)
 
 
 _default = None

@@ -13,6 +13,8 @@ uses numpy.einsum.  Heads map to groups contiguously, g = head // (H // G).
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 
@@ -49,5 +51,47 @@ def brute_force(H, P, N, G, cu_seqlens, slot, fresh, x, dt, A, B, C, state):
                     decay[k, j] = np.prod(a[j + 1: k + 1])
             hs = lead[:, None, None] * h0[None] + np.einsum("kj,jp,jn->kpn", decay, u, Bs)
             y[t0:t1, hd, :] = np.einsum("kpn,kn->kp", hs, Cs)
+            st[slot[s], hd] = hs[-1]
+    return y, st
+
+
+def softplus_rule(v):
+    """softplus with the pages' cut-off: log1p(exp(v)) up to 20, v above."""
+    return math.log1p(math.exp(v)) if v <= 20.0 else v
+
+
+def brute_force_general(H, P, N, G, cu_seqlens, slot, fresh, x, dt_eff, A_hn, B, C, state):
+    """Unrolled closed form with a decay per (head, state index):
+    a_k[n] = exp(dt_eff_k * A[h][n]); h_t[p,n] = (prod a[n]) h_0[p,n] +
+    sum_j (prod_{r>j} a_r[n]) dt_eff_j x_j[p] B_j[n].  dt_eff [T][H] and
+    A_hn [H][N] are given in float64.  Returns (y, state_out) in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    dt_eff = np.asarray(dt_eff, dtype=np.float64)
+    A_hn = np.asarray(A_hn, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    C = np.asarray(C, dtype=np.float64)
+    st = np.array(state, dtype=np.float64, copy=True)
+    y = np.zeros((x.shape[0], H, P))
+    hpg = H // G
+    for s in range(len(slot)):
+        t0, t1 = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        L = t1 - t0
+        for hd in range(H):
+            g = hd // hpg
+            h0 = np.zeros((P, N)) if fresh[s] else st[slot[s], hd].copy()
+            if L == 0:
+                st[slot[s], hd] = h0
+                continue
+            a = np.exp(dt_eff[t0:t1, hd, None] * A_hn[None, hd, :])        # [L, N]
+            u = dt_eff[t0:t1, hd, None] * x[t0:t1, hd, :]                   # [L, P]
+            hs = np.zeros((L, P, N))
+            for k in range(L):
+                lead = np.prod(a[: k + 1], axis=0)                          # [N]
+                acc = lead[None, :] * h0
+                for j in range(k + 1):
+                    dec = np.prod(a[j + 1: k + 1], axis=0)                  # [N]
+                    acc = acc + dec[None, :] * np.outer(u[j], B[t0 + j, g])
+                hs[k] = acc
+            y[t0:t1, hd, :] = np.einsum("kpn,kn->kp", hs, C[t0:t1, g])
             st[slot[s], hd] = hs[-1]
     return y, st

@@ -13,7 +13,7 @@ import os
 import numpy as np
 
 import ssm_inputs
-from closed_form import brute_force
+from closed_form import brute_force, brute_force_general, softplus_rule
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
 
@@ -278,7 +278,84 @@ def pin_thread_count(orc):
     assert np.array_equal(y1, y8) and np.array_equal(st1, st8, equal_nan=True)
 
 
+# ------------------------------------------------------------ option pins
+def pin_softplus_single_token(orc):
+    """T = 1 from zero with dt_eff = softplus(dt + bias): y = dt_eff*x*(B.C),
+    h = dt_eff * x (outer) B; biases put dt + bias on both sides of the 20
+    cut-off (and right next to it); bias without softplus just adds."""
+    H, P, N, G = 6, 3, 5, 2
+    case = ssm_inputs.make_case(H, P, N, G, [1, 1], [1, 1], seed=31)
+    bias = np.array([-3.0, 0.5, 19.93, 20.05, 25.0, -0.2], np.float32)
+    for softplus in (True, False):
+        y64, st64 = orc.scan_case(case, precision="f64", dt_bias=bias, dt_softplus=softplus)
+        y32, st32 = orc.scan_case(case, precision="f32", dt_bias=bias, dt_softplus=softplus)
+        for s in range(2):
+            for hd in range(H):
+                v = float(case.dt[s, hd]) + float(bias[hd])
+                d = softplus_rule(v) if softplus else v
+                g = hd // (H // G)
+                b = case.B[s, g].astype(np.float64)
+                u = d * case.x[s, hd].astype(np.float64)
+                y_ref = u * math.fsum(b * case.C[s, g].astype(np.float64))
+                for y, st, tol in ((y64, st64, 1e-12), (y32, st32, 2e-6)):
+                    assert rel_err(y[s, hd], y_ref) < tol, (softplus, s, hd)
+                    assert rel_err(st[case.slot[s], hd], np.outer(u, b)) < tol, (softplus, s, hd)
+
+
+def pin_per_state_A_closed_form(orc):
+    """A per (head, state index): unrolled closed form with a decay per n, on
+    a packed batch with softplus and bias on as well."""
+    case = small_random_case(41, lengths=(5, 0, 7, 2), fresh=(1, 0, 0, 1), n_slots=5)
+    rng = np.random.Generator(np.random.PCG64(42))
+    A_hn = (-np.exp(rng.uniform(0.0, math.log(16.0), size=(case.H, case.N)))).astype(np.float32)
+    bias = rng.uniform(-2.0, 2.0, size=case.H).astype(np.float32)
+    dt_eff = np.array([[softplus_rule(float(case.dt[t, h]) + float(bias[h]))
+                        for h in range(case.H)] for t in range(case.n_tokens)])
+    y_bf, st_bf = brute_force_general(case.H, case.P, case.N, case.G, case.cu_seqlens, case.slot,
+                                      case.fresh, case.x, dt_eff, A_hn.astype(np.float64),
+                                      case.B, case.C, case.state)
+    kw = dict(dt_bias=bias, dt_softplus=True, A_per_state=True)
+    c2 = small_random_case(41, lengths=(5, 0, 7, 2), fresh=(1, 0, 0, 1), n_slots=5)
+    c2.A = A_hn
+    y64, st64 = orc.scan_case(c2, precision="f64", **kw)
+    y32, st32 = orc.scan_case(c2, precision="f32", **kw)
+    assert rel_err(y64, y_bf) < 1e-12 and rel_err(st64, st_bf) < 1e-12
+    assert rel_err(y32, y_bf) < 1e-5 and rel_err(st32, st_bf) < 1e-5
+
+
+def pin_per_state_A_constant_rows(orc):
+    """A[h][n] equal for every n gives the scalar-A scan, bit for bit."""
+    case = small_random_case(43)
+    y1, st1 = orc.scan_case(case, precision="f32")
+    c2 = small_random_case(43)
+    c2.A = np.repeat(case.A[:, None], case.N, axis=1)
+    y2, st2 = orc.scan_case(c2, precision="f32", A_per_state=True)
+    assert np.array_equal(y1, y2) and np.array_equal(st1, st2)
+
+
+def pin_snapshots(orc):
+    """Snapshots: the state after every token.  The last one of each sequence
+    is its final state, and the snapshot after token t equals the final state
+    of the same sequence run only through t (bit for bit)."""
+    case = small_random_case(47, lengths=(4, 1, 6), fresh=(0, 1, 0), n_slots=4)
+    y, st, snaps = orc.scan_case(case, precision="f32", snapshots=True)
+    y0, st0 = orc.scan_case(case, precision="f32")
+    assert np.array_equal(y, y0) and np.array_equal(st, st0)
+    for s in range(case.n_seqs):
+        t0, t1 = int(case.cu_seqlens[s]), int(case.cu_seqlens[s + 1])
+        assert np.array_equal(snaps[t1 - 1], st[case.slot[s]]), s
+        for t in range(t0, t1):
+            part = ssm_inputs.ScanCase(
+                H=case.H, P=case.P, N=case.N, G=case.G, lengths=np.array([t + 1 - t0], np.int32),
+                cu_seqlens=np.array([0, t + 1 - t0], np.int32), slot=case.slot[s:s + 1],
+                fresh=case.fresh[s:s + 1], x=case.x[t0:t + 1], dt=case.dt[t0:t + 1], A=case.A,
+                B=case.B[t0:t + 1], C=case.C[t0:t + 1], state=case.state)
+            _, stp = orc.scan_case(part, precision="f32")
+            assert np.array_equal(snaps[t], stp[case.slot[s]]), (s, t)
+
+
 ALL_PINS = [pin_hand_worked, pin_brute_force, pin_brute_force_tiny_workload,
             pin_single_token_dot, pin_prefix_sum, pin_decay_only, pin_split_resume,
             pin_batch_independence, pin_linearity, pin_group_equivalence,
-            pin_slot_hygiene, pin_thread_count]
+            pin_slot_hygiene, pin_thread_count, pin_softplus_single_token,
+            pin_per_state_A_closed_form, pin_per_state_A_constant_rows, pin_snapshots]
