@@ -126,9 +126,51 @@ int ssm_scan_prefill_ws(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tok
                         size_t workspace_bytes, void *stream);
 
 /* Workspace bytes ssm_scan_prefill_ws needs for these sizes (0 if it would not
- * split).  Touches no device. */
+ * split).  Touches no device.  The same size serves ssm_scan_prefill_opt, which
+ * ignores the workspace when its options force a whole-sequence scan. */
 int ssm_scan_prefill_workspace_size(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens,
                                     int32_t max_seqlen, int32_t n_segments, size_t *bytes);
+
+/*
+ * Options of ssm_scan_prefill_opt / ssm_scan_decode_opt (a NULL pointer to
+ * this struct, or a zeroed one, is the plain scan):
+ *   dt_bias      [H] device array or NULL: dt_eff = dt + dt_bias[head]
+ *   dt_softplus  1: dt_eff = softplus(dt_eff) = log1p(exp(dt_eff)) for
+ *                dt_eff <= 20 and dt_eff itself above -- the rule of ggml's scan
+ *                kernels ("The llama journey", Day 11 and Day 14) and of
+ *                Foundry's decay gate ("ssm_gated_delta.cu", fc_ssm_decay_gate)
+ *   a_per_state  1: A is [H][N] and element n of a head decays by
+ *                exp(dt_eff * A[head][n]) -- the Mamba1 form of ggml's CPU
+ *                table (Day 12) and kernel (Day 11); 0: A is [H]
+ *   snapshots    [n_tokens][H][P][N] device array or NULL: receives the state
+ *                after every token, in packed token order, for rolling back a
+ *                partly accepted speculative draft ("ssm_gated_delta.cu", the
+ *                snaps argument of the scan kernels)
+ * dt_eff replaces dt everywhere (decay and input scaling).  a_per_state or
+ * snapshots make ssm_scan_prefill_opt scan whole sequences (no time split).
+ * Pointers must be 4-byte aligned (16 for the vector path), like the others.
+ */
+typedef struct ssm_scan_options {
+    const float *dt_bias;
+    int32_t dt_softplus;
+    int32_t a_per_state;
+    float *snapshots;
+} ssm_scan_options;
+
+/* ssm_scan_prefill_ws with options (opts may be NULL). */
+int ssm_scan_prefill_opt(const ssm_scan_dims *dims, const ssm_scan_options *opts, int32_t n_seqs,
+                         int32_t n_tokens, int32_t max_seqlen, int32_t n_segments,
+                         const int32_t *cu_seqlens, const int32_t *slot, const uint8_t *fresh,
+                         const float *x, const float *dt, const float *A, const float *B,
+                         const float *C, float *state, int32_t n_slots, float *y, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/* ssm_scan_decode with options (opts may be NULL; snapshots then has one
+ * entry per sequence, equal to the state written to its slot). */
+int ssm_scan_decode_opt(const ssm_scan_dims *dims, const ssm_scan_options *opts, int32_t n_seqs,
+                        const int32_t *slot, const uint8_t *fresh, const float *x,
+                        const float *dt, const float *A, const float *B, const float *C,
+                        float *state, int32_t n_slots, float *y, void *stream);
 
 /*
  * Decode: one token for each of n_seqs sequences (token s belongs to sequence

@@ -59,6 +59,11 @@ class Dims(ctypes.Structure):
                 ("d_state", ctypes.c_int32), ("n_groups", ctypes.c_int32)]
 
 
+class Options(ctypes.Structure):
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int32),
+                ("a_per_state", ctypes.c_int32), ("snapshots", ctypes.c_void_p)]
+
+
 class Geometry(ctypes.Structure):
     _fields_ = [("lanes_per_row", ctypes.c_int32), ("elems_per_lane", ctypes.c_int32),
                 ("rows_per_block", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
@@ -98,6 +103,13 @@ _lib.ssm_scan_prefill_workspace_size.restype = ctypes.c_int
 _lib.ssm_scan_prefill_ws.argtypes = ([ctypes.POINTER(Dims), _i32, _i32, _i32, _i32] + [_vp] * 9
                                      + [_i32, _vp, _vp, ctypes.c_size_t, _vp])
 _lib.ssm_scan_prefill_ws.restype = ctypes.c_int
+_lib.ssm_scan_prefill_opt.argtypes = ([ctypes.POINTER(Dims), ctypes.POINTER(Options), _i32, _i32,
+                                       _i32, _i32] + [_vp] * 9
+                                      + [_i32, _vp, _vp, ctypes.c_size_t, _vp])
+_lib.ssm_scan_prefill_opt.restype = ctypes.c_int
+_lib.ssm_scan_decode_opt.argtypes = ([ctypes.POINTER(Dims), ctypes.POINTER(Options), _i32]
+                                     + [_vp] * 8 + [_i32, _vp, _vp])
+_lib.ssm_scan_decode_opt.restype = ctypes.c_int
 
 
 class ScanError(RuntimeError):
@@ -196,6 +208,20 @@ def _dev_ptr(t, dtype, name, device):
     return t.data_ptr() if t.numel() else None
 
 
+def _options(dev, T, H, P, N, dt_bias, dt_softplus, A_per_state, snapshots):
+    """The ssm_scan_options struct for these keyword options, or None if all
+    are off."""
+    import torch
+    if dt_bias is None and not dt_softplus and not A_per_state and snapshots is None:
+        return None
+    if dt_bias is not None and tuple(dt_bias.shape) != (H,):
+        raise ValueError("dt_bias must have shape [H]")
+    if snapshots is not None and tuple(snapshots.shape) != (T, H, P, N):
+        raise ValueError("snapshots must have shape [T, H, P, N]")
+    return Options(_dev_ptr(dt_bias, torch.float32, "dt_bias", dev), int(bool(dt_softplus)),
+                   int(bool(A_per_state)), _dev_ptr(snapshots, torch.float32, "snapshots", dev))
+
+
 def _stream_handle(stream, device):
     import torch
     if stream is None:
@@ -203,20 +229,32 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def prefill(x, dt, A, B, C, state, cu_seqlens, slot, fresh, y=None, stream=None):
-    """Scan a packed batch on the GPU (``ssm_scan_prefill``).
+def prefill(x, dt, A, B, C, state, cu_seqlens, slot, fresh, y=None, stream=None,
+            dt_bias=None, dt_softplus=False, A_per_state=False, snapshots=None):
+    """Scan a packed batch on the GPU (``ssm_scan_prefill``), one pass per
+    sequence.
 
-    x [T, H, P], dt [T, H], A [H], B and C [T, G, N] fp32; state
-    [n_slots, H, P, N] fp32 (updated in place); cu_seqlens [n_seqs+1] and
-    slot [n_seqs] int32; fresh [n_seqs] uint8.  Returns y [T, H, P] (``y`` if
-    given).  Enqueued on ``stream`` (default: the current stream), no sync.
+    x [T, H, P], dt [T, H], A [H] (or [H, N] with ``A_per_state``), B and C
+    [T, G, N] fp32; state [n_slots, H, P, N] fp32 (updated in place);
+    cu_seqlens [n_seqs+1] and slot [n_seqs] int32; fresh [n_seqs] uint8.
+    Options (``ssm_scan_prefill_opt``): ``dt_bias`` [H], ``dt_softplus``,
+    ``A_per_state``, ``snapshots`` [T, H, P, N] fp32 output.  Returns y
+    [T, H, P] (``y`` if given).  Enqueued on ``stream`` (default: the current
+    stream), no sync.
     """
+    return _prefill_any(x, dt, A, B, C, state, cu_seqlens, slot, fresh, 0, 1, None, y, stream,
+                        dt_bias, dt_softplus, A_per_state, snapshots)
+
+
+def _prefill_any(x, dt, A, B, C, state, cu_seqlens, slot, fresh, max_seqlen, segments,
+                 workspace, y, stream, dt_bias, dt_softplus, A_per_state, snapshots):
     import torch
     n_slots, H, P, N = (int(v) for v in state.shape)
     T = int(x.shape[0])
     G = int(B.shape[1])
     n_seqs = int(slot.shape[0])
-    if tuple(x.shape) != (T, H, P) or tuple(dt.shape) != (T, H) or tuple(A.shape) != (H,):
+    a_shape = (H, N) if A_per_state else (H,)
+    if tuple(x.shape) != (T, H, P) or tuple(dt.shape) != (T, H) or tuple(A.shape) != a_shape:
         raise ValueError("x, dt or A has the wrong shape")
     if tuple(B.shape) != (T, G, N) or tuple(C.shape) != (T, G, N):
         raise ValueError("B or C has the wrong shape")
@@ -227,70 +265,63 @@ def prefill(x, dt, A, B, C, state, cu_seqlens, slot, fresh, y=None, stream=None)
         y = torch.empty((T, H, P), dtype=torch.float32, device=dev)
     elif tuple(y.shape) != (T, H, P):
         raise ValueError("y has the wrong shape")
+    opts = _options(dev, T, H, P, N, dt_bias, dt_softplus, A_per_state, snapshots)
     f32, i32 = torch.float32, torch.int32
-    rc = _lib.ssm_scan_prefill(
-        ctypes.byref(Dims(H, P, N, G)), n_seqs, T,
-        _dev_ptr(cu_seqlens, i32, "cu_seqlens", dev), _dev_ptr(slot, i32, "slot", dev),
-        _dev_ptr(fresh, torch.uint8, "fresh", dev), _dev_ptr(x, f32, "x", dev),
-        _dev_ptr(dt, f32, "dt", dev), _dev_ptr(A, f32, "A", dev), _dev_ptr(B, f32, "B", dev),
-        _dev_ptr(C, f32, "C", dev), _dev_ptr(state, f32, "state", dev), n_slots,
-        _dev_ptr(y, f32, "y", dev), _stream_handle(stream, dev))
-    _check(rc, "ssm_scan_prefill")
+    args = (_dev_ptr(cu_seqlens, i32, "cu_seqlens", dev), _dev_ptr(slot, i32, "slot", dev),
+            _dev_ptr(fresh, torch.uint8, "fresh", dev), _dev_ptr(x, f32, "x", dev),
+            _dev_ptr(dt, f32, "dt", dev), _dev_ptr(A, f32, "A", dev), _dev_ptr(B, f32, "B", dev),
+            _dev_ptr(C, f32, "C", dev), _dev_ptr(state, f32, "state", dev), n_slots,
+            _dev_ptr(y, f32, "y", dev))
+    if opts is None and max_seqlen == 0:
+        rc = _lib.ssm_scan_prefill(ctypes.byref(Dims(H, P, N, G)), n_seqs, T, *args,
+                                   _stream_handle(stream, dev))
+        _check(rc, "ssm_scan_prefill")
+        return y
+    ws_ptr, ws_bytes = None, 0
+    if max_seqlen:
+        need = workspace_size(H, P, N, G, n_seqs, T, max_seqlen, segments)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if workspace is not None:
+            ws_ptr = _dev_ptr(workspace, torch.uint8, "workspace", dev)
+            ws_bytes = int(workspace.numel())
+    rc = _lib.ssm_scan_prefill_opt(ctypes.byref(Dims(H, P, N, G)),
+                                   None if opts is None else ctypes.byref(opts), n_seqs, T,
+                                   int(max_seqlen), int(segments), *args, ws_ptr, ws_bytes,
+                                   _stream_handle(stream, dev))
+    _check(rc, "ssm_scan_prefill_opt")
     return y
 
 
 def prefill_ws(x, dt, A, B, C, state, cu_seqlens, slot, fresh, max_seqlen, segments=0,
-               workspace=None, y=None, stream=None):
-    """``ssm_scan_prefill_ws``: like ``prefill``, but long sequences may be
-    split over time when the batch is too small to fill the GPU.
-    ``max_seqlen`` (host int) bounds the sequence lengths; ``segments`` 0 =
-    automatic, 1 = never split, k = about k segments.  ``workspace`` (a uint8
-    CUDA tensor of at least ``workspace_size(...)`` bytes) is allocated here
-    when not given."""
-    import torch
-    n_slots, H, P, N = (int(v) for v in state.shape)
-    T = int(x.shape[0])
-    G = int(B.shape[1])
-    n_seqs = int(slot.shape[0])
-    if tuple(x.shape) != (T, H, P) or tuple(dt.shape) != (T, H) or tuple(A.shape) != (H,):
-        raise ValueError("x, dt or A has the wrong shape")
-    if tuple(B.shape) != (T, G, N) or tuple(C.shape) != (T, G, N):
-        raise ValueError("B or C has the wrong shape")
-    if tuple(cu_seqlens.shape) != (n_seqs + 1,) or tuple(fresh.shape) != (n_seqs,):
-        raise ValueError("cu_seqlens or fresh has the wrong shape")
-    dev = state.device
-    if y is None:
-        y = torch.empty((T, H, P), dtype=torch.float32, device=dev)
-    elif tuple(y.shape) != (T, H, P):
-        raise ValueError("y has the wrong shape")
-    need = workspace_size(H, P, N, G, n_seqs, T, max_seqlen, segments)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_ptr = _dev_ptr(workspace, torch.uint8, "workspace", dev) if workspace is not None else None
-    ws_bytes = int(workspace.numel()) if workspace is not None else 0
-    f32, i32 = torch.float32, torch.int32
-    rc = _lib.ssm_scan_prefill_ws(
-        ctypes.byref(Dims(H, P, N, G)), n_seqs, T, int(max_seqlen), int(segments),
-        _dev_ptr(cu_seqlens, i32, "cu_seqlens", dev), _dev_ptr(slot, i32, "slot", dev),
-        _dev_ptr(fresh, torch.uint8, "fresh", dev), _dev_ptr(x, f32, "x", dev),
-        _dev_ptr(dt, f32, "dt", dev), _dev_ptr(A, f32, "A", dev), _dev_ptr(B, f32, "B", dev),
-        _dev_ptr(C, f32, "C", dev), _dev_ptr(state, f32, "state", dev), n_slots,
-        _dev_ptr(y, f32, "y", dev), ws_ptr, ws_bytes, _stream_handle(stream, dev))
-    _check(rc, "ssm_scan_prefill_ws")
-    return y
+               workspace=None, y=None, stream=None, dt_bias=None, dt_softplus=False,
+               A_per_state=False, snapshots=None):
+    """``ssm_scan_prefill_opt`` / ``ssm_scan_prefill_ws``: like ``prefill``, but
+    long sequences may be split over time when the batch is too small to fill
+    the GPU.  ``max_seqlen`` (host int) bounds the sequence lengths;
+    ``segments`` 0 = automatic, 1 = never split, k = about k segments.
+    ``workspace`` (a uint8 CUDA tensor of at least ``workspace_size(...)``
+    bytes) is allocated here when not given.  Options as for ``prefill``."""
+    return _prefill_any(x, dt, A, B, C, state, cu_seqlens, slot, fresh, max(int(max_seqlen), 0),
+                        segments, workspace, y, stream, dt_bias, dt_softplus, A_per_state,
+                        snapshots)
 
 
-def decode(x, dt, A, B, C, state, slot, fresh, y=None, stream=None):
-    """One token per sequence on the GPU (``ssm_scan_decode``).
+def decode(x, dt, A, B, C, state, slot, fresh, y=None, stream=None, dt_bias=None,
+           dt_softplus=False, A_per_state=False, snapshots=None):
+    """One token per sequence on the GPU (``ssm_scan_decode``, or
+    ``ssm_scan_decode_opt`` with options).
 
-    x [S, H, P], dt [S, H], A [H], B and C [S, G, N]; state as for prefill;
-    slot [S] int32, fresh [S] uint8.  Returns y [S, H, P].
+    x [S, H, P], dt [S, H], A [H] (or [H, N]), B and C [S, G, N]; state as for
+    prefill; slot [S] int32, fresh [S] uint8; snapshots [S, H, P, N].
+    Returns y [S, H, P].
     """
     import torch
     n_slots, H, P, N = (int(v) for v in state.shape)
     S = int(slot.shape[0])
     G = int(B.shape[1])
-    if tuple(x.shape) != (S, H, P) or tuple(dt.shape) != (S, H) or tuple(A.shape) != (H,):
+    a_shape = (H, N) if A_per_state else (H,)
+    if tuple(x.shape) != (S, H, P) or tuple(dt.shape) != (S, H) or tuple(A.shape) != a_shape:
         raise ValueError("x, dt or A has the wrong shape")
     if tuple(B.shape) != (S, G, N) or tuple(C.shape) != (S, G, N):
         raise ValueError("B or C has the wrong shape")
@@ -301,14 +332,19 @@ def decode(x, dt, A, B, C, state, slot, fresh, y=None, stream=None):
         y = torch.empty((S, H, P), dtype=torch.float32, device=dev)
     elif tuple(y.shape) != (S, H, P):
         raise ValueError("y has the wrong shape")
+    opts = _options(dev, S, H, P, N, dt_bias, dt_softplus, A_per_state, snapshots)
     f32 = torch.float32
-    rc = _lib.ssm_scan_decode(
-        ctypes.byref(Dims(H, P, N, G)), S, _dev_ptr(slot, torch.int32, "slot", dev),
-        _dev_ptr(fresh, torch.uint8, "fresh", dev), _dev_ptr(x, f32, "x", dev),
-        _dev_ptr(dt, f32, "dt", dev), _dev_ptr(A, f32, "A", dev), _dev_ptr(B, f32, "B", dev),
-        _dev_ptr(C, f32, "C", dev), _dev_ptr(state, f32, "state", dev), n_slots,
-        _dev_ptr(y, f32, "y", dev), _stream_handle(stream, dev))
-    _check(rc, "ssm_scan_decode")
+    args = (_dev_ptr(slot, torch.int32, "slot", dev), _dev_ptr(fresh, torch.uint8, "fresh", dev),
+            _dev_ptr(x, f32, "x", dev), _dev_ptr(dt, f32, "dt", dev), _dev_ptr(A, f32, "A", dev),
+            _dev_ptr(B, f32, "B", dev), _dev_ptr(C, f32, "C", dev),
+            _dev_ptr(state, f32, "state", dev), n_slots, _dev_ptr(y, f32, "y", dev),
+            _stream_handle(stream, dev))
+    if opts is None:
+        rc = _lib.ssm_scan_decode(ctypes.byref(Dims(H, P, N, G)), S, *args)
+        _check(rc, "ssm_scan_decode")
+    else:
+        rc = _lib.ssm_scan_decode_opt(ctypes.byref(Dims(H, P, N, G)), ctypes.byref(opts), S, *args)
+        _check(rc, "ssm_scan_decode_opt")
     return y
 
 

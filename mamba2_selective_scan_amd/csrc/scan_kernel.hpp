@@ -73,7 +73,24 @@ struct ScanArgs {
     float *ws_state;             // [n_seqs][n_segs][H][P][N] segment end / carried-in states
     float *ws_dtot;              // [n_seqs][n_segs][H] product of dA over each segment
     float *ws_dcum;              // [T][H] product of dA from the segment start through t
+    // Options.  dt_eff = dt + dt_bias[h] (if given), then softplus (identity
+    // above 20) if dt_softplus; with OPT_A_PER_STATE A is [H][N]; with
+    // OPT_SNAPSHOTS the state after every token goes to snapshots.
+    const float *dt_bias;        // [H] or null
+    int32_t dt_softplus;
+    float *snapshots;            // [T][H][P][N]
 };
+
+// Compile-time option bits of a prefill/decode kernel instance.
+constexpr int OPT_A_PER_STATE = 1;
+constexpr int OPT_SNAPSHOTS = 2;
+
+// dt after the optional bias and softplus: log1p(exp(v)) up to 20, v above.
+__device__ __forceinline__ float dt_transform(float v, float bias, int softplus) {
+    v += bias;
+    if (softplus && v <= 20.0f) v = log1pf(expf(v));
+    return v;
+}
 
 enum class Mode { kPrefill, kSegScan, kDecode, kCorrect };
 
@@ -166,6 +183,12 @@ __device__ __forceinline__ f4 load4(const float *p, int n_valid) {
 
 __device__ __forceinline__ int clamp4(int v) { return v < 0 ? 0 : (v > 4 ? 4 : v); }
 
+// One state element: h <- h*dA + b*x_dt, with the rounding spelled out (one
+// product rounded, then a fused multiply-add) so every caller gets the same bits.
+__device__ __forceinline__ float step(float h, float dA, float b, float x_dt) {
+    return __builtin_fmaf(b, x_dt, h * dA);
+}
+
 // One token of the recurrence for the lane's E = 4J state elements, given the
 // lane's J 4-groups of B and C for the token.  Returns the lane's partial y.
 // Prefill and decode both go through here, so their arithmetic is identical.
@@ -176,14 +199,36 @@ __device__ __forceinline__ float update_token(float (&h)[4 * J], const f4 (&b)[J
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         float *hj = h + 4 * j;
-        hj[0] = hj[0] * dA + b[j].x * x_dt;
-        hj[1] = hj[1] * dA + b[j].y * x_dt;
-        hj[2] = hj[2] * dA + b[j].z * x_dt;
-        hj[3] = hj[3] * dA + b[j].w * x_dt;
-        acc0 += hj[0] * c[j].x;
-        acc1 += hj[1] * c[j].y;
-        acc0 += hj[2] * c[j].z;
-        acc1 += hj[3] * c[j].w;
+        hj[0] = step(hj[0], dA, b[j].x, x_dt);
+        hj[1] = step(hj[1], dA, b[j].y, x_dt);
+        hj[2] = step(hj[2], dA, b[j].z, x_dt);
+        hj[3] = step(hj[3], dA, b[j].w, x_dt);
+        acc0 = __builtin_fmaf(hj[0], c[j].x, acc0);
+        acc1 = __builtin_fmaf(hj[1], c[j].y, acc1);
+        acc0 = __builtin_fmaf(hj[2], c[j].z, acc0);
+        acc1 = __builtin_fmaf(hj[3], c[j].w, acc1);
+    }
+    return acc0 + acc1;
+}
+
+// The same with a decay per state element (A per (head, n)): dA[e] for the
+// lane's E elements.
+template <int J>
+__device__ __forceinline__ float update_token_pe(float (&h)[4 * J], const f4 (&b)[J], const f4 (&c)[J],
+                                                 const float (&dA)[4 * J], float x_dt) {
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        float *hj = h + 4 * j;
+        const float *dj = dA + 4 * j;
+        hj[0] = step(hj[0], dj[0], b[j].x, x_dt);
+        hj[1] = step(hj[1], dj[1], b[j].y, x_dt);
+        hj[2] = step(hj[2], dj[2], b[j].z, x_dt);
+        hj[3] = step(hj[3], dj[3], b[j].w, x_dt);
+        acc0 = __builtin_fmaf(hj[0], c[j].x, acc0);
+        acc1 = __builtin_fmaf(hj[1], c[j].y, acc1);
+        acc0 = __builtin_fmaf(hj[2], c[j].z, acc0);
+        acc1 = __builtin_fmaf(hj[3], c[j].w, acc1);
     }
     return acc0 + acc1;
 }
@@ -220,7 +265,7 @@ __device__ __forceinline__ SegRange segment_range(const ScanArgs &a, int s, int 
 // MODE kDecode: one token per sequence, B/C/x/dt read straight into registers.
 // MODE kCorrect: for a time segment k >= 1, add the carried-in state's
 //   contribution dcum[t] * (C_t . carry) to the y the segment scan wrote.
-template <class S, bool VEC, Mode MODE>
+template <class S, bool VEC, Mode MODE, int OPT = 0>
 __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     extern __shared__ float4 lds_raw[];
     float *const lds = reinterpret_cast<float *>(lds_raw);
@@ -229,6 +274,10 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     constexpr bool DECODE = MODE == Mode::kDecode;
     constexpr bool CORRECT = MODE == Mode::kCorrect;
     constexpr bool SEGMENTED = MODE == Mode::kSegScan || CORRECT;   // grid has a segment axis
+    constexpr bool A_PER_STATE = (OPT & OPT_A_PER_STATE) != 0;
+    constexpr bool SNAPSHOTS = (OPT & OPT_SNAPSHOTS) != 0;
+    static_assert(OPT == 0 || MODE == Mode::kPrefill || MODE == Mode::kDecode,
+                  "options are built for whole-sequence prefill and decode only");
 
     // ---- workgroup -> (sequence, segment, head, row block); XCD-contiguous order
     const int bid = blockIdx.x;
@@ -280,12 +329,40 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     // where the state comes from: the slot; for a correction, the state carried
     // into this segment (the combine pass left it in the previous entry)
     float *const src_block = CORRECT ? ws_block - hpn : st_block;
-    const float A_h = a.A[hd];
-
-    // ---- state -> registers
+    const float A_h = A_PER_STATE ? 0.f : a.A[hd];
+    const float bias_h = a.dt_bias ? a.dt_bias[hd] : 0.f;
+    // A per state element: this lane's E values of A[hd][n] (0 past N)
+    float Ae[A_PER_STATE ? E : 1];
+    if constexpr (A_PER_STATE) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int n0 = 4 * (j * R + r);
+            const f4 v = load4<false>(a.A + int64_t(hd) * N + n0, clamp4(N - n0));
+            Ae[4 * j + 0] = v.x; Ae[4 * j + 1] = v.y; Ae[4 * j + 2] = v.z; Ae[4 * j + 3] = v.w;
+        }
+    }
     float h[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) h[e] = 0.f;
+    // the state after token t, to the snapshot buffer
+    auto snapshot = [&](int t) {
+        float *dst = a.snapshots + (int64_t(t) * H + hd) * P * int64_t(N) + int64_t(p0 + i) * N;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int n0 = 4 * (j * R + r);
+            const int nv = row_ok ? clamp4(N - n0) : 0;
+            if constexpr (VEC) {
+                if (nv > 0) *reinterpret_cast<f4 *>(dst + n0) = f4{h[4 * j + 0], h[4 * j + 1], h[4 * j + 2], h[4 * j + 3]};
+            } else {
+                if (nv > 0) dst[n0 + 0] = h[4 * j + 0];
+                if (nv > 1) dst[n0 + 1] = h[4 * j + 1];
+                if (nv > 2) dst[n0 + 2] = h[4 * j + 2];
+                if (nv > 3) dst[n0 + 3] = h[4 * j + 3];
+            }
+        }
+    };
+
+    // ---- state -> registers
     if (!fresh) {
         if constexpr (VEC) {
 #pragma unroll
@@ -331,11 +408,20 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
             bl[j] = load4<VEC>(a.B + bc + n0, nv);
             cl[j] = load4<VEC>(a.C + bc + n0, nv);
         }
-        const float dt = a.dt[int64_t(s) * H + hd];
+        const float dt = dt_transform(a.dt[int64_t(s) * H + hd], bias_h, a.dt_softplus);
         const float x = row_ok ? a.x[(int64_t(s) * H + hd) * P + p0 + i] : 0.f;
-        const float dA = expf(dt * A_h);
-        const float yv = row_allreduce<R>(update_token<J>(h, bl, cl, dA, x * dt));
+        float part;
+        if constexpr (A_PER_STATE) {
+            float dAe[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) dAe[e] = __expf(dt * Ae[e]);
+            part = update_token_pe<J>(h, bl, cl, dAe, x * dt);
+        } else {
+            part = update_token<J>(h, bl, cl, expf(dt * A_h), x * dt);
+        }
+        const float yv = row_allreduce<R>(part);
         if (r == 0 && row_ok) a.y[(int64_t(s) * H + hd) * P + p0 + i] = yv;
+        if constexpr (SNAPSHOTS) snapshot(s);
     } else {
         // All state loads are complete before the chunk pipeline starts, so the
         // token loop never waits on the next chunk's prefetch.
@@ -372,7 +458,8 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                 const int nv = ok ? clamp4(rows_valid - pi) : 0;
                 px[u] = load4<VEC>(xsrc + (int64_t(t0 + tt) * H + hd) * P + p0 + pi, nv);
             }
-            pdt = (tid < nt) ? a.dt[int64_t(t0 + tid) * H + hd] : 0.f;
+            pdt = (tid < nt) ? dt_transform(a.dt[int64_t(t0 + tid) * H + hd], bias_h, a.dt_softplus)
+                             : 0.f;
         };
 
         float run = 1.f;                                    // wave 0: dA product so far
@@ -424,6 +511,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         // instructions and the keep-select needs no runtime compare.
         constexpr int KY = R < 16 ? R : 16;
         const int rk = r % KY;
+        int chunk_t0 = 0;                                   // first token of the chunk in compute
         auto token_y = [&](const float *base, int tt) -> float {
             f4 cv[J];
             lds_groups<R, J>(cv, base + S::OFF_C + 4 * r + tt * NP);
@@ -442,8 +530,19 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
             } else {
                 f4 bv[J];
                 lds_groups<R, J>(bv, base + S::OFF_B + 4 * r + tt * NP);
-                return row_allreduce<R>(update_token<J>(
-                    h, bv, cv, base[S::OFF_DA + tt], base[S::OFF_X + tt * RB + i] * base[S::OFF_DT + tt]));
+                const float dt = base[S::OFF_DT + tt];
+                const float x_dt = base[S::OFF_X + tt * RB + i] * dt;
+                float part;
+                if constexpr (A_PER_STATE) {
+                    float dAe[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) dAe[e] = __expf(dt * Ae[e]);
+                    part = update_token_pe<J>(h, bv, cv, dAe, x_dt);
+                } else {
+                    part = update_token<J>(h, bv, cv, base[S::OFF_DA + tt], x_dt);
+                }
+                if constexpr (SNAPSHOTS) snapshot(chunk_t0 + tt);
+                return row_allreduce<R>(part);
             }
         };
         auto compute = [&](int buf, int nt) {
@@ -505,6 +604,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
             const bool has_next = c + 1 < n_chunks;
             if (has_next) issue_loads(t0 + CT, min(CT, t_end - t0 - CT));
             if (c > 0) flush_y(buf ^ 1, t0 - CT, CT);    // previous chunk, always full
+            chunk_t0 = t0;
             compute(buf, nt);
             if (has_next) commit(buf ^ 1, t0 + CT, min(CT, t_end - t0 - CT));
             __syncthreads();

@@ -61,9 +61,9 @@ int hip_fail(hipError_t err, int code) {
     return code;
 }
 
-template <class S, bool VEC, Mode MODE>
+template <class S, bool VEC, Mode MODE, int OPT = 0>
 int launch(const ScanArgs &a, hipStream_t stream) {
-    const void *kern = reinterpret_cast<const void *>(&ssm::scan_kernel<S, VEC, MODE>);
+    const void *kern = reinterpret_cast<const void *>(&ssm::scan_kernel<S, VEC, MODE, OPT>);
     const int lds_bytes = S::lds_floats(MODE, VEC) * int(sizeof(float));
     if (lds_bytes > 64 * 1024) {
         // Opt in to more than 64 KB of dynamic LDS, once per device.
@@ -107,21 +107,31 @@ enum class Kind { kPrefill, kDecode, kSegScan, kCorrect };
 
 constexpr int seg_chunk(int CT) { return CT / 2 > 2 ? CT / 2 : 2; }
 
+// Whole-sequence prefill or decode with option bits OPT (A per state element,
+// snapshots), vector or scalar path.
+template <class S, Mode MODE>
+int launch_opt(const ScanArgs &a, bool vec, int opt, hipStream_t stream) {
+    switch (opt) {
+    case 0: return vec ? launch<S, true, MODE, 0>(a, stream) : launch<S, false, MODE, 0>(a, stream);
+    case 1: return vec ? launch<S, true, MODE, 1>(a, stream) : launch<S, false, MODE, 1>(a, stream);
+    case 2: return vec ? launch<S, true, MODE, 2>(a, stream) : launch<S, false, MODE, 2>(a, stream);
+    case 3: return vec ? launch<S, true, MODE, 3>(a, stream) : launch<S, false, MODE, 3>(a, stream);
+    default: return SSM_ERR_UNSUPPORTED;
+    }
+}
+
 struct Launch {
     const ScanArgs &a;
     bool vec;
     Kind kind;
     hipStream_t stream;
+    int opt;
     template <int R, int J, int CT, int DR, int DJ>
     int run() const {
         constexpr int SCT = seg_chunk(CT);
         switch (kind) {
-        case Kind::kDecode:
-            return vec ? launch<Shape<DR, DJ, 1>, true, Mode::kDecode>(a, stream)
-                       : launch<Shape<DR, DJ, 1>, false, Mode::kDecode>(a, stream);
-        case Kind::kPrefill:
-            return vec ? launch<Shape<R, J, CT>, true, Mode::kPrefill>(a, stream)
-                       : launch<Shape<R, J, CT>, false, Mode::kPrefill>(a, stream);
+        case Kind::kDecode: return launch_opt<Shape<DR, DJ, 1>, Mode::kDecode>(a, vec, opt, stream);
+        case Kind::kPrefill: return launch_opt<Shape<R, J, CT>, Mode::kPrefill>(a, vec, opt, stream);
         case Kind::kSegScan:
             return vec ? launch<Shape<R, J, SCT>, true, Mode::kSegScan>(a, stream)
                        : launch<Shape<R, J, SCT>, false, Mode::kSegScan>(a, stream);
@@ -227,10 +237,16 @@ WsLayout ws_layout(const ssm_scan_dims *d, int32_t n_seqs, int32_t n_tokens, int
 // plan.n_segs > 1, `ws` (256-byte aligned, ws_layout() bytes) receives the
 // segment end states, their total and running decays, and three kernels run:
 // segment scans, the combine pass and the corrections.
-int scan_common(const ssm_scan_dims *d, int32_t n_seqs, int32_t n_tokens,
-                const int32_t *cu_seqlens, const int32_t *slot, const uint8_t *fresh,
-                const float *x, const float *dt, const float *A, const float *B, const float *C,
-                float *state, float *y, bool decode, SegPlan plan, char *ws, void *stream_ptr) {
+int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_seqs,
+                int32_t n_tokens, const int32_t *cu_seqlens, const int32_t *slot,
+                const uint8_t *fresh, const float *x, const float *dt, const float *A,
+                const float *B, const float *C, float *state, float *y, bool decode,
+                SegPlan plan, char *ws, void *stream_ptr) {
+    const ssm_scan_options none{};
+    if (!opts) opts = &none;
+    const int opt = (opts->a_per_state ? ssm::OPT_A_PER_STATE : 0) |
+                    (opts->snapshots ? ssm::OPT_SNAPSHOTS : 0);
+    if (opt) plan = SegPlan{1, 0};           // these options run whole sequences
     const ShapeRow *row = shape_for(d->d_state);
     if (!row) return SSM_ERR_UNSUPPORTED;
     const bool split = !decode && plan.n_segs > 1;
@@ -240,7 +256,7 @@ int scan_common(const ssm_scan_dims *d, int32_t n_seqs, int32_t n_tokens,
     const int64_t n_blocks = int64_t(n_seqs) * (split ? plan.n_segs : 1) * d->n_heads * n_row_blocks;
     if (n_blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
 
-    const void *fptrs[] = {x, dt, A, B, C, state, y};
+    const void *fptrs[] = {x, dt, A, B, C, state, y, opts->dt_bias, opts->snapshots};
     bool vec = (d->d_state % 4 == 0) && (d->head_dim % 4 == 0);
     for (const void *p : fptrs) {
         if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
@@ -268,14 +284,17 @@ int scan_common(const ssm_scan_dims *d, int32_t n_seqs, int32_t n_tokens,
     a.n_blocks = int32_t(n_blocks);
     a.n_segs = split ? plan.n_segs : 1;
     a.seg_len = split ? plan.seg_len : 0;
+    a.dt_bias = opts->dt_bias;
+    a.dt_softplus = opts->dt_softplus ? 1 : 0;
+    a.snapshots = opts->snapshots;
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-    if (!split) return with_row(*row, Launch{a, vec, kind, stream});
+    if (!split) return with_row(*row, Launch{a, vec, kind, stream, opt});
 
     const WsLayout w = ws_layout(d, n_seqs, n_tokens, plan.n_segs);
     a.ws_state = reinterpret_cast<float *>(ws + w.state);
     a.ws_dtot = reinterpret_cast<float *>(ws + w.dtot);
     a.ws_dcum = reinterpret_cast<float *>(ws + w.dcum);
-    int rc = with_row(*row, Launch{a, vec, Kind::kSegScan, stream});
+    int rc = with_row(*row, Launch{a, vec, Kind::kSegScan, stream, 0});
     if (rc != SSM_OK) return rc;
     {
         const int64_t units = int64_t(n_seqs) * d->n_heads * d->head_dim * d->d_state / (vec ? 4 : 1);
@@ -307,7 +326,7 @@ int scan_common(const ssm_scan_dims *d, int32_t n_seqs, int32_t n_tokens,
             hipLaunchKernel(kern, dim3(unsigned(grid)), dim3(kThreads), params, 0, stream);
         return err == hipSuccess ? SSM_OK : hip_fail(err, SSM_ERR_LAUNCH);
     }
-    return with_row(*row, Launch{a, vec, Kind::kCorrect, stream});
+    return with_row(*row, Launch{a, vec, Kind::kCorrect, stream, 0});
 }
 
 }  // namespace
@@ -325,8 +344,8 @@ int ssm_scan_prefill(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens
     if (n_slots == 0) return SSM_ERR_DIMS;
     if (!cu_seqlens || !slot || !fresh || !A || !state) return SSM_ERR_NULL;
     if (n_tokens > 0 && (!x || !dt || !B || !C || !y)) return SSM_ERR_NULL;
-    return scan_common(dims, n_seqs, n_tokens, cu_seqlens, slot, fresh, x, dt, A, B, C, state,
-                       y, /*decode=*/false, SegPlan{1, 0}, nullptr, stream);
+    return scan_common(dims, nullptr, n_seqs, n_tokens, cu_seqlens, slot, fresh, x, dt, A, B, C,
+                       state, y, /*decode=*/false, SegPlan{1, 0}, nullptr, stream);
 }
 
 int ssm_scan_prefill_workspace_size(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens,
@@ -341,12 +360,12 @@ int ssm_scan_prefill_workspace_size(const ssm_scan_dims *dims, int32_t n_seqs, i
     return SSM_OK;
 }
 
-int ssm_scan_prefill_ws(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens,
-                        int32_t max_seqlen, int32_t n_segments, const int32_t *cu_seqlens,
-                        const int32_t *slot, const uint8_t *fresh, const float *x,
-                        const float *dt, const float *A, const float *B, const float *C,
-                        float *state, int32_t n_slots, float *y, void *workspace,
-                        size_t workspace_bytes, void *stream) {
+int ssm_scan_prefill_opt(const ssm_scan_dims *dims, const ssm_scan_options *opts, int32_t n_seqs,
+                         int32_t n_tokens, int32_t max_seqlen, int32_t n_segments,
+                         const int32_t *cu_seqlens, const int32_t *slot, const uint8_t *fresh,
+                         const float *x, const float *dt, const float *A, const float *B,
+                         const float *C, float *state, int32_t n_slots, float *y, void *workspace,
+                         size_t workspace_bytes, void *stream) {
     const int rc = check_dims(dims);
     if (rc != SSM_OK) return rc;
     if (n_seqs < 0 || n_tokens < 0 || n_slots < 0 || max_seqlen < 0 || n_segments < 0)
@@ -367,22 +386,41 @@ int ssm_scan_prefill_ws(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tok
             ws = reinterpret_cast<char *>((p + 255) / 256 * 256);
         }
     }
-    return scan_common(dims, n_seqs, n_tokens, cu_seqlens, slot, fresh, x, dt, A, B, C, state,
-                       y, /*decode=*/false, plan, ws, stream);
+    return scan_common(dims, opts, n_seqs, n_tokens, cu_seqlens, slot, fresh, x, dt, A, B, C,
+                       state, y, /*decode=*/false, plan, ws, stream);
 }
 
-int ssm_scan_decode(const ssm_scan_dims *dims, int32_t n_seqs, const int32_t *slot,
-                    const uint8_t *fresh, const float *x, const float *dt, const float *A,
-                    const float *B, const float *C, float *state, int32_t n_slots, float *y,
-                    void *stream) {
+int ssm_scan_prefill_ws(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens,
+                        int32_t max_seqlen, int32_t n_segments, const int32_t *cu_seqlens,
+                        const int32_t *slot, const uint8_t *fresh, const float *x,
+                        const float *dt, const float *A, const float *B, const float *C,
+                        float *state, int32_t n_slots, float *y, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    return ssm_scan_prefill_opt(dims, nullptr, n_seqs, n_tokens, max_seqlen, n_segments,
+                                cu_seqlens, slot, fresh, x, dt, A, B, C, state, n_slots, y,
+                                workspace, workspace_bytes, stream);
+}
+
+int ssm_scan_decode_opt(const ssm_scan_dims *dims, const ssm_scan_options *opts, int32_t n_seqs,
+                        const int32_t *slot, const uint8_t *fresh, const float *x,
+                        const float *dt, const float *A, const float *B, const float *C,
+                        float *state, int32_t n_slots, float *y, void *stream) {
     const int rc = check_dims(dims);
     if (rc != SSM_OK) return rc;
     if (n_seqs < 0 || n_slots < 0) return SSM_ERR_DIMS;
     if (n_seqs == 0) return SSM_OK;
     if (n_slots == 0) return SSM_ERR_DIMS;
     if (!slot || !fresh || !A || !state || !x || !dt || !B || !C || !y) return SSM_ERR_NULL;
-    return scan_common(dims, n_seqs, n_seqs, nullptr, slot, fresh, x, dt, A, B, C, state, y,
-                       /*decode=*/true, SegPlan{1, 0}, nullptr, stream);
+    return scan_common(dims, opts, n_seqs, n_seqs, nullptr, slot, fresh, x, dt, A, B, C, state,
+                       y, /*decode=*/true, SegPlan{1, 0}, nullptr, stream);
+}
+
+int ssm_scan_decode(const ssm_scan_dims *dims, int32_t n_seqs, const int32_t *slot,
+                    const uint8_t *fresh, const float *x, const float *dt, const float *A,
+                    const float *B, const float *C, float *state, int32_t n_slots, float *y,
+                    void *stream) {
+    return ssm_scan_decode_opt(dims, nullptr, n_seqs, slot, fresh, x, dt, A, B, C, state, n_slots,
+                               y, stream);
 }
 
 const char *ssm_scan_strerror(int code) {

@@ -26,14 +26,18 @@ def rel_err(a, ref):
 
 
 def run_gpu(case, mode="prefill", device="cuda:0", offset_floats=0, max_seqlen=None,
-            segments=0, workspace_bytes=None):
+            segments=0, workspace_bytes=None, dt_bias=None, dt_softplus=False,
+            A_per_state=False, snapshots=False):
     """Run ``case`` on the GPU; returns (y, state) as numpy.  ``mode`` is
     "prefill" or "decode" (every length must be 1).  ``offset_floats`` > 0
     places every float array at that element offset inside a larger buffer,
     which breaks 16-byte alignment and forces the scalar path.  Mode
     "prefill_ws" calls ssm_scan_prefill_ws with ``max_seqlen`` (default: the
     longest length) and ``segments``; ``workspace_bytes`` overrides the
-    workspace size the library asks for."""
+    workspace size the library asks for.  Options (``dt_bias`` numpy [H],
+    ``dt_softplus``, ``A_per_state`` with case.A [H][N], ``snapshots``) go
+    through the ``_opt`` entry points; with ``snapshots`` the result is
+    (y, state, snapshots)."""
     import torch
     import mamba2_selective_scan_amd as ssm
 
@@ -51,9 +55,13 @@ def run_gpu(case, mode="prefill", device="cuda:0", offset_floats=0, max_seqlen=N
     slot = put(case.slot)
     fresh = put(case.fresh)
     y = put(np.zeros((case.n_tokens, case.H, case.P), np.float32))
+    opts = dict(dt_bias=None if dt_bias is None else put(np.asarray(dt_bias, np.float32)),
+                dt_softplus=dt_softplus, A_per_state=A_per_state,
+                snapshots=put(np.full((case.n_tokens, case.H, case.P, case.N), np.nan, np.float32))
+                if snapshots else None)
     if mode == "prefill":
         cu = put(case.cu_seqlens)
-        ssm.prefill(x, dt, A, B, C, state, cu, slot, fresh, y=y)
+        ssm.prefill(x, dt, A, B, C, state, cu, slot, fresh, y=y, **opts)
     elif mode == "prefill_ws":
         cu = put(case.cu_seqlens)
         ms = int(case.lengths.max()) if max_seqlen is None and case.n_seqs else int(max_seqlen or 0)
@@ -62,13 +70,15 @@ def run_gpu(case, mode="prefill", device="cuda:0", offset_floats=0, max_seqlen=N
         nbytes = need if workspace_bytes is None else workspace_bytes
         ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device=device)  # garbage
         ssm.prefill_ws(x, dt, A, B, C, state, cu, slot, fresh, ms, segments=segments,
-                       workspace=ws[:nbytes] if nbytes else None, y=y)
+                       workspace=ws[:nbytes] if nbytes else None, y=y, **opts)
     elif mode == "decode":
         assert np.all(case.lengths == 1)
-        ssm.decode(x, dt, A, B, C, state, slot, fresh, y=y)
+        ssm.decode(x, dt, A, B, C, state, slot, fresh, y=y, **opts)
     else:
         raise ValueError(mode)
     torch.cuda.synchronize()
+    if snapshots:
+        return y.cpu().numpy(), state.cpu().numpy(), opts["snapshots"].cpu().numpy()
     return y.cpu().numpy(), state.cpu().numpy()
 
 

@@ -20,7 +20,8 @@ def test_exports_every_declared_symbol():
                           "ssm_scan_version", "ssm_scan_check_metadata",
                           "ssm_scan_query_geometry", "ssm_scan_last_hip_error",
                           "ssm_scan_last_hip_error_string", "ssm_scan_prefill_ws",
-                          "ssm_scan_prefill_workspace_size", "ssm_scan_query_prefill_plan"}
+                          "ssm_scan_prefill_workspace_size", "ssm_scan_query_prefill_plan",
+                          "ssm_scan_prefill_opt", "ssm_scan_decode_opt"}
     for n in names:
         assert hasattr(m.lib(), n), n
 
@@ -114,9 +115,9 @@ def test_no_kernel_uses_scratch():
     text = open(report).read()
     names = re.findall(r"Function Name: (\S+)", text)
     scratch = [int(v) for v in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
-    # 7 state-size classes x (prefill, segment scan, correction, decode) x (vector, scalar)
-    # + 2 combine kernels + 3 matrix-core corrections
-    assert len(names) == 61 and len(scratch) == len(names)
+    # 7 state-size classes x (vector, scalar) x (4 option sets x (prefill, decode)
+    # + segment scan + correction) + 2 combine kernels + 3 matrix-core corrections
+    assert len(names) == 7 * 2 * (4 * 2 + 2) + 2 + 3 and len(scratch) == len(names)
     assert all(v == 0 for v in scratch), dict(zip(names, scratch))
 
 

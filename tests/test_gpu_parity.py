@@ -307,3 +307,80 @@ def test_split_prefill_small_workspace_falls_back(ssm, orc):
     ys, sts = run_gpu(case, "prefill_ws", segments=3)
     y32, st32 = orc.scan_case(case, precision="f32")
     assert_parity(case, ys, sts, y32, st32, label="tiny split 3")
+
+
+# ---------------------------------------------------------------- options
+def _bias(H, seed):
+    return np.random.Generator(np.random.PCG64(seed)).uniform(-4.0, 1.0, H).astype(np.float32)
+
+
+def _a_per_state(case, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    case.A = (-np.exp(rng.uniform(0.0, np.log(16.0), size=(case.H, case.N)))).astype(np.float32)
+    return case
+
+
+@pytest.mark.parametrize("mode", ["prefill", "prefill_ws", "decode"])
+def test_option_softplus_bias(ssm, orc, mode):
+    """dt_eff = softplus(dt + bias) in prefill, in the time-split prefill and in
+    decode; a few biases push dt + bias past the 20 cut-off."""
+    if mode == "decode":
+        case = ssm_inputs.workload("decode16")
+    elif mode == "prefill_ws":
+        case = ssm_inputs.make_case(64, 64, 128, 8, [2048], [0], seed=51)
+    else:
+        case = ssm_inputs.workload("mixed")
+    bias = _bias(case.H, 52)
+    bias[1] = 25.0
+    say(f"softplus + bias, {mode}")
+    kw = dict(dt_bias=bias, dt_softplus=True)
+    y, st = run_gpu(case, mode, **kw)
+    y32, st32 = orc.scan_case(case, precision="f32", **kw)
+    assert_parity(case, y, st, y32, st32, label=f"softplus+bias {mode}")
+    small = (np.abs(bias) * 0.02).astype(np.float32)            # bias alone: keep dt > 0
+    y0, st0 = run_gpu(case, mode, dt_bias=small)
+    y32, st32 = orc.scan_case(case, precision="f32", dt_bias=small)
+    assert_parity(case, y0, st0, y32, st32, label=f"bias only {mode}")
+
+
+@pytest.mark.parametrize("name", ["mixed", "decode16", "tiny"])
+def test_option_a_per_state(ssm, orc, name):
+    """A as [H][N] (a decay per state element), with softplus on as well."""
+    case = _a_per_state(ssm_inputs.workload(name), 53)
+    mode = "decode" if name == "decode16" else "prefill"
+    say(f"A per state, {name}")
+    kw = dict(A_per_state=True, dt_softplus=True)
+    y, st = run_gpu(case, mode, **kw)
+    y32, st32 = orc.scan_case(case, precision="f32", **kw)
+    assert_parity(case, y, st, y32, st32, label=f"A per state {name}")
+
+
+@pytest.mark.parametrize("N,P", [(33, 5), (128, 96), (1024, 16)])
+def test_option_a_per_state_shapes(ssm, orc, N, P):
+    case = _a_per_state(ssm_inputs.make_case(4, P, N, 2, [0, 1, 40, 3], [1, 0, 0, 1], seed=54 + N,
+                                             slots=[3, 0, 1, 2], n_slots=5, poison_fresh=True,
+                                             sentinel_unused=True), 55)
+    y, st = run_gpu(case, "prefill", A_per_state=True)
+    y32, st32 = orc.scan_case(case, precision="f32", A_per_state=True)
+    assert_parity(case, y, st, y32, st32, label=f"A per state N={N} P={P}")
+    y, st = run_gpu(case, "prefill", A_per_state=True, offset_floats=1)       # scalar path
+    assert_parity(case, y, st, y32, st32, label=f"A per state N={N} P={P} scalar")
+
+
+@pytest.mark.parametrize("name,mode", [("mixed", "prefill"), ("tiny", "prefill"),
+                                       ("decode16", "decode"), ("mixed", "prefill_ws")])
+def test_option_snapshots(ssm, orc, name, mode):
+    """Snapshots hold the state after every token (against the oracle's); the
+    last one of each sequence is bit for bit the state written to its slot.
+    Asking the split path for snapshots makes it scan whole sequences."""
+    case = ssm_inputs.workload(name)
+    say(f"snapshots {name} {mode}")
+    extra = dict(segments=3) if mode == "prefill_ws" else {}
+    y, st, snaps = run_gpu(case, mode, snapshots=True, **extra)
+    y32, st32, sn32 = orc.scan_case(case, precision="f32", snapshots=True)
+    assert_parity(case, y, st, y32, st32, label=f"snapshots {name} {mode}")
+    assert rel_err(snaps, sn32) <= TOL
+    for s in range(case.n_seqs):
+        t1 = int(case.cu_seqlens[s + 1])
+        if case.lengths[s] > 0:
+            assert np.array_equal(snaps[t1 - 1], st[case.slot[s]]), s
