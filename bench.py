@@ -94,21 +94,28 @@ def host_cores():
 
 
 def cpu_baseline_decode(case, seconds):
-    """The fp32 oracle on the same decode step, repeated for ~``seconds``."""
+    """The fp32 oracle on the same decode step, repeated for ~``seconds`` on
+    all host threads (up to 16) and for ~seconds/3 on one thread."""
     import oracle
     threads = min(16, host_cores())
     orc = oracle.default()
-    orc.scan_case(case, threads=threads)               # page in
-    n, t0 = 0, time.perf_counter()
-    while True:
-        orc.scan_case(case, threads=threads)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+
+    def rate(th, budget):
+        orc.scan_case(case, threads=th)                # page in
+        n, t0 = 0, time.perf_counter()
+        while True:
+            orc.scan_case(case, threads=th)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return n, el
+    n, el = rate(threads, seconds)
+    n1, el1 = rate(1, max(1.0, seconds / 3))
     return {"value": round(el / n * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle",
+            "value_1_thread": round(el1 / n1 * 1e6, 1),
             "sample": f"{n} repetitions of the full decode 16x1 step (16 seqs x 64 heads x 64 "
-                      f"rows x 128 state, fp32, resuming), {el:.1f} s of CPU time"}
+                      f"rows x 128 state, fp32, resuming) on {threads} threads, {el:.1f} s; "
+                      f"{n1} on 1 thread, {el1:.1f} s"}
 
 
 def _timed(fn, n, stream):
@@ -195,6 +202,87 @@ def profile_mode(args, dev, stream):
     print(json.dumps(out), flush=True)
 
 
+def _event_ms(fn, n, warm, stream):
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def secondary(args, dev, stream):
+    """Time the other workloads and the option paths (eager launches, HIP
+    events; each is also a GPU parity case in tests/)."""
+    import numpy as np
+    import torch
+
+    import mamba2_selective_scan_amd as ssm
+    import ssm_inputs
+    out = {}
+    # decode 256 x 1: 1.07 GB of state traffic per step, far past any cache
+    c = ssm_inputs.workload("decode256")
+    d = ssm.to_device(c, dev)
+    y = torch.empty((256, H, P), device=dev)
+    us = 1e3 * _event_ms(lambda: ssm.decode(d["x"], d["dt"], d["A"], d["B"], d["C"], d["state"],
+                                             d["slot"], d["fresh"], y=y), 20, 3, stream)
+    gbs = decode_bytes(256) / (us * 1e-6) / 1e9
+    out["decode_256x1"] = {"us": round(us, 2), "GBs": round(gbs, 1),
+                           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                           "algorithmic_bytes": decode_bytes(256)}
+    del d, y
+    # mixed edge batch
+    c = ssm_inputs.workload("mixed")
+    d = ssm.to_device(c, dev)
+    ym = torch.empty((c.n_tokens, c.H, c.P), device=dev)
+    us = 1e3 * _event_ms(lambda: ssm.prefill(d["x"], d["dt"], d["A"], d["B"], d["C"], d["state"],
+                                              d["cu_seqlens"], d["slot"], d["fresh"], y=ym),
+                         20, 3, stream)
+    out["mixed_batch"] = {"us": round(us, 2), "tokens": c.n_tokens,
+                          "workload": "8 seqs, lengths 1..150, H16 P96 N100 G4"}
+    # options on the headline shapes
+    pc = ssm_inputs.workload("prefill4096")
+    pd = ssm.to_device(pc, dev)
+    py = torch.empty((PREFILL_T, H, P), device=dev)
+    rng = np.random.Generator(np.random.PCG64(7))
+    bias = torch.from_numpy(rng.uniform(-4, 1, H).astype(np.float32)).to(dev)
+    ws = torch.empty(max(1, ssm.workspace_size(H, P, N, G, 1, PREFILL_T, PREFILL_T)),
+                     dtype=torch.uint8, device=dev)
+    base = (pd["x"], pd["dt"], pd["A"], pd["B"], pd["C"], pd["state"], pd["cu_seqlens"],
+            pd["slot"], pd["fresh"])
+    ms = _event_ms(lambda: ssm.prefill_ws(*base, PREFILL_T, workspace=ws, y=py, dt_bias=bias,
+                                          dt_softplus=True), 5, 2, stream)
+    out["prefill_1x4096_softplus_bias"] = {"ms": round(ms, 4), "path": "time split"}
+    A_hn = torch.from_numpy((-np.exp(rng.uniform(0, np.log(16), (H, N)))).astype(np.float32)).to(dev)
+    base_a = (pd["x"], pd["dt"], A_hn) + base[3:]
+    ms = _event_ms(lambda: ssm.prefill(*base_a, y=py, A_per_state=True, dt_softplus=True),
+                   5, 2, stream)
+    out["prefill_1x4096_A_per_state"] = {"ms": round(ms, 4), "path": "whole sequence"}
+    short = ssm_inputs.make_case(H, P, N, G, [8] * 16, [0] * 16, seed=8)
+    sd = ssm.to_device(short, dev)
+    snaps = torch.empty((short.n_tokens, H, P, N), device=dev)
+    ys = torch.empty((short.n_tokens, H, P), device=dev)
+    us = 1e3 * _event_ms(lambda: ssm.prefill(sd["x"], sd["dt"], sd["A"], sd["B"], sd["C"],
+                                              sd["state"], sd["cu_seqlens"], sd["slot"],
+                                              sd["fresh"], y=ys, snapshots=snaps), 20, 3, stream)
+    out["draft_16x8_snapshots"] = {"us": round(us, 2),
+                                   "workload": "16 seqs x 8 draft tokens, state after every token "
+                                               "written (268 MB of snapshots)"}
+    dd = ssm.to_device(ssm_inputs.workload("decode16"), dev)
+    yd = torch.empty((16, H, P), device=dev)
+    us = 1e3 * _event_ms(lambda: ssm.decode(dd["x"], dd["dt"], dd["A"], dd["B"], dd["C"],
+                                             dd["state"], dd["slot"], dd["fresh"], y=yd,
+                                             dt_bias=bias, dt_softplus=True), 50, 5, stream)
+    out["decode_16x1_softplus_bias_eager"] = {"us": round(us, 2),
+                                              "note": "eager launches, one slot set (warm cache)"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +293,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the secondary workloads (decode 256x1, mixed batch, options)")
     ap.add_argument("--mode", choices=("all", "decode", "prefill", "prefill1", "copy", "copy16"),
                     default="all",
                     help="decode/prefill: launch only that path (prefill: the time-split path; "
@@ -354,6 +444,9 @@ def main():
                          "algorithmic_bytes_per_launch": prefill_bytes(),
                          "achieved_GBs": round(prefill_bytes() / (pf_ms * 1e-3) / 1e9, 1)},
         }
+
+    if not args.no_secondary:
+        result["secondary"] = secondary(args, dev, stream)
 
     if not args.no_cpu_baseline:
         one_set = ssm_inputs.workload("decode16")
