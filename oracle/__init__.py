@@ -1,4 +1,5 @@
-"""CPU oracle for the Mamba2 selective-state scan -- TEST INFRASTRUCTURE.
+"""CPU oracle for the Mamba2 selective-state scan and its neighbouring steps
+(causal conv1d + SiLU, gated RMSNorm) -- TEST INFRASTRUCTURE.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
 leg may import this package.  The GPU library never calls it and shares no code
@@ -46,6 +47,18 @@ class Oracle:
         self.lib.ssm_oracle_scan_opt_f64.argtypes = (common + [_f64p, _f64p, ctypes.c_int32]
                                                      + opts + [_f64p])
         self.lib.ssm_oracle_scan_opt_f64.restype = ctypes.c_int
+        meta = [ctypes.c_int32] * 3 + [_i32p, _i32p, _u8p, _f32p, _f32p]
+        self.lib.ssm_oracle_conv1d_silu_f32.argtypes = meta + [_f32p] * 3 + [ctypes.c_int32]
+        self.lib.ssm_oracle_conv1d_silu_f32.restype = ctypes.c_int
+        self.lib.ssm_oracle_conv1d_silu_f64.argtypes = meta + [_f64p] * 3 + [ctypes.c_int32]
+        self.lib.ssm_oracle_conv1d_silu_f64.restype = ctypes.c_int
+        norm = [ctypes.c_int64, ctypes.c_int32, _f32p, _f32p, _f32p]
+        self.lib.ssm_oracle_gated_rmsnorm_f32.argtypes = norm + [ctypes.c_float, _f32p,
+                                                                 ctypes.c_int32]
+        self.lib.ssm_oracle_gated_rmsnorm_f32.restype = ctypes.c_int
+        self.lib.ssm_oracle_gated_rmsnorm_f64.argtypes = norm + [ctypes.c_double, _f64p,
+                                                                 ctypes.c_int32]
+        self.lib.ssm_oracle_gated_rmsnorm_f64.restype = ctypes.c_int
 
     def scan(self, H, P, N, G, cu_seqlens, slot, fresh, x, dt, A, B, C, state,
              precision="f32", threads=None, dt_bias=None, dt_softplus=False,
@@ -104,6 +117,79 @@ class Oracle:
         return self.scan(case.H, case.P, case.N, case.G, case.cu_seqlens, case.slot,
                          case.fresh, case.x, case.dt, case.A, case.B, case.C,
                          case.state, precision=precision, threads=threads, **options)
+
+    # ------------------------------------------------------------ neighbours
+    def conv1d_silu(self, K, cu_seqlens, slot, fresh, x, w, conv_state, precision="f32",
+                    threads=None, snapshots=False):
+        """Causal depthwise conv1d + SiLU with a rolling history over a packed
+        batch.  x [T][D], w [D][K], conv_state [n_slots][D][K-1] (not
+        modified).  Returns ``(out, conv_state_out)``, or ``(out, state_out,
+        snapshots)`` with ``snapshots=True`` ([T][D][K-1], the history after
+        each token)."""
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        slot = np.ascontiguousarray(slot, dtype=np.int32)
+        fresh = np.ascontiguousarray(fresh, dtype=np.uint8)
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        n_seqs = slot.shape[0]
+        T = int(cu[-1]) if cu.shape[0] else 0
+        D = w.shape[0]
+        assert cu.shape[0] == n_seqs + 1 and w.shape == (D, K) and x.shape == (T, D)
+        assert conv_state.ndim == 3 and conv_state.shape[1:] == (D, K - 1)
+        if threads is None:
+            threads = os.cpu_count() or 1
+        if precision == "f32":
+            dtype, fn, fp = np.float32, self.lib.ssm_oracle_conv1d_silu_f32, _f32p
+        elif precision == "f64":
+            dtype, fn, fp = np.float64, self.lib.ssm_oracle_conv1d_silu_f64, _f64p
+        else:
+            raise ValueError(precision)
+        st = np.array(conv_state, dtype=dtype, copy=True, order="C")
+        out = np.zeros((T, D), dtype=dtype)
+        snaps = np.zeros((T, D, K - 1), dtype=dtype) if snapshots else None
+        rc = fn(D, K, n_seqs, _ptr(cu, _i32p), _ptr(slot, _i32p), _ptr(fresh, _u8p),
+                _ptr(x, _f32p), _ptr(w, _f32p), _ptr(st, fp), _ptr(out, fp),
+                None if snaps is None else _ptr(snaps, fp), int(threads))
+        if rc != 0:
+            raise ValueError(f"oracle rejected the dimensions (rc={rc})")
+        return (out, st, snaps) if snapshots else (out, st)
+
+    def conv_case(self, case, precision="f32", threads=None, snapshots=False):
+        """``conv1d_silu`` on an ``ssm_inputs.ConvCase``."""
+        return self.conv1d_silu(case.K, case.cu_seqlens, case.slot, case.fresh, case.x,
+                                case.w, case.state, precision=precision, threads=threads,
+                                snapshots=snapshots)
+
+    def gated_rmsnorm(self, y, z, w, eps, precision="f32", threads=None):
+        """Gated RMSNorm over the last axis: y, z [..., L], w [L]."""
+        y = np.ascontiguousarray(y, dtype=np.float32)
+        z = np.ascontiguousarray(z, dtype=np.float32)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        L = w.shape[0]
+        assert y.shape == z.shape and y.shape[-1] == L
+        n_rows = y.size // L
+        if threads is None:
+            threads = os.cpu_count() or 1
+        if precision == "f32":
+            out = np.zeros(y.shape, dtype=np.float32)
+            rc = self.lib.ssm_oracle_gated_rmsnorm_f32(n_rows, L, _ptr(y, _f32p), _ptr(z, _f32p),
+                                                       _ptr(w, _f32p), float(eps),
+                                                       _ptr(out, _f32p), int(threads))
+        elif precision == "f64":
+            out = np.zeros(y.shape, dtype=np.float64)
+            rc = self.lib.ssm_oracle_gated_rmsnorm_f64(n_rows, L, _ptr(y, _f32p), _ptr(z, _f32p),
+                                                       _ptr(w, _f32p), float(eps),
+                                                       _ptr(out, _f64p), int(threads))
+        else:
+            raise ValueError(precision)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the dimensions (rc={rc})")
+        return out
+
+    def norm_case(self, case, precision="f32", threads=None):
+        """``gated_rmsnorm`` on an ``ssm_inputs.NormCase``."""
+        return self.gated_rmsnorm(case.y, case.z, case.w, case.eps, precision=precision,
+                                  threads=threads)
 
 
 _default = None

@@ -1,5 +1,7 @@
 /*
- * ssm_oracle.c -- plain, sequential CPU oracle for the Mamba2 selective-state scan.
+ * ssm_oracle.c -- plain, sequential CPU oracle for the Mamba2 selective-state scan
+ * and the two steps beside it in a layer (causal conv1d + SiLU with a rolling
+ * history, gated RMSNorm; see the second half of this file).
  *
  * TEST INFRASTRUCTURE.  This file is the correctness reference the GPU library
  * is compared against.  Only the tests, the smoke check and the benchmark's CPU
@@ -53,7 +55,7 @@
 #include <stdint.h>
 #include <string.h>
 
-int ssm_oracle_version(void) { return 2; }
+int ssm_oracle_version(void) { return 3; }
 
 /* dt after the optional bias and softplus (see the header). */
 static float dt_eff_f32(float dt, const float *dt_bias, int64_t hd, int32_t softplus)
@@ -188,4 +190,165 @@ int ssm_oracle_scan_f64(int32_t H, int32_t P, int32_t N, int32_t G, int32_t n_se
 {
     return ssm_oracle_scan_opt_f64(H, P, N, G, n_seqs, cu_seqlens, slot, fresh, x, dt, A, B, C,
                                    state, y, n_threads, NULL, 0, 0, NULL);
+}
+
+/* ------------------------------------------------------------------------
+ * The two steps on either side of the scan in a Mamba2-style layer.
+ *
+ * SiLU: silu(v) = v * sigmoid(v), written as v / (1 + exp(-v)) as in the
+ * fc_ssm_silu helper of "ssm_gated_delta.cu".
+ * ------------------------------------------------------------------------ */
+static float silu_f32(float v) { return v / (1.0f + expf(-v)); }
+static double silu_f64(double v) { return v / (1.0 + exp(-v)); }
+
+/*
+ * Causal depthwise conv1d + SiLU with a rolling per-channel history, over a
+ * packed batch ("ssm_gated_delta.cu": fc_ssm_conv1d_silu for one token,
+ * fc_ssm_conv1d_silu_seq for a run of positions, fc_ssm_conv1d_silu_slots for
+ * one token of several users).  For channel c the window at each token is the
+ * K-1 previous raw inputs, oldest first, followed by the token's own input;
+ *     out[t][c] = silu( x[t][c] * w[c][K-1] + sum_{i<K-1} hist[i] * w[c][i] )
+ * accumulated in that order (the token's own tap first, then the history from
+ * oldest to newest), after which the history drops its oldest value and
+ * appends x[t][c].
+ *
+ * Layouts: x and out [T][D] token-major (tokens of all sequences packed as for
+ * the scan), w [D][K], conv_state [n_slots][D][K-1] with each channel's
+ * history oldest..newest, snapshots (optional) [T][D][K-1] = the history after
+ * each token.  Sequence s reads its history from slot[s] unless fresh[s] (then
+ * it starts from zeros and never reads the slot) and leaves it there.
+ * Channels and sequences are independent, so (sequence, channel) pairs may run
+ * on several threads with bitwise the same result.
+ */
+int ssm_oracle_conv1d_silu_f32(int32_t D, int32_t K, int32_t n_seqs,
+                               const int32_t *cu_seqlens, const int32_t *slot,
+                               const uint8_t *fresh, const float *x, const float *w,
+                               float *conv_state, float *out, float *snapshots,
+                               int32_t n_threads)
+{
+    if (D <= 0 || K < 1 || n_seqs < 0)
+        return -1;
+    if (n_threads < 1)
+        n_threads = 1;
+    const int64_t km1 = K - 1;
+    const int64_t pairs = (int64_t)n_seqs * D;
+
+#pragma omp parallel for schedule(static) num_threads(n_threads)
+    for (int64_t k = 0; k < pairs; ++k) {
+        const int64_t s = k / D;
+        const int64_t c = k % D;
+        float *hist = conv_state + ((int64_t)slot[s] * D + c) * km1;
+        const float *wc = w + c * K;
+        if (fresh[s])
+            for (int64_t i = 0; i < km1; ++i)
+                hist[i] = 0.0f;
+        for (int64_t t = cu_seqlens[s]; t < cu_seqlens[s + 1]; ++t) {
+            const float xv = x[t * D + c];
+            float acc = xv * wc[km1];
+            for (int64_t i = 0; i < km1; ++i)
+                acc += hist[i] * wc[i];
+            out[t * D + c] = silu_f32(acc);
+            for (int64_t i = 0; i + 1 < km1; ++i)
+                hist[i] = hist[i + 1];
+            if (km1 > 0)
+                hist[km1 - 1] = xv;
+            if (snapshots)
+                for (int64_t i = 0; i < km1; ++i)
+                    snapshots[(t * D + c) * km1 + i] = hist[i];
+        }
+    }
+    return 0;
+}
+
+/* The same in double (inputs fp32; history, output and snapshots double). */
+int ssm_oracle_conv1d_silu_f64(int32_t D, int32_t K, int32_t n_seqs,
+                               const int32_t *cu_seqlens, const int32_t *slot,
+                               const uint8_t *fresh, const float *x, const float *w,
+                               double *conv_state, double *out, double *snapshots,
+                               int32_t n_threads)
+{
+    if (D <= 0 || K < 1 || n_seqs < 0)
+        return -1;
+    if (n_threads < 1)
+        n_threads = 1;
+    const int64_t km1 = K - 1;
+    const int64_t pairs = (int64_t)n_seqs * D;
+
+#pragma omp parallel for schedule(static) num_threads(n_threads)
+    for (int64_t k = 0; k < pairs; ++k) {
+        const int64_t s = k / D;
+        const int64_t c = k % D;
+        double *hist = conv_state + ((int64_t)slot[s] * D + c) * km1;
+        const float *wc = w + c * K;
+        if (fresh[s])
+            for (int64_t i = 0; i < km1; ++i)
+                hist[i] = 0.0;
+        for (int64_t t = cu_seqlens[s]; t < cu_seqlens[s + 1]; ++t) {
+            const double xv = (double)x[t * D + c];
+            double acc = xv * (double)wc[km1];
+            for (int64_t i = 0; i < km1; ++i)
+                acc += hist[i] * (double)wc[i];
+            out[t * D + c] = silu_f64(acc);
+            for (int64_t i = 0; i + 1 < km1; ++i)
+                hist[i] = hist[i + 1];
+            if (km1 > 0)
+                hist[km1 - 1] = xv;
+            if (snapshots)
+                for (int64_t i = 0; i < km1; ++i)
+                    snapshots[(t * D + c) * km1 + i] = hist[i];
+        }
+    }
+    return 0;
+}
+
+/*
+ * Gated RMSNorm ("ssm_gated_delta.cu", fc_ssm_gated_norm): each row of L
+ * values (one head of one token) is divided by its root mean square, then
+ * scaled by a weight that all rows share and by silu of the gate:
+ *     rms      = sqrt( (sum_d y[d]^2) / L + eps )
+ *     out[d]   = y[d] * (1 / rms) * w[d] * silu(z[d])
+ * multiplied left to right in that order.  y, z, out [n_rows][L]; w [L].
+ */
+int ssm_oracle_gated_rmsnorm_f32(int64_t n_rows, int32_t L, const float *y, const float *z,
+                                 const float *w, float eps, float *out, int32_t n_threads)
+{
+    if (n_rows < 0 || L <= 0)
+        return -1;
+    if (n_threads < 1)
+        n_threads = 1;
+
+#pragma omp parallel for schedule(static) num_threads(n_threads)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const float *yr = y + r * L;
+        const float *zr = z + r * L;
+        float sum_sq = 0.0f;
+        for (int64_t d = 0; d < L; ++d)
+            sum_sq += yr[d] * yr[d];
+        const float inv_rms = 1.0f / sqrtf(sum_sq / (float)L + eps);
+        for (int64_t d = 0; d < L; ++d)
+            out[r * L + d] = yr[d] * inv_rms * w[d] * silu_f32(zr[d]);
+    }
+    return 0;
+}
+
+int ssm_oracle_gated_rmsnorm_f64(int64_t n_rows, int32_t L, const float *y, const float *z,
+                                 const float *w, double eps, double *out, int32_t n_threads)
+{
+    if (n_rows < 0 || L <= 0)
+        return -1;
+    if (n_threads < 1)
+        n_threads = 1;
+
+#pragma omp parallel for schedule(static) num_threads(n_threads)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const float *yr = y + r * L;
+        const float *zr = z + r * L;
+        double sum_sq = 0.0;
+        for (int64_t d = 0; d < L; ++d)
+            sum_sq += (double)yr[d] * (double)yr[d];
+        const double inv_rms = 1.0 / sqrt(sum_sq / (double)L + eps);
+        for (int64_t d = 0; d < L; ++d)
+            out[r * L + d] = (double)yr[d] * inv_rms * (double)w[d] * silu_f64((double)zr[d]);
+    }
+    return 0;
 }

@@ -23,7 +23,9 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["ScanCase", "make_case", "WORKLOADS", "workload", "lengths_to_cu"]
+__all__ = ["ScanCase", "make_case", "WORKLOADS", "workload", "lengths_to_cu",
+           "ConvCase", "make_conv_case", "CONV_WORKLOADS", "conv_workload",
+           "NormCase", "make_norm_case", "NORM_WORKLOADS", "norm_workload"]
 
 
 @dataclass
@@ -155,3 +157,140 @@ WORKLOADS = {
 
 def workload(name: str, **kw) -> ScanCase:
     return WORKLOADS[name](**kw)
+
+
+# ---------------------------------------------------------------------------
+# The steps on either side of the scan.
+#
+# Causal conv1d + SiLU: x [T][D] token-major (packed like the scan's x), the
+# depthwise weight [D][K], the rolling history [n_slots][D][K-1] oldest first
+# (the layout of "ssm_gated_delta.cu", fc_ssm_conv1d_silu).  In a Mamba2 layer
+# the conv runs over the concatenation of x, B and C, so D = H*P + 2*G*N with
+# K = 4.  Values: x and history ~ N(0, 1) (the history holds past raw inputs);
+# weights ~ U(-1/sqrt(K), 1/sqrt(K)), the usual fan-in scale of a depthwise
+# conv.  Draw order: w, x, state.
+#
+# Gated RMSNorm: y and z [T][H][P], the shared weight [P] (the layout of
+# fc_ssm_gated_norm, one row per head).  Values: y, z ~ N(0, 1), weight
+# 1 + 0.1 * N(0, 1), eps 1e-5.  Draw order: w, y, z.
+# ---------------------------------------------------------------------------
+@dataclass
+class ConvCase:
+    D: int
+    K: int
+    lengths: np.ndarray          # int32 [n_seqs]
+    cu_seqlens: np.ndarray       # int32 [n_seqs + 1]
+    slot: np.ndarray             # int32 [n_seqs]
+    fresh: np.ndarray            # uint8 [n_seqs]
+    x: np.ndarray                # f32 [T, D]
+    w: np.ndarray                # f32 [D, K]
+    state: np.ndarray            # f32 [n_slots, D, K - 1]
+    seed: int = 0
+    name: str = ""
+
+    @property
+    def n_seqs(self) -> int:
+        return int(self.lengths.shape[0])
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def n_slots(self) -> int:
+        return int(self.state.shape[0])
+
+
+def make_conv_case(D, K, lengths, fresh, seed, *, slots=None, n_slots=None,
+                   poison_fresh=False, sentinel_unused=False, name="") -> ConvCase:
+    """Draw one packed conv batch; ``slots``, ``poison_fresh`` and
+    ``sentinel_unused`` mean what they mean for ``make_case``."""
+    lengths = np.asarray(lengths, dtype=np.int32)
+    fresh = np.asarray(fresh, dtype=np.uint8)
+    n_seqs = lengths.shape[0]
+    if slots is None:
+        slots = np.arange(n_seqs, dtype=np.int32)
+    slots = np.asarray(slots, dtype=np.int32)
+    if n_slots is None:
+        n_slots = int(slots.max()) + 1 if n_seqs else 0
+    cu = lengths_to_cu(lengths)
+    T = int(cu[-1])
+    rng = np.random.Generator(np.random.PCG64(seed))
+    bound = 1.0 / math.sqrt(K)
+    w = rng.uniform(-bound, bound, size=(D, K)).astype(np.float32)
+    x = rng.standard_normal((T, D), dtype=np.float32)
+    state = rng.standard_normal((n_slots, D, K - 1), dtype=np.float32)
+    if sentinel_unused:
+        used = np.zeros(n_slots, dtype=bool)
+        used[slots] = True
+        for k in np.nonzero(~used)[0]:
+            state[k] = np.float32(1000.0 + k)
+    if poison_fresh:
+        for s in range(n_seqs):
+            if fresh[s]:
+                state[slots[s]] = np.nan
+    return ConvCase(D=D, K=K, lengths=lengths, cu_seqlens=cu, slot=slots, fresh=fresh,
+                    x=x, w=w, state=state, seed=seed, name=name)
+
+
+def conv_channels(H, P, N, G) -> int:
+    """Channels of a Mamba2 layer's conv: x, B and C side by side."""
+    return H * P + 2 * G * N
+
+
+CONV_WORKLOADS = {
+    "tiny": lambda seed=10: make_conv_case(conv_channels(4, 16, 16, 1), 4, [64], [1], seed,
+                                           name="conv_tiny_T64_D96_K4"),
+    "decode16": lambda seed=11, sets=1: make_conv_case(
+        conv_channels(64, 64, 128, 8), 4, [1] * 16, [0] * 16, seed, n_slots=16 * sets,
+        name="conv_decode_16x1_D6144_K4"),
+    "prefill4096": lambda seed=12: make_conv_case(
+        conv_channels(64, 64, 128, 8), 4, [4096], [1], seed,
+        name="conv_prefill_1x4096_D6144_K4"),
+    "mixed": lambda seed=13: make_conv_case(
+        conv_channels(16, 96, 100, 4), 4, [1, 7, 25, 26, 64, 100, 150, 150],
+        [1 - (i % 2) for i in range(8)], seed,
+        slots=np.random.Generator(np.random.PCG64(seed + 1000)).permutation(10)[:8]
+        .astype(np.int32), n_slots=10, poison_fresh=True, sentinel_unused=True,
+        name="conv_mixed_8seq_D2336_K4"),
+    "decode256": lambda seed=14: make_conv_case(
+        conv_channels(64, 64, 128, 8), 4, [1] * 256, [0] * 256, seed,
+        name="conv_decode_256x1_D6144_K4"),
+}
+
+
+def conv_workload(name: str, **kw) -> ConvCase:
+    return CONV_WORKLOADS[name](**kw)
+
+
+@dataclass
+class NormCase:
+    y: np.ndarray                # f32 [T, H, P]
+    z: np.ndarray                # f32 [T, H, P]
+    w: np.ndarray                # f32 [P]
+    eps: float
+    seed: int = 0
+    name: str = ""
+
+
+def make_norm_case(T, H, P, seed, *, eps=1e-5, y_std=1.0, name="") -> NormCase:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w = (1.0 + 0.1 * rng.standard_normal(P)).astype(np.float32)
+    y = rng.standard_normal((T, H, P), dtype=np.float32)
+    y *= np.float32(y_std)
+    z = rng.standard_normal((T, H, P), dtype=np.float32)
+    return NormCase(y=y, z=z, w=w, eps=float(eps), seed=seed, name=name)
+
+
+NORM_WORKLOADS = {
+    "tiny": lambda seed=20: make_norm_case(64, 4, 16, seed, name="norm_tiny_T64_H4_P16"),
+    "decode16": lambda seed=21: make_norm_case(16, 64, 64, seed, name="norm_16x1_H64_P64"),
+    "prefill4096": lambda seed=22: make_norm_case(4096, 64, 64, seed,
+                                                  name="norm_1x4096_H64_P64"),
+    "mixed": lambda seed=23: make_norm_case(523, 16, 96, seed, name="norm_T523_H16_P96"),
+    "decode256": lambda seed=24: make_norm_case(256, 64, 64, seed, name="norm_256x1_H64_P64"),
+}
+
+
+def norm_workload(name: str, **kw) -> NormCase:
+    return NORM_WORKLOADS[name](**kw)

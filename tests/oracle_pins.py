@@ -359,3 +359,8 @@ ALL_PINS = [pin_hand_worked, pin_brute_force, pin_brute_force_tiny_workload,
             pin_batch_independence, pin_linearity, pin_group_equivalence,
             pin_slot_hygiene, pin_thread_count, pin_softplus_single_token,
             pin_per_state_A_closed_form, pin_per_state_A_constant_rows, pin_snapshots]
+
+# the neighbouring steps (conv1d + SiLU, gated RMSNorm)
+from neighbour_pins import CONV_PINS, NORM_PINS  # noqa: E402
+
+ALL_PINS = ALL_PINS + CONV_PINS + NORM_PINS

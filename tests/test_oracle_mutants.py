@@ -29,8 +29,8 @@ MUTANTS = [
      "h_p[n] = h_p[n] * dA_n + C_t[n] * x_dt;\n                    acc += h_p[n] * B_t[n];"),
     ("fresh_flag_ignored", "        if (fresh[s])\n            memset(", "        if (0)\n            memset("),
     ("first_token_skipped",
-     "for (int64_t t = cu_seqlens[s]; t < cu_seqlens[s + 1]; ++t) {\n            const float",
-     "for (int64_t t = cu_seqlens[s] + 1; t < cu_seqlens[s + 1]; ++t) {\n            const float"),
+     "for (int64_t t = cu_seqlens[s]; t < cu_seqlens[s + 1]; ++t) {\n            const float dt_t",
+     "for (int64_t t = cu_seqlens[s] + 1; t < cu_seqlens[s + 1]; ++t) {\n            const float dt_t"),
     ("rows_reversed_in_x", "x[(t * H + hd) * P + p] * dt_t;\n                float *h_p",
      "x[(t * H + hd) * P + (P - 1 - p)] * dt_t;\n                float *h_p"),
     ("slot_index_ignored", "float *h = state + ((int64_t)slot[s] * H + hd) * P * N;",
@@ -49,6 +49,42 @@ MUTANTS = [
     ("snapshot_of_previous_token",
      "memcpy(snapshots + (t * H + hd) * P * N, h,",
      "memcpy(snapshots + ((t > cu_seqlens[s] ? t - 1 : t) * H + hd) * P * N, h,"),
+    # conv1d + SiLU
+    ("silu_sign_flipped", "static float silu_f32(float v) { return v / (1.0f + expf(-v)); }",
+     "static float silu_f32(float v) { return v / (1.0f + expf(v)); }"),
+    ("conv_taps_reversed", "            for (int64_t i = 0; i < km1; ++i)\n"
+     "                acc += hist[i] * wc[i];\n            out[t * D + c] = silu_f32(acc);",
+     "            for (int64_t i = 0; i < km1; ++i)\n"
+     "                acc += hist[i] * wc[km1 - 1 - i];\n            out[t * D + c] = silu_f32(acc);"),
+    ("conv_own_tap_wrong", "float acc = xv * wc[km1];", "float acc = xv * wc[0];"),
+    ("conv_no_silu", "out[t * D + c] = silu_f32(acc);", "out[t * D + c] = acc;"),
+    ("conv_history_not_rolled", "                hist[i] = hist[i + 1];\n            if (km1 > 0)\n"
+     "                hist[km1 - 1] = xv;\n            if (snapshots)\n                for (int64_t i = 0; i < km1; ++i)\n"
+     "                    snapshots[(t * D + c) * km1 + i] = hist[i];\n        }\n    }\n    return 0;\n}\n\n/* The same in double",
+     "                hist[i] = hist[i];\n            if (km1 > 0)\n"
+     "                hist[km1 - 1] = xv;\n            if (snapshots)\n                for (int64_t i = 0; i < km1; ++i)\n"
+     "                    snapshots[(t * D + c) * km1 + i] = hist[i];\n        }\n    }\n    return 0;\n}\n\n/* The same in double"),
+    ("conv_fresh_not_zeroed", "        if (fresh[s])\n            for (int64_t i = 0; i < km1; ++i)\n"
+     "                hist[i] = 0.0f;",
+     "        if (0)\n            for (int64_t i = 0; i < km1; ++i)\n                hist[i] = 0.0f;"),
+    ("conv_slot_ignored", "float *hist = conv_state + ((int64_t)slot[s] * D + c) * km1;",
+     "float *hist = conv_state + ((int64_t)s * D + c) * km1;"),
+    ("conv_snapshot_reversed", "snapshots[(t * D + c) * km1 + i] = hist[i];\n        }\n    }\n"
+     "    return 0;\n}\n\n/* The same in double",
+     "snapshots[(t * D + c) * km1 + i] = hist[km1 - 1 - i];\n        }\n    }\n"
+     "    return 0;\n}\n\n/* The same in double"),
+    # gated RMSNorm
+    ("norm_sum_not_mean", "sqrtf(sum_sq / (float)L + eps)", "sqrtf(sum_sq + eps)"),
+    ("norm_no_sqrt", "1.0f / sqrtf(sum_sq / (float)L + eps)", "1.0f / (sum_sq / (float)L + eps)"),
+    ("norm_eps_outside_sqrt", "1.0f / sqrtf(sum_sq / (float)L + eps)",
+     "1.0f / (sqrtf(sum_sq / (float)L) + eps)"),
+    ("norm_weight_reversed", "out[r * L + d] = yr[d] * inv_rms * w[d] * silu_f32(zr[d]);",
+     "out[r * L + d] = yr[d] * inv_rms * w[L - 1 - d] * silu_f32(zr[d]);"),
+    ("norm_gate_not_silu", "out[r * L + d] = yr[d] * inv_rms * w[d] * silu_f32(zr[d]);",
+     "out[r * L + d] = yr[d] * inv_rms * w[d] * zr[d];"),
+    ("norm_gate_from_y", "out[r * L + d] = yr[d] * inv_rms * w[d] * silu_f32(zr[d]);",
+     "out[r * L + d] = yr[d] * inv_rms * w[d] * silu_f32(yr[d]);"),
+    ("norm_abs_not_square", "sum_sq += yr[d] * yr[d];", "sum_sq += fabsf(yr[d]);"),
 ]
 
 

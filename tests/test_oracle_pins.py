@@ -28,3 +28,21 @@ def test_f32_against_f64(orc, name):
     assert np.all(np.isfinite(y32)) and np.all(np.isfinite(st32[used]))
     assert rel_err(y32, y64) <= 1e-4
     assert rel_err(st32[used], st64[used]) <= 1e-4
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode16", "mixed", "decode256", "prefill4096"])
+def test_conv_f32_against_f64(orc, name):
+    """conv1d + SiLU: fp32 oracle within the parity bound of the fp64 oracle."""
+    case = ssm_inputs.conv_workload(name)
+    o32, s32 = orc.conv_case(case, precision="f32")
+    o64, s64 = orc.conv_case(case, precision="f64")
+    used = np.unique(case.slot)
+    assert np.all(np.isfinite(o32))
+    assert rel_err(o32, o64) <= 1e-4
+    assert np.array_equal(s32[used], s64[used].astype(np.float32))   # raw inputs, copied
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode16", "mixed", "decode256", "prefill4096"])
+def test_norm_f32_against_f64(orc, name):
+    case = ssm_inputs.norm_workload(name)
+    assert rel_err(orc.norm_case(case, precision="f32"), orc.norm_case(case, precision="f64")) <= 1e-4
