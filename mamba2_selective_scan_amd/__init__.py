@@ -1,8 +1,9 @@
 """Python binding of the MI355X Mamba2 selective-state scan library.
 
-Argument marshalling only: every step of the scan runs in the HIP kernels of
-``libssmscan.so`` (built from ``csrc/`` by ``build.py``), reached through its C
-ABI (``include/ssm_scan.h``).  torch supplies device memory and the current
+Argument marshalling only: every step of the scan, and of the conv1d + SiLU
+and gated RMSNorm beside it, runs in the HIP kernels of ``libssmscan.so``
+(built from ``csrc/`` by ``build.py``), reached through its C ABI
+(``include/ssm_scan.h``, ``include/ssm_conv_norm.h``).  torch supplies device memory and the current
 stream; tensors are passed as raw device pointers.  There is no CPU fallback:
 if the library is missing, importing this package raises.
 """
@@ -15,6 +16,7 @@ import re
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libssmscan.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "ssm_scan.h")
+HEADERS = [HEADER, os.path.join(os.path.dirname(PKG), "include", "ssm_conv_norm.h")]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -112,6 +114,21 @@ _lib.ssm_scan_decode_opt.argtypes = ([ctypes.POINTER(Dims), ctypes.POINTER(Optio
 _lib.ssm_scan_decode_opt.restype = ctypes.c_int
 
 
+class ConvDims(ctypes.Structure):
+    _fields_ = [("channels", ctypes.c_int32), ("kernel", ctypes.c_int32)]
+
+
+MAX_CONV_KERNEL = 4
+_lib.ssm_conv1d_silu_prefill.argtypes = ([ctypes.POINTER(ConvDims), _i32, _i32] + [_vp] * 6
+                                         + [_i32, _vp, _vp, _vp])
+_lib.ssm_conv1d_silu_prefill.restype = ctypes.c_int
+_lib.ssm_conv1d_silu_decode.argtypes = ([ctypes.POINTER(ConvDims), _i32] + [_vp] * 5
+                                        + [_i32, _vp, _vp])
+_lib.ssm_conv1d_silu_decode.restype = ctypes.c_int
+_lib.ssm_gated_rmsnorm.argtypes = [ctypes.c_int64, _i32, _vp, _vp, _vp, ctypes.c_float, _vp, _vp]
+_lib.ssm_gated_rmsnorm.restype = ctypes.c_int
+
+
 class ScanError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
@@ -129,9 +146,12 @@ def lib() -> ctypes.CDLL:
 
 
 def header_symbols() -> list:
-    """Names of the functions include/ssm_scan.h declares."""
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ssm_scan_\w+)\s*\(", text, re.M)))
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ssm_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def strerror(code: int) -> str:
@@ -346,6 +366,90 @@ def decode(x, dt, A, B, C, state, slot, fresh, y=None, stream=None, dt_bias=None
         rc = _lib.ssm_scan_decode_opt(ctypes.byref(Dims(H, P, N, G)), ctypes.byref(opts), S, *args)
         _check(rc, "ssm_scan_decode_opt")
     return y
+
+
+# ------------------------------------------------------------ beside the scan
+def conv1d_silu(x, weight, conv_state, cu_seqlens, slot, fresh, out=None, snapshots=None,
+                stream=None):
+    """Causal depthwise conv1d + SiLU over a packed batch
+    (``ssm_conv1d_silu_prefill``).
+
+    x [T, D], weight [D, K] (K <= 4), conv_state [n_slots, D, K-1] fp32
+    (updated in place); cu_seqlens [n_seqs+1] and slot [n_seqs] int32, fresh
+    [n_seqs] uint8; ``snapshots`` [T, D, K-1] fp32 receives the history after
+    every token.  Returns out [T, D] (``out`` if given)."""
+    import torch
+    T, D = (int(v) for v in x.shape)
+    K = int(weight.shape[1])
+    n_slots = int(conv_state.shape[0])
+    n_seqs = int(slot.shape[0])
+    if tuple(weight.shape) != (D, K) or tuple(conv_state.shape) != (n_slots, D, K - 1):
+        raise ValueError("weight or conv_state has the wrong shape")
+    if tuple(cu_seqlens.shape) != (n_seqs + 1,) or tuple(fresh.shape) != (n_seqs,):
+        raise ValueError("cu_seqlens or fresh has the wrong shape")
+    if snapshots is not None and tuple(snapshots.shape) != (T, D, K - 1):
+        raise ValueError("snapshots must have shape [T, D, K-1]")
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.float32, device=dev)
+    elif tuple(out.shape) != (T, D):
+        raise ValueError("out has the wrong shape")
+    f32 = torch.float32
+    rc = _lib.ssm_conv1d_silu_prefill(
+        ctypes.byref(ConvDims(D, K)), n_seqs, T, _dev_ptr(cu_seqlens, torch.int32, "cu_seqlens", dev),
+        _dev_ptr(slot, torch.int32, "slot", dev), _dev_ptr(fresh, torch.uint8, "fresh", dev),
+        _dev_ptr(x, f32, "x", dev), _dev_ptr(weight, f32, "weight", dev),
+        _dev_ptr(conv_state, f32, "conv_state", dev), n_slots, _dev_ptr(out, f32, "out", dev),
+        _dev_ptr(snapshots, f32, "snapshots", dev), _stream_handle(stream, dev))
+    _check(rc, "ssm_conv1d_silu_prefill")
+    return out
+
+
+def conv1d_silu_decode(x, weight, conv_state, slot, fresh, out=None, stream=None):
+    """One token per sequence (``ssm_conv1d_silu_decode``): x [S, D], the rest
+    as for ``conv1d_silu``.  Returns out [S, D]."""
+    import torch
+    S, D = (int(v) for v in x.shape)
+    K = int(weight.shape[1])
+    n_slots = int(conv_state.shape[0])
+    if tuple(weight.shape) != (D, K) or tuple(conv_state.shape) != (n_slots, D, K - 1):
+        raise ValueError("weight or conv_state has the wrong shape")
+    if tuple(slot.shape) != (S,) or tuple(fresh.shape) != (S,):
+        raise ValueError("slot or fresh has the wrong shape")
+    dev = x.device
+    if out is None:
+        out = torch.empty((S, D), dtype=torch.float32, device=dev)
+    elif tuple(out.shape) != (S, D):
+        raise ValueError("out has the wrong shape")
+    f32 = torch.float32
+    rc = _lib.ssm_conv1d_silu_decode(
+        ctypes.byref(ConvDims(D, K)), S, _dev_ptr(slot, torch.int32, "slot", dev),
+        _dev_ptr(fresh, torch.uint8, "fresh", dev), _dev_ptr(x, f32, "x", dev),
+        _dev_ptr(weight, f32, "weight", dev), _dev_ptr(conv_state, f32, "conv_state", dev),
+        n_slots, _dev_ptr(out, f32, "out", dev), _stream_handle(stream, dev))
+    _check(rc, "ssm_conv1d_silu_decode")
+    return out
+
+
+def gated_rmsnorm(y, z, weight, eps, out=None, stream=None):
+    """Gated RMSNorm over the last axis (``ssm_gated_rmsnorm``): y, z [..., L]
+    fp32, weight [L] shared by every row.  Returns out shaped like y."""
+    import torch
+    L = int(weight.shape[0])
+    if tuple(z.shape) != tuple(y.shape) or int(y.shape[-1]) != L or weight.dim() != 1:
+        raise ValueError("y, z and weight shapes disagree")
+    dev = y.device
+    if out is None:
+        out = torch.empty(y.shape, dtype=torch.float32, device=dev)
+    elif tuple(out.shape) != tuple(y.shape):
+        raise ValueError("out has the wrong shape")
+    f32 = torch.float32
+    rc = _lib.ssm_gated_rmsnorm(y.numel() // L, L, _dev_ptr(y, f32, "y", dev),
+                                _dev_ptr(z, f32, "z", dev), _dev_ptr(weight, f32, "weight", dev),
+                                float(eps), _dev_ptr(out, f32, "out", dev),
+                                _stream_handle(stream, dev))
+    _check(rc, "ssm_gated_rmsnorm")
+    return out
 
 
 def to_device(case, device="cuda:0"):

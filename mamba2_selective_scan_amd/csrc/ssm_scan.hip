@@ -14,8 +14,23 @@
 
 #include "correct_mfma.hpp"
 #include "scan_kernel.hpp"
+#include "status.hpp"
+
+namespace ssm {
+
+thread_local hipError_t t_last_hip_error = hipSuccess;
+
+int hip_fail(hipError_t err, int code) {
+    t_last_hip_error = err;
+    return code;
+}
+
+}  // namespace ssm
 
 namespace {
+
+using ssm::hip_fail;
+using ssm::t_last_hip_error;
 
 using ssm::kThreads;
 using ssm::ScanArgs;
@@ -53,13 +68,6 @@ const ShapeRow *shape_for(int N) {
 }
 
 constexpr int kMaxDevices = 64;
-
-thread_local hipError_t t_last_hip_error = hipSuccess;
-
-int hip_fail(hipError_t err, int code) {
-    t_last_hip_error = err;
-    return code;
-}
 
 template <class S, bool VEC, Mode MODE, int OPT = 0>
 int launch(const ScanArgs &a, hipStream_t stream) {

@@ -105,3 +105,62 @@ def sub_case(case, seqs):
                                slot=case.slot[list(seqs)], fresh=case.fresh[list(seqs)],
                                x=case.x[idx], dt=case.dt[idx], A=case.A, B=case.B[idx],
                                C=case.C[idx], state=case.state, name=case.name + f"[{seqs}]")
+
+
+def _put(arr, device, offset_floats=0):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(arr))
+    if offset_floats and t.dtype == torch.float32:
+        flat = torch.empty(t.numel() + offset_floats, dtype=t.dtype, device=device)
+        view = flat[offset_floats:].view(t.shape)
+        view.copy_(t.to(device))
+        return view
+    return t.to(device)
+
+
+def run_conv_gpu(case, mode="prefill", device="cuda:0", offset_floats=0, snapshots=False):
+    """Run an ``ssm_inputs.ConvCase`` through the conv1d + SiLU ABI; returns
+    (out, state) or (out, state, snapshots) as numpy.  ``mode`` "prefill" or
+    "decode" (every length 1); ``offset_floats`` > 0 breaks 16-byte alignment."""
+    import torch
+    import mamba2_selective_scan_amd as ssm
+    put = lambda a: _put(a, device, offset_floats)
+    x, w, st = put(case.x), put(case.w), put(case.state)
+    slot, fresh = put(case.slot), put(case.fresh)
+    out = put(np.full((case.n_tokens, case.D), np.nan, np.float32))
+    snaps = (put(np.full((case.n_tokens, case.D, case.K - 1), np.nan, np.float32))
+             if snapshots else None)
+    if mode == "prefill":
+        ssm.conv1d_silu(x, w, st, put(case.cu_seqlens), slot, fresh, out=out, snapshots=snaps)
+    elif mode == "decode":
+        assert np.all(case.lengths == 1) and not snapshots
+        ssm.conv1d_silu_decode(x, w, st, slot, fresh, out=out)
+    else:
+        raise ValueError(mode)
+    torch.cuda.synchronize()
+    res = (out.cpu().numpy(), st.cpu().numpy())
+    return res + (snaps.cpu().numpy(),) if snapshots else res
+
+
+def assert_conv_parity(case, out_gpu, st_gpu, out_ref, st_ref, tol=TOL, label=""):
+    """out within ``tol``; the history holds raw inputs, so it must match
+    bitwise; slots no sequence names come back unchanged."""
+    used = np.unique(case.slot)
+    e = rel_err(out_gpu, out_ref)
+    say(f"  {label or case.name}: max rel err out={e:.3e}")
+    assert np.all(np.isfinite(out_gpu)), "non-finite output"
+    assert e <= tol, f"output error {e} > {tol}"
+    assert np.array_equal(st_gpu[used], st_ref[used]), "history differs"
+    for k in np.setdiff1d(np.arange(case.n_slots), used):
+        assert np.array_equal(st_gpu[k], case.state[k], equal_nan=True), f"unused slot {k} changed"
+
+
+def run_norm_gpu(case, device="cuda:0", offset_floats=0, eps=None):
+    import torch
+    import mamba2_selective_scan_amd as ssm
+    put = lambda a: _put(a, device, offset_floats)
+    y, z, w = put(case.y), put(case.z), put(case.w)
+    out = put(np.full(case.y.shape, np.nan, np.float32))
+    ssm.gated_rmsnorm(y, z, w, case.eps if eps is None else eps, out=out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()

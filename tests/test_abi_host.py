@@ -1,5 +1,5 @@
 """The C-ABI library on the host (no GPU): it loads, exports every function
-include/ssm_scan.h declares, rejects bad arguments with the documented codes
+include/ssm_scan.h and include/ssm_conv_norm.h declare, rejects bad arguments with the documented codes
 before touching any device, and reports launch geometry; every compiled
 kernel keeps its state in registers (no scratch)."""
 import ctypes
@@ -21,7 +21,9 @@ def test_exports_every_declared_symbol():
                           "ssm_scan_query_geometry", "ssm_scan_last_hip_error",
                           "ssm_scan_last_hip_error_string", "ssm_scan_prefill_ws",
                           "ssm_scan_prefill_workspace_size", "ssm_scan_query_prefill_plan",
-                          "ssm_scan_prefill_opt", "ssm_scan_decode_opt"}
+                          "ssm_scan_prefill_opt", "ssm_scan_decode_opt",
+                          "ssm_conv1d_silu_prefill", "ssm_conv1d_silu_decode",
+                          "ssm_gated_rmsnorm"}
     for n in names:
         assert hasattr(m.lib(), n), n
 
@@ -116,8 +118,13 @@ def test_no_kernel_uses_scratch():
     names = re.findall(r"Function Name: (\S+)", text)
     scratch = [int(v) for v in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
     # 7 state-size classes x (vector, scalar) x (4 option sets x (prefill, decode)
-    # + segment scan + correction) + 2 combine kernels + 3 matrix-core corrections
-    assert len(names) == 7 * 2 * (4 * 2 + 2) + 2 + 3 and len(scratch) == len(names)
+    # + segment scan + correction) + 2 combine kernels + 3 matrix-core corrections;
+    # conv1d + SiLU: (vector, scalar) x (4 history lengths x (decode, prefill)
+    # + 3 with snapshots); gated RMSNorm: (vector, scalar) x 6 row-length classes
+    n_scan = 7 * 2 * (4 * 2 + 2) + 2 + 3
+    n_conv = 2 * (4 * 2 + 3)
+    n_norm = 2 * 6
+    assert len(names) == n_scan + n_conv + n_norm and len(scratch) == len(names)
     assert all(v == 0 for v in scratch), dict(zip(names, scratch))
 
 
@@ -152,3 +159,58 @@ def test_prefill_ws_errors(bad):
                                      kw["n_segments"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                      FAKE, FAKE, 1, FAKE, None, 0, None)
     assert rc == m.SSM_ERR_DIMS
+
+
+# ------------------------------------------------------------ conv1d + SiLU, gated RMSNorm
+CD = m.ConvDims
+
+
+def _conv(dims, n_seqs=1, n_tokens=4, ptrs=None, n_slots=1, fake=FAKE, decode=False):
+    p = dict(cu=fake, slot=fake, fresh=fake, x=fake, w=fake, state=fake, out=fake, snaps=None)
+    p.update(ptrs or {})
+    d = None if dims is None else ctypes.byref(dims)
+    if decode:
+        return m.lib().ssm_conv1d_silu_decode(d, n_seqs, p["slot"], p["fresh"], p["x"], p["w"],
+                                              p["state"], n_slots, p["out"], None)
+    return m.lib().ssm_conv1d_silu_prefill(d, n_seqs, n_tokens, p["cu"], p["slot"], p["fresh"],
+                                           p["x"], p["w"], p["state"], n_slots, p["out"],
+                                           p["snaps"], None)
+
+
+@pytest.mark.parametrize("decode", [False, True])
+def test_conv_argument_errors(decode):
+    ok = CD(64, 4)
+    call = lambda *a, **k: _conv(*a, decode=decode, **k)
+    assert call(None) == m.SSM_ERR_NULL
+    assert call(CD(0, 4)) == m.SSM_ERR_DIMS
+    assert call(CD(64, 0)) == m.SSM_ERR_DIMS
+    assert call(CD(64, 5)) == m.SSM_ERR_UNSUPPORTED
+    assert call(ok, n_seqs=-1) == m.SSM_ERR_DIMS
+    assert call(ok, n_seqs=0) == m.SSM_OK                 # no-op, nothing touched
+    assert call(ok, n_slots=0) == m.SSM_ERR_DIMS
+    for name in ("slot", "fresh", "x", "w", "state", "out"):
+        assert call(ok, ptrs={name: None}) == m.SSM_ERR_NULL, name
+    for name in ("x", "w", "state", "out"):
+        assert call(ok, ptrs={name: FAKE + 2}) == m.SSM_ERR_ALIGN, name
+    assert call(ok, ptrs={"slot": FAKE + 1}) == m.SSM_ERR_ALIGN
+    if not decode:
+        assert call(ok, n_tokens=-1) == m.SSM_ERR_DIMS
+        assert call(ok, ptrs={"cu": None}) == m.SSM_ERR_NULL
+        assert call(ok, ptrs={"cu": FAKE + 2}) == m.SSM_ERR_ALIGN
+        assert call(ok, ptrs={"snaps": FAKE + 2}) == m.SSM_ERR_ALIGN
+
+
+def test_norm_argument_errors():
+    f = m.lib().ssm_gated_rmsnorm
+    assert f(4, 0, FAKE, FAKE, FAKE, 1e-5, FAKE, None) == m.SSM_ERR_DIMS
+    assert f(-1, 8, FAKE, FAKE, FAKE, 1e-5, FAKE, None) == m.SSM_ERR_DIMS
+    assert f(4, 8, FAKE, FAKE, FAKE, -1.0, FAKE, None) == m.SSM_ERR_DIMS
+    assert f(4, 8, FAKE, FAKE, FAKE, float("nan"), FAKE, None) == m.SSM_ERR_DIMS
+    assert f(4, 8, FAKE, FAKE, FAKE, float("inf"), FAKE, None) == m.SSM_ERR_DIMS
+    assert f(0, 8, None, None, None, 1e-5, None, None) == m.SSM_OK
+    for i in range(4):
+        ptrs = [FAKE] * 4
+        ptrs[i] = None
+        assert f(4, 8, ptrs[0], ptrs[1], ptrs[2], 1e-5, ptrs[3], None) == m.SSM_ERR_NULL
+        ptrs[i] = FAKE + 2
+        assert f(4, 8, ptrs[0], ptrs[1], ptrs[2], 1e-5, ptrs[3], None) == m.SSM_ERR_ALIGN
