@@ -283,6 +283,87 @@ def secondary(args, dev, stream):
     return out
 
 
+def _graph_us(calls, replays, stream):
+    """Capture ``calls`` (closures that each enqueue one launch) in one HIP
+    graph, replay it ``replays`` times between HIP events and return the
+    average time per call in microseconds (launch overhead out of the way)."""
+    import torch
+    for f in calls:                                     # eager warm-up
+        f()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for f in calls:
+            f()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (replays * len(calls))
+
+
+def beside(args, dev, stream):
+    """The steps beside the scan in a layer at the same geometry: causal conv1d
+    + SiLU over D = H*P + 2*G*N channels (K = 4) and gated RMSNorm over y
+    [T][H][P].  Both are HBM-bound; algorithmic bytes count every operand
+    once (the conv history only where it is read or written).  Each line is
+    the average over a replayed HIP graph of 8 launches."""
+    import torch
+
+    import mamba2_selective_scan_amd as ssm
+    import ssm_inputs
+    out = {}
+    D = ssm_inputs.conv_channels(H, P, N, G)
+    K = 4
+
+    def line(us, nbytes, **extra):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return dict({"us": round(us, 2), "GBs": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes},
+                    **extra)
+
+    c = ssm_inputs.conv_workload("prefill4096")
+    t = {f: torch.from_numpy(getattr(c, f)).to(dev)
+         for f in ("x", "w", "state", "cu_seqlens", "slot", "fresh")}
+    o = torch.empty((PREFILL_T, D), device=dev)
+    conv = lambda: ssm.conv1d_silu(t["x"], t["w"], t["state"], t["cu_seqlens"], t["slot"],
+                                   t["fresh"], out=o)
+    us = _graph_us([conv] * 8, 10, stream)
+    nbytes = 4 * (2 * PREFILL_T * D + D * K + D * (K - 1))
+    out["conv1d_silu_prefill_1x4096_D6144_K4"] = line(us, nbytes)
+    del t, o
+    # decode: rotate over 8 slot sets so the histories are not cache-resident
+    for n_seq in (16, 256):
+        sets = 8
+        c = ssm_inputs.make_conv_case(D, K, [1] * n_seq, [0] * n_seq, 11, n_slots=n_seq * sets)
+        x, w = torch.from_numpy(c.x).to(dev), torch.from_numpy(c.w).to(dev)
+        st = torch.from_numpy(c.state).to(dev)
+        fresh = torch.from_numpy(c.fresh).to(dev)
+        slots = [torch.arange(k * n_seq, (k + 1) * n_seq, dtype=torch.int32, device=dev)
+                 for k in range(sets)]
+        o = torch.empty((n_seq, D), device=dev)
+        calls = [(lambda k=k: ssm.conv1d_silu_decode(x, w, st, slots[k], fresh, out=o))
+                 for k in range(sets)]
+        us = _graph_us(calls, 40, stream)
+        nbytes = 4 * (2 * n_seq * D + D * K + 2 * n_seq * D * (K - 1))
+        out[f"conv1d_silu_decode_{n_seq}x1_D6144_K4"] = line(
+            us, nbytes, note=f"{sets} history slot sets rotated")
+        del x, w, st, o, slots, calls
+    for name, T in (("prefill4096", PREFILL_T), ("decode16", 16), ("decode256", 256)):
+        nc = ssm_inputs.norm_workload(name)
+        y, z, w = (torch.from_numpy(getattr(nc, f)).to(dev) for f in ("y", "z", "w"))
+        o = torch.empty_like(y)
+        us = _graph_us([lambda: ssm.gated_rmsnorm(y, z, w, nc.eps, out=o)] * 8, 20, stream)
+        nbytes = 4 * (3 * T * H * P + P)
+        out[f"gated_rmsnorm_{T}x{H}x{P}"] = line(us, nbytes)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -447,6 +528,7 @@ def main():
 
     if not args.no_secondary:
         result["secondary"] = secondary(args, dev, stream)
+        result["beside_the_scan"] = beside(args, dev, stream)
 
     if not args.no_cpu_baseline:
         one_set = ssm_inputs.workload("decode16")
