@@ -1,5 +1,6 @@
-"""CPU oracle for the Mamba2 selective-state scan and its neighbouring steps
-(causal conv1d + SiLU, gated RMSNorm) -- TEST INFRASTRUCTURE.
+"""CPU oracle for the Mamba2 selective-state scan, its neighbouring steps
+(causal conv1d + SiLU, gated RMSNorm) and the gated delta-rule recurrence --
+TEST INFRASTRUCTURE.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
 leg may import this package.  The GPU library never calls it and shares no code
@@ -59,6 +60,11 @@ class Oracle:
         self.lib.ssm_oracle_gated_rmsnorm_f64.argtypes = norm + [ctypes.c_double, _f64p,
                                                                  ctypes.c_int32]
         self.lib.ssm_oracle_gated_rmsnorm_f64.restype = ctypes.c_int
+        gdn = [ctypes.c_int32] * 5 + [_i32p, _i32p, _u8p] + [_f32p] * 5
+        self.lib.ssm_oracle_gdn_f32.argtypes = gdn + [ctypes.c_float] + [_f32p] * 3 + [ctypes.c_int32]
+        self.lib.ssm_oracle_gdn_f32.restype = ctypes.c_int
+        self.lib.ssm_oracle_gdn_f64.argtypes = gdn + [ctypes.c_double] + [_f64p] * 3 + [ctypes.c_int32]
+        self.lib.ssm_oracle_gdn_f64.restype = ctypes.c_int
 
     def scan(self, H, P, N, G, cu_seqlens, slot, fresh, x, dt, A, B, C, state,
              precision="f32", threads=None, dt_bias=None, dt_softplus=False,
@@ -190,6 +196,47 @@ class Oracle:
         """``gated_rmsnorm`` on an ``ssm_inputs.NormCase``."""
         return self.gated_rmsnorm(case.y, case.z, case.w, case.eps, precision=precision,
                                   threads=threads)
+
+    # ------------------------------------------------------------ delta rule
+    def gdn(self, Hv, Hk, Dk, Dv, cu_seqlens, slot, fresh, q, k, v, g, beta, scale, state,
+            precision="f32", threads=None, snapshots=False):
+        """Gated delta-rule recurrence over a packed batch.  q, k [T][Hk][Dk],
+        v [T][Hv][Dv], g and beta [T][Hv], state [n_slots][Hv][Dv][Dk] (not
+        modified).  Returns ``(y, state_out)`` or ``(y, state_out, snapshots)``."""
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        slot = np.ascontiguousarray(slot, dtype=np.int32)
+        fresh = np.ascontiguousarray(fresh, dtype=np.uint8)
+        q, k, v, g, beta = (np.ascontiguousarray(a, dtype=np.float32) for a in (q, k, v, g, beta))
+        n_seqs = slot.shape[0]
+        T = int(cu[-1]) if cu.shape[0] else 0
+        assert cu.shape[0] == n_seqs + 1
+        assert q.shape == (T, Hk, Dk) and k.shape == (T, Hk, Dk) and v.shape == (T, Hv, Dv)
+        assert g.shape == (T, Hv) and beta.shape == (T, Hv)
+        assert state.ndim == 4 and state.shape[1:] == (Hv, Dv, Dk)
+        if threads is None:
+            threads = os.cpu_count() or 1
+        if precision == "f32":
+            dtype, fn, fp = np.float32, self.lib.ssm_oracle_gdn_f32, _f32p
+        elif precision == "f64":
+            dtype, fn, fp = np.float64, self.lib.ssm_oracle_gdn_f64, _f64p
+        else:
+            raise ValueError(precision)
+        st = np.array(state, dtype=dtype, copy=True, order="C")
+        y = np.zeros((T, Hv, Dv), dtype=dtype)
+        snaps = np.zeros((T, Hv, Dv, Dk), dtype=dtype) if snapshots else None
+        rc = fn(Hv, Hk, Dk, Dv, n_seqs, _ptr(cu, _i32p), _ptr(slot, _i32p), _ptr(fresh, _u8p),
+                _ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p), _ptr(g, _f32p),
+                _ptr(beta, _f32p), float(scale), _ptr(st, fp), _ptr(y, fp),
+                None if snaps is None else _ptr(snaps, fp), int(threads))
+        if rc != 0:
+            raise ValueError(f"oracle rejected the dimensions (rc={rc})")
+        return (y, st, snaps) if snapshots else (y, st)
+
+    def gdn_case(self, case, precision="f32", threads=None, snapshots=False):
+        """``gdn`` on an ``ssm_inputs.GdnCase``."""
+        return self.gdn(case.Hv, case.Hk, case.Dk, case.Dv, case.cu_seqlens, case.slot,
+                        case.fresh, case.q, case.k, case.v, case.g, case.beta, case.scale,
+                        case.state, precision=precision, threads=threads, snapshots=snapshots)
 
 
 _default = None

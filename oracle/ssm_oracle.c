@@ -1,7 +1,8 @@
 /*
  * ssm_oracle.c -- plain, sequential CPU oracle for the Mamba2 selective-state scan
  * and the two steps beside it in a layer (causal conv1d + SiLU with a rolling
- * history, gated RMSNorm; see the second half of this file).
+ * history, gated RMSNorm), and the gated delta-rule recurrence (the second
+ * workload on the same register design); each section cites its source.
  *
  * TEST INFRASTRUCTURE.  This file is the correctness reference the GPU library
  * is compared against.  Only the tests, the smoke check and the benchmark's CPU
@@ -55,7 +56,7 @@
 #include <stdint.h>
 #include <string.h>
 
-int ssm_oracle_version(void) { return 3; }
+int ssm_oracle_version(void) { return 4; }
 
 /* dt after the optional bias and softplus (see the header). */
 static float dt_eff_f32(float dt, const float *dt_bias, int64_t hd, int32_t softplus)
@@ -349,6 +350,126 @@ int ssm_oracle_gated_rmsnorm_f64(int64_t n_rows, int32_t L, const float *y, cons
         const double inv_rms = 1.0 / sqrt(sum_sq / (double)L + eps);
         for (int64_t d = 0; d < L; ++d)
             out[r * L + d] = (double)yr[d] * inv_rms * (double)w[d] * silu_f64((double)zr[d]);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Gated delta-rule recurrence ("ssm_gated_delta.cu": fc_ssm_recurrence for one
+ * token, fc_ssm_recurrence_seq for a run of positions with optional
+ * snapshots, fc_ssm_recurrence_slots for one token of several users).
+ *
+ * Per value head vh the state is Dv rows of Dk values, stored transposed as on
+ * that page: row j (one value coordinate) is contiguous over the key
+ * coordinate i.  Queries and keys come per key head kh; value heads map to key
+ * heads interleaved, kh = vh % Hk (the page's GQA tiling vh = r*Hk + kh).  Per
+ * token, for every row j, in this order:
+ *     row[i] = row[i] * exp(g)                          (decay)
+ *     pred   = sum_i row[i] * k[i]                      (retrieval)
+ *     delta  = (v[j] - pred) * beta
+ *     row[i] = row[i] + k[i] * delta                    (rank-1 write)
+ *     y[j]   = scale * sum_i row[i] * q[i]              (read after the write)
+ * Layouts: q, k [T][Hk][Dk]; v, y [T][Hv][Dv]; g (log decay, exp'd here) and
+ * beta [T][Hv]; state [n_slots][Hv][Dv][Dk]; snapshots [T][Hv][Dv][Dk].  Slot,
+ * fresh and zero-length rules are the scan's.  (sequence, value head) pairs
+ * are independent and may run on several threads.
+ * ------------------------------------------------------------------------ */
+int ssm_oracle_gdn_f32(int32_t Hv, int32_t Hk, int32_t Dk, int32_t Dv, int32_t n_seqs,
+                       const int32_t *cu_seqlens, const int32_t *slot, const uint8_t *fresh,
+                       const float *q, const float *k, const float *v, const float *g,
+                       const float *beta, float scale, float *state, float *y,
+                       float *snapshots, int32_t n_threads)
+{
+    if (Hv <= 0 || Hk <= 0 || Dk <= 0 || Dv <= 0 || Hv % Hk != 0 || n_seqs < 0)
+        return -1;
+    if (n_threads < 1)
+        n_threads = 1;
+    const int64_t pairs = (int64_t)n_seqs * Hv;
+    const int64_t block = (int64_t)Dv * Dk;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads)
+    for (int64_t w = 0; w < pairs; ++w) {
+        const int64_t s = w / Hv;
+        const int64_t vh = w % Hv;
+        const int64_t kh = vh % Hk;
+        float *st = state + ((int64_t)slot[s] * Hv + vh) * block;
+        if (fresh[s])
+            for (int64_t e = 0; e < block; ++e)
+                st[e] = 0.0f;
+        for (int64_t t = cu_seqlens[s]; t < cu_seqlens[s + 1]; ++t) {
+            const float decay = expf(g[t * Hv + vh]);
+            const float b = beta[t * Hv + vh];
+            const float *kt = k + (t * Hk + kh) * Dk;
+            const float *qt = q + (t * Hk + kh) * Dk;
+            for (int64_t j = 0; j < Dv; ++j) {
+                float *row = st + j * Dk;
+                for (int64_t i = 0; i < Dk; ++i)
+                    row[i] = row[i] * decay;
+                float pred = 0.0f;
+                for (int64_t i = 0; i < Dk; ++i)
+                    pred += row[i] * kt[i];
+                const float delta = (v[(t * Hv + vh) * Dv + j] - pred) * b;
+                for (int64_t i = 0; i < Dk; ++i)
+                    row[i] = row[i] + kt[i] * delta;
+                float acc = 0.0f;
+                for (int64_t i = 0; i < Dk; ++i)
+                    acc += row[i] * qt[i];
+                y[(t * Hv + vh) * Dv + j] = scale * acc;
+            }
+            if (snapshots)
+                memcpy(snapshots + (t * Hv + vh) * block, st, sizeof(float) * (size_t)block);
+        }
+    }
+    return 0;
+}
+
+/* The same in double (inputs fp32; state, y and snapshots double). */
+int ssm_oracle_gdn_f64(int32_t Hv, int32_t Hk, int32_t Dk, int32_t Dv, int32_t n_seqs,
+                       const int32_t *cu_seqlens, const int32_t *slot, const uint8_t *fresh,
+                       const float *q, const float *k, const float *v, const float *g,
+                       const float *beta, double scale, double *state, double *y,
+                       double *snapshots, int32_t n_threads)
+{
+    if (Hv <= 0 || Hk <= 0 || Dk <= 0 || Dv <= 0 || Hv % Hk != 0 || n_seqs < 0)
+        return -1;
+    if (n_threads < 1)
+        n_threads = 1;
+    const int64_t pairs = (int64_t)n_seqs * Hv;
+    const int64_t block = (int64_t)Dv * Dk;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads)
+    for (int64_t w = 0; w < pairs; ++w) {
+        const int64_t s = w / Hv;
+        const int64_t vh = w % Hv;
+        const int64_t kh = vh % Hk;
+        double *st = state + ((int64_t)slot[s] * Hv + vh) * block;
+        if (fresh[s])
+            for (int64_t e = 0; e < block; ++e)
+                st[e] = 0.0;
+        for (int64_t t = cu_seqlens[s]; t < cu_seqlens[s + 1]; ++t) {
+            const double decay = exp((double)g[t * Hv + vh]);
+            const double b = (double)beta[t * Hv + vh];
+            const float *kt = k + (t * Hk + kh) * Dk;
+            const float *qt = q + (t * Hk + kh) * Dk;
+            for (int64_t j = 0; j < Dv; ++j) {
+                double *row = st + j * Dk;
+                for (int64_t i = 0; i < Dk; ++i)
+                    row[i] = row[i] * decay;
+                double pred = 0.0;
+                for (int64_t i = 0; i < Dk; ++i)
+                    pred += row[i] * (double)kt[i];
+                const double delta = ((double)v[(t * Hv + vh) * Dv + j] - pred) * b;
+                for (int64_t i = 0; i < Dk; ++i)
+                    row[i] = row[i] + (double)kt[i] * delta;
+                double acc = 0.0;
+                for (int64_t i = 0; i < Dk; ++i)
+                    acc += row[i] * (double)qt[i];
+                y[(t * Hv + vh) * Dv + j] = scale * acc;
+            }
+            if (snapshots)
+                for (int64_t e = 0; e < block; ++e)
+                    snapshots[(t * Hv + vh) * block + e] = st[e];
+        }
     }
     return 0;
 }

@@ -25,7 +25,8 @@ import numpy as np
 
 __all__ = ["ScanCase", "make_case", "WORKLOADS", "workload", "lengths_to_cu",
            "ConvCase", "make_conv_case", "CONV_WORKLOADS", "conv_workload",
-           "NormCase", "make_norm_case", "NORM_WORKLOADS", "norm_workload"]
+           "NormCase", "make_norm_case", "NORM_WORKLOADS", "norm_workload",
+           "GdnCase", "make_gdn_case", "GDN_WORKLOADS", "gdn_workload"]
 
 
 @dataclass
@@ -294,3 +295,107 @@ NORM_WORKLOADS = {
 
 def norm_workload(name: str, **kw) -> NormCase:
     return NORM_WORKLOADS[name](**kw)
+
+
+# ---------------------------------------------------------------------------
+# Gated delta-rule recurrence ("ssm_gated_delta.cu").  q, k [T][Hk][Dk] arrive
+# L2-normalised per head, as on that page; v [T][Hv][Dv]; the log decay
+# g = a[h] * dt with a = -exp(U[0, ln 16]) per head and dt ~ U[0.001, 0.1]
+# (the scan's decay distribution, g in [-1.6, -0.001]); beta = sigmoid(N(0,1));
+# a resuming state ~ 0.5 * N(0, 1); scale = 1/sqrt(Dk).  Draw order: a, dt, q,
+# k, v, beta, state.  The page's model geometry: Hv 32, Hk 16, Dk = Dv = 128.
+# ---------------------------------------------------------------------------
+@dataclass
+class GdnCase:
+    Hv: int
+    Hk: int
+    Dk: int
+    Dv: int
+    lengths: np.ndarray
+    cu_seqlens: np.ndarray
+    slot: np.ndarray
+    fresh: np.ndarray
+    q: np.ndarray                # f32 [T, Hk, Dk], unit rows
+    k: np.ndarray                # f32 [T, Hk, Dk], unit rows
+    v: np.ndarray                # f32 [T, Hv, Dv]
+    g: np.ndarray                # f32 [T, Hv], log decay
+    beta: np.ndarray             # f32 [T, Hv]
+    state: np.ndarray            # f32 [n_slots, Hv, Dv, Dk]
+    scale: float
+    seed: int = 0
+    name: str = ""
+
+    @property
+    def n_seqs(self) -> int:
+        return int(self.lengths.shape[0])
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def n_slots(self) -> int:
+        return int(self.state.shape[0])
+
+
+def _unit_rows(a):
+    n = np.sqrt(np.sum(a.astype(np.float64) ** 2, axis=-1, keepdims=True))
+    return (a / np.maximum(n, 1e-6)).astype(np.float32)
+
+
+def make_gdn_case(Hv, Hk, Dk, Dv, lengths, fresh, seed, *, slots=None, n_slots=None,
+                  state_std=0.5, poison_fresh=False, sentinel_unused=False, name="") -> GdnCase:
+    lengths = np.asarray(lengths, dtype=np.int32)
+    fresh = np.asarray(fresh, dtype=np.uint8)
+    n_seqs = lengths.shape[0]
+    if slots is None:
+        slots = np.arange(n_seqs, dtype=np.int32)
+    slots = np.asarray(slots, dtype=np.int32)
+    if n_slots is None:
+        n_slots = int(slots.max()) + 1 if n_seqs else 0
+    cu = lengths_to_cu(lengths)
+    T = int(cu[-1])
+    rng = np.random.Generator(np.random.PCG64(seed))
+    a = -np.exp(rng.uniform(0.0, math.log(16.0), size=Hv))
+    dt = rng.uniform(0.001, 0.1, size=(T, Hv))
+    g = (a[None, :] * dt).astype(np.float32)
+    q = _unit_rows(rng.standard_normal((T, Hk, Dk), dtype=np.float32))
+    k = _unit_rows(rng.standard_normal((T, Hk, Dk), dtype=np.float32))
+    v = rng.standard_normal((T, Hv, Dv), dtype=np.float32)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((T, Hv))))).astype(np.float32)
+    state = rng.standard_normal((n_slots, Hv, Dv, Dk), dtype=np.float32)
+    state *= np.float32(state_std)
+    if sentinel_unused:
+        used = np.zeros(n_slots, dtype=bool)
+        used[slots] = True
+        for kk in np.nonzero(~used)[0]:
+            state[kk] = np.float32(1000.0 + kk)
+    if poison_fresh:
+        for s in range(n_seqs):
+            if fresh[s]:
+                state[slots[s]] = np.nan
+    return GdnCase(Hv=Hv, Hk=Hk, Dk=Dk, Dv=Dv, lengths=lengths, cu_seqlens=cu, slot=slots,
+                   fresh=fresh, q=q, k=k, v=v, g=g, beta=beta, state=state,
+                   scale=float(np.float32(1.0 / math.sqrt(Dk))), seed=seed, name=name)
+
+
+GDN_WORKLOADS = {
+    "tiny": lambda seed=30: make_gdn_case(4, 2, 16, 16, [64], [1], seed,
+                                          name="gdn_tiny_T64_Hv4_Hk2_D16"),
+    "decode16": lambda seed=31, sets=1: make_gdn_case(
+        32, 16, 128, 128, [1] * 16, [0] * 16, seed, n_slots=16 * sets,
+        name="gdn_decode_16x1_Hv32_Hk16_D128"),
+    "prefill4096": lambda seed=32: make_gdn_case(32, 16, 128, 128, [4096], [1], seed,
+                                                 name="gdn_prefill_1x4096_Hv32_Hk16_D128"),
+    "mixed": lambda seed=33: make_gdn_case(
+        8, 4, 100, 96, [1, 7, 25, 26, 64, 100, 150, 150], [1 - (i % 2) for i in range(8)], seed,
+        slots=np.random.Generator(np.random.PCG64(seed + 1000)).permutation(10)[:8]
+        .astype(np.int32), n_slots=10, poison_fresh=True, sentinel_unused=True,
+        name="gdn_mixed_8seq_Hv8_Hk4_Dk100_Dv96"),
+    "decode256": lambda seed=34: make_gdn_case(32, 16, 128, 128, [1] * 256, [0] * 256, seed,
+                                               name="gdn_decode_256x1_Hv32_Hk16_D128"),
+}
+
+
+def gdn_workload(name: str, **kw) -> GdnCase:
+    return GDN_WORKLOADS[name](**kw)

@@ -364,3 +364,8 @@ ALL_PINS = [pin_hand_worked, pin_brute_force, pin_brute_force_tiny_workload,
 from neighbour_pins import CONV_PINS, NORM_PINS  # noqa: E402
 
 ALL_PINS = ALL_PINS + CONV_PINS + NORM_PINS
+
+# the gated delta-rule recurrence
+from gdn_pins import GDN_PINS  # noqa: E402
+
+ALL_PINS = ALL_PINS + GDN_PINS

@@ -37,8 +37,8 @@ MUTANTS = [
      "float *h = state + ((int64_t)s * H + hd) * P * N;"),
     ("state_index_transposed", "float *h_p = h + p * N;", "float *h_p = h + p;"),
     ("dt_head_index_wrong", "dt_eff_f32(dt[t * H + hd],", "dt_eff_f32(dt[t * H + (H - 1 - hd)],"),
-    ("y_not_reset_per_row", "                float acc = 0.0f;\n",
-     "                float acc = (float)p;\n"),
+    ("y_not_reset_per_row", "                float acc = 0.0f;\n                for (int64_t n = 0;",
+     "                float acc = (float)p;\n                for (int64_t n = 0;"),
     # options
     ("softplus_cutoff_reversed", "if (softplus && v <= 20.0f)", "if (softplus && v > 20.0f)"),
     ("softplus_not_applied", "        v = log1pf(expf(v));", "        v = v;"),
@@ -85,6 +85,39 @@ MUTANTS = [
     ("norm_gate_from_y", "out[r * L + d] = yr[d] * inv_rms * w[d] * silu_f32(zr[d]);",
      "out[r * L + d] = yr[d] * inv_rms * w[d] * silu_f32(yr[d]);"),
     ("norm_abs_not_square", "sum_sq += yr[d] * yr[d];", "sum_sq += fabsf(yr[d]);"),
+    # gated delta rule
+    ("gdn_decay_not_exp", "const float decay = expf(g[t * Hv + vh]);",
+     "const float decay = g[t * Hv + vh];"),
+    ("gdn_decay_after_retrieval",
+     "                for (int64_t i = 0; i < Dk; ++i)\n                    row[i] = row[i] * decay;\n"
+     "                float pred = 0.0f;\n                for (int64_t i = 0; i < Dk; ++i)\n"
+     "                    pred += row[i] * kt[i];\n",
+     "                float pred = 0.0f;\n                for (int64_t i = 0; i < Dk; ++i)\n"
+     "                    pred += row[i] * kt[i];\n                for (int64_t i = 0; i < Dk; ++i)\n"
+     "                    row[i] = row[i] * decay;\n"),
+    ("gdn_delta_sign", "const float delta = (v[(t * Hv + vh) * Dv + j] - pred) * b;",
+     "const float delta = (pred - v[(t * Hv + vh) * Dv + j]) * b;"),
+    ("gdn_beta_ignored", "const float delta = (v[(t * Hv + vh) * Dv + j] - pred) * b;",
+     "const float delta = (v[(t * Hv + vh) * Dv + j] - pred);"),
+    ("gdn_write_with_query", "row[i] = row[i] + kt[i] * delta;\n                float acc = 0.0f;",
+     "row[i] = row[i] + qt[i] * delta;\n                float acc = 0.0f;"),
+    ("gdn_y_before_write",
+     "                for (int64_t i = 0; i < Dk; ++i)\n                    row[i] = row[i] + kt[i] * delta;\n"
+     "                float acc = 0.0f;\n                for (int64_t i = 0; i < Dk; ++i)\n"
+     "                    acc += row[i] * qt[i];\n",
+     "                float acc = 0.0f;\n                for (int64_t i = 0; i < Dk; ++i)\n"
+     "                    acc += row[i] * qt[i];\n                for (int64_t i = 0; i < Dk; ++i)\n"
+     "                    row[i] = row[i] + kt[i] * delta;\n"),
+    ("gdn_gqa_contiguous", "        const int64_t kh = vh % Hk;\n        float *st",
+     "        const int64_t kh = vh / (Hv / Hk);\n        float *st"),
+    ("gdn_scale_missing", "acc += row[i] * qt[i];\n                y[(t * Hv + vh) * Dv + j] = scale * acc;",
+     "acc += row[i] * qt[i];\n                y[(t * Hv + vh) * Dv + j] = acc;"),
+    ("gdn_rows_overlap", "float *row = st + j * Dk;", "float *row = st + j;"),
+    ("gdn_fresh_ignored", "        if (fresh[s])\n            for (int64_t e = 0; e < block; ++e)\n"
+     "                st[e] = 0.0f;",
+     "        if (0)\n            for (int64_t e = 0; e < block; ++e)\n                st[e] = 0.0f;"),
+    ("gdn_value_index_wrong", "const float delta = (v[(t * Hv + vh) * Dv + j] - pred) * b;",
+     "const float delta = (v[(t * Hv + vh) * Dv + (Dv - 1 - j)] - pred) * b;"),
 ]
 
 

@@ -46,3 +46,15 @@ def test_conv_f32_against_f64(orc, name):
 def test_norm_f32_against_f64(orc, name):
     case = ssm_inputs.norm_workload(name)
     assert rel_err(orc.norm_case(case, precision="f32"), orc.norm_case(case, precision="f64")) <= 1e-4
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode16", "mixed", "decode256", "prefill4096"])
+def test_gdn_f32_against_f64(orc, name):
+    """Gated delta rule: fp32 oracle within the parity bound of the fp64 oracle."""
+    case = ssm_inputs.gdn_workload(name)
+    y32, s32 = orc.gdn_case(case, precision="f32")
+    y64, s64 = orc.gdn_case(case, precision="f64")
+    used = np.unique(case.slot)
+    assert np.all(np.isfinite(y32)) and np.all(np.isfinite(s32[used]))
+    assert rel_err(y32, y64) <= 1e-4
+    assert rel_err(s32[used], s64[used]) <= 1e-4
