@@ -1,9 +1,9 @@
 """Python binding of the MI355X Mamba2 selective-state scan library.
 
-Argument marshalling only: every step of the scan, and of the conv1d + SiLU
-and gated RMSNorm beside it, runs in the HIP kernels of ``libssmscan.so``
+Argument marshalling only: every step of the scan, of the conv1d + SiLU
+and gated RMSNorm beside it, and of the gated delta-rule recurrence runs in the HIP kernels of ``libssmscan.so``
 (built from ``csrc/`` by ``build.py``), reached through its C ABI
-(``include/ssm_scan.h``, ``include/ssm_conv_norm.h``).  torch supplies device memory and the current
+(``include/ssm_scan.h``, ``include/ssm_conv_norm.h``, ``include/ssm_gdn.h``).  torch supplies device memory and the current
 stream; tensors are passed as raw device pointers.  There is no CPU fallback:
 if the library is missing, importing this package raises.
 """
@@ -16,7 +16,8 @@ import re
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libssmscan.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "ssm_scan.h")
-HEADERS = [HEADER, os.path.join(os.path.dirname(PKG), "include", "ssm_conv_norm.h")]
+HEADERS = [HEADER] + [os.path.join(os.path.dirname(PKG), "include", h)
+                      for h in ("ssm_conv_norm.h", "ssm_gdn.h")]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -127,6 +128,20 @@ _lib.ssm_conv1d_silu_decode.argtypes = ([ctypes.POINTER(ConvDims), _i32] + [_vp]
 _lib.ssm_conv1d_silu_decode.restype = ctypes.c_int
 _lib.ssm_gated_rmsnorm.argtypes = [ctypes.c_int64, _i32, _vp, _vp, _vp, ctypes.c_float, _vp, _vp]
 _lib.ssm_gated_rmsnorm.restype = ctypes.c_int
+
+
+class GdnDims(ctypes.Structure):
+    _fields_ = [("n_v_heads", ctypes.c_int32), ("n_k_heads", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32)]
+
+
+MAX_GDN_DK = 256
+_lib.ssm_gdn_prefill.argtypes = ([ctypes.POINTER(GdnDims), _i32, _i32] + [_vp] * 8
+                                 + [ctypes.c_float, _vp, _i32, _vp, _vp, _vp])
+_lib.ssm_gdn_prefill.restype = ctypes.c_int
+_lib.ssm_gdn_decode.argtypes = ([ctypes.POINTER(GdnDims), _i32] + [_vp] * 7
+                                + [ctypes.c_float, _vp, _i32, _vp, _vp, _vp])
+_lib.ssm_gdn_decode.restype = ctypes.c_int
 
 
 class ScanError(RuntimeError):
@@ -450,6 +465,78 @@ def gated_rmsnorm(y, z, weight, eps, out=None, stream=None):
                                 _stream_handle(stream, dev))
     _check(rc, "ssm_gated_rmsnorm")
     return out
+
+
+# ------------------------------------------------------------ gated delta rule
+def _gdn_args(q, k, v, g, beta, state, y, snapshots, T):
+    import torch
+    n_slots, Hv, Dv, Dk = (int(d) for d in state.shape)
+    Hk = int(k.shape[1])
+    if tuple(q.shape) != (T, Hk, Dk) or tuple(k.shape) != (T, Hk, Dk):
+        raise ValueError("q and k must have shape [T, Hk, Dk]")
+    if tuple(v.shape) != (T, Hv, Dv) or tuple(g.shape) != (T, Hv) or tuple(beta.shape) != (T, Hv):
+        raise ValueError("v, g or beta has the wrong shape")
+    if snapshots is not None and tuple(snapshots.shape) != (T, Hv, Dv, Dk):
+        raise ValueError("snapshots must have shape [T, Hv, Dv, Dk]")
+    dev = state.device
+    if y is None:
+        y = torch.empty((T, Hv, Dv), dtype=torch.float32, device=dev)
+    elif tuple(y.shape) != (T, Hv, Dv):
+        raise ValueError("y has the wrong shape")
+    f32 = torch.float32
+    ptrs = [_dev_ptr(t, f32, n, dev) for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"),
+                                                   (beta, "beta"))]
+    return GdnDims(Hv, Hk, Dk, Dv), n_slots, dev, y, ptrs
+
+
+def gdn_prefill(q, k, v, g, beta, state, cu_seqlens, slot, fresh, scale=None, y=None,
+                snapshots=None, stream=None):
+    """Gated delta-rule recurrence over a packed batch (``ssm_gdn_prefill``).
+
+    q, k [T, Hk, Dk]; v [T, Hv, Dv]; g (log decay) and beta [T, Hv]; state
+    [n_slots, Hv, Dv, Dk] fp32, updated in place; cu_seqlens [n_seqs+1] and
+    slot [n_seqs] int32, fresh [n_seqs] uint8; ``scale`` defaults to
+    1/sqrt(Dk); ``snapshots`` [T, Hv, Dv, Dk] receives the state after every
+    token.  Returns y [T, Hv, Dv]."""
+    import math
+    import torch
+    T = int(v.shape[0])
+    n_seqs = int(slot.shape[0])
+    dims, n_slots, dev, y, ptrs = _gdn_args(q, k, v, g, beta, state, y, snapshots, T)
+    if tuple(cu_seqlens.shape) != (n_seqs + 1,) or tuple(fresh.shape) != (n_seqs,):
+        raise ValueError("cu_seqlens or fresh has the wrong shape")
+    sc = 1.0 / math.sqrt(dims.d_k) if scale is None else float(scale)
+    rc = _lib.ssm_gdn_prefill(ctypes.byref(dims), n_seqs, T,
+                              _dev_ptr(cu_seqlens, torch.int32, "cu_seqlens", dev),
+                              _dev_ptr(slot, torch.int32, "slot", dev),
+                              _dev_ptr(fresh, torch.uint8, "fresh", dev), *ptrs, sc,
+                              _dev_ptr(state, torch.float32, "state", dev), n_slots,
+                              _dev_ptr(y, torch.float32, "y", dev),
+                              _dev_ptr(snapshots, torch.float32, "snapshots", dev),
+                              _stream_handle(stream, dev))
+    _check(rc, "ssm_gdn_prefill")
+    return y
+
+
+def gdn_decode(q, k, v, g, beta, state, slot, fresh, scale=None, y=None, snapshots=None,
+               stream=None):
+    """One token per sequence (``ssm_gdn_decode``): the token arrays are
+    indexed by sequence; the rest as for ``gdn_prefill``."""
+    import math
+    import torch
+    S = int(slot.shape[0])
+    dims, n_slots, dev, y, ptrs = _gdn_args(q, k, v, g, beta, state, y, snapshots, S)
+    if tuple(fresh.shape) != (S,):
+        raise ValueError("fresh has the wrong shape")
+    sc = 1.0 / math.sqrt(dims.d_k) if scale is None else float(scale)
+    rc = _lib.ssm_gdn_decode(ctypes.byref(dims), S, _dev_ptr(slot, torch.int32, "slot", dev),
+                             _dev_ptr(fresh, torch.uint8, "fresh", dev), *ptrs, sc,
+                             _dev_ptr(state, torch.float32, "state", dev), n_slots,
+                             _dev_ptr(y, torch.float32, "y", dev),
+                             _dev_ptr(snapshots, torch.float32, "snapshots", dev),
+                             _stream_handle(stream, dev))
+    _check(rc, "ssm_gdn_decode")
+    return y
 
 
 def to_device(case, device="cuda:0"):

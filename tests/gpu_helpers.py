@@ -164,3 +164,28 @@ def run_norm_gpu(case, device="cuda:0", offset_floats=0, eps=None):
     ssm.gated_rmsnorm(y, z, w, case.eps if eps is None else eps, out=out)
     torch.cuda.synchronize()
     return out.cpu().numpy()
+
+
+def run_gdn_gpu(case, mode="prefill", device="cuda:0", offset_floats=0, snapshots=False):
+    """Run an ``ssm_inputs.GdnCase`` through the delta-rule ABI; returns (y,
+    state) or (y, state, snapshots) as numpy."""
+    import torch
+    import mamba2_selective_scan_amd as ssm
+    put = lambda a: _put(a, device, offset_floats)
+    q, k, v, g, beta = (put(getattr(case, f)) for f in ("q", "k", "v", "g", "beta"))
+    st = put(case.state)
+    slot, fresh = put(case.slot), put(case.fresh)
+    y = put(np.full((case.n_tokens, case.Hv, case.Dv), np.nan, np.float32))
+    sn = (put(np.full((case.n_tokens, case.Hv, case.Dv, case.Dk), np.nan, np.float32))
+          if snapshots else None)
+    if mode == "prefill":
+        ssm.gdn_prefill(q, k, v, g, beta, st, put(case.cu_seqlens), slot, fresh, scale=case.scale,
+                        y=y, snapshots=sn)
+    elif mode == "decode":
+        assert np.all(case.lengths == 1)
+        ssm.gdn_decode(q, k, v, g, beta, st, slot, fresh, scale=case.scale, y=y, snapshots=sn)
+    else:
+        raise ValueError(mode)
+    torch.cuda.synchronize()
+    res = (y.cpu().numpy(), st.cpu().numpy())
+    return res + (sn.cpu().numpy(),) if snapshots else res

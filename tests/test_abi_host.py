@@ -1,5 +1,5 @@
 """The C-ABI library on the host (no GPU): it loads, exports every function
-include/ssm_scan.h and include/ssm_conv_norm.h declare, rejects bad arguments with the documented codes
+include/ssm_scan.h, include/ssm_conv_norm.h and include/ssm_gdn.h declare, rejects bad arguments with the documented codes
 before touching any device, and reports launch geometry; every compiled
 kernel keeps its state in registers (no scratch)."""
 import ctypes
@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol():
                           "ssm_scan_prefill_workspace_size", "ssm_scan_query_prefill_plan",
                           "ssm_scan_prefill_opt", "ssm_scan_decode_opt",
                           "ssm_conv1d_silu_prefill", "ssm_conv1d_silu_decode",
-                          "ssm_gated_rmsnorm"}
+                          "ssm_gated_rmsnorm", "ssm_gdn_prefill", "ssm_gdn_decode"}
     for n in names:
         assert hasattr(m.lib(), n), n
 
@@ -124,7 +124,10 @@ def test_no_kernel_uses_scratch():
     n_scan = 7 * 2 * (4 * 2 + 2) + 2 + 3
     n_conv = 2 * (4 * 2 + 3)
     n_norm = 2 * 6
-    assert len(names) == n_scan + n_conv + n_norm and len(scratch) == len(names)
+    # gated delta rule: 5 key-width classes x (vector, scalar) x (prefill, decode)
+    # x (snapshots or not)
+    n_gdn = 5 * 2 * 2 * 2
+    assert len(names) == n_scan + n_conv + n_norm + n_gdn and len(scratch) == len(names)
     assert all(v == 0 for v in scratch), dict(zip(names, scratch))
 
 
@@ -214,3 +217,43 @@ def test_norm_argument_errors():
         assert f(4, 8, ptrs[0], ptrs[1], ptrs[2], 1e-5, ptrs[3], None) == m.SSM_ERR_NULL
         ptrs[i] = FAKE + 2
         assert f(4, 8, ptrs[0], ptrs[1], ptrs[2], 1e-5, ptrs[3], None) == m.SSM_ERR_ALIGN
+
+
+# ------------------------------------------------------------ gated delta rule
+GD = m.GdnDims
+
+
+def _gdn(dims, n_seqs=1, n_tokens=4, ptrs=None, n_slots=1, fake=FAKE, decode=False):
+    p = dict(cu=fake, slot=fake, fresh=fake, q=fake, k=fake, v=fake, g=fake, beta=fake,
+             state=fake, y=fake, snaps=None)
+    p.update(ptrs or {})
+    d = None if dims is None else ctypes.byref(dims)
+    if decode:
+        return m.lib().ssm_gdn_decode(d, n_seqs, p["slot"], p["fresh"], p["q"], p["k"], p["v"],
+                                      p["g"], p["beta"], 0.125, p["state"], n_slots, p["y"],
+                                      p["snaps"], None)
+    return m.lib().ssm_gdn_prefill(d, n_seqs, n_tokens, p["cu"], p["slot"], p["fresh"], p["q"],
+                                   p["k"], p["v"], p["g"], p["beta"], 0.125, p["state"], n_slots,
+                                   p["y"], p["snaps"], None)
+
+
+@pytest.mark.parametrize("decode", [False, True])
+def test_gdn_argument_errors(decode):
+    ok = GD(32, 16, 128, 128)
+    call = lambda *a, **k: _gdn(*a, decode=decode, **k)
+    assert call(None) == m.SSM_ERR_NULL
+    for bad in (GD(0, 1, 8, 8), GD(4, 0, 8, 8), GD(4, 2, 0, 8), GD(4, 2, 8, 0), GD(6, 4, 8, 8)):
+        assert call(bad) == m.SSM_ERR_DIMS
+    assert call(GD(4, 2, 257, 8)) == m.SSM_ERR_UNSUPPORTED
+    assert call(ok, n_seqs=-1) == m.SSM_ERR_DIMS
+    assert call(ok, n_seqs=0) == m.SSM_OK
+    assert call(ok, n_slots=0) == m.SSM_ERR_DIMS
+    for name in ("slot", "fresh", "state", "q", "k", "v", "g", "beta", "y"):
+        assert call(ok, ptrs={name: None}) == m.SSM_ERR_NULL, name
+    for name in ("q", "k", "v", "g", "beta", "state", "y"):
+        assert call(ok, ptrs={name: FAKE + 2}) == m.SSM_ERR_ALIGN, name
+    assert call(ok, ptrs={"snaps": FAKE + 2}) == m.SSM_ERR_ALIGN
+    assert call(ok, ptrs={"slot": FAKE + 1}) == m.SSM_ERR_ALIGN
+    if not decode:
+        assert call(ok, n_tokens=-1) == m.SSM_ERR_DIMS
+        assert call(ok, ptrs={"cu": None}) == m.SSM_ERR_NULL
