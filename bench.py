@@ -364,6 +364,53 @@ def beside(args, dev, stream):
     return out
 
 
+def gated_delta(args, dev, stream):
+    """The gated delta-rule recurrence at the page's model geometry (Hv 32,
+    Hk 16, Dk = Dv = 128): prefill 1 x 4096 (VALU-bound; algorithmic work 7
+    flop per state value per token: decay, the two dots, the write) and decode
+    16 x 1 / 256 x 1 (HBM-bound; the state read and written once).  Decode 16
+    rotates 16 slot sets through a replayed HIP graph, as the scan's."""
+    import torch
+
+    import mamba2_selective_scan_amd as ssm
+    import ssm_inputs
+    out = {}
+    Hv, Hk, D = 32, 16, 128
+    c = ssm_inputs.gdn_workload("prefill4096")
+    t = {f: torch.from_numpy(getattr(c, f)).to(dev)
+         for f in ("q", "k", "v", "g", "beta", "state", "cu_seqlens", "slot", "fresh")}
+    y = torch.empty((c.n_tokens, Hv, D), device=dev)
+    ms = _event_ms(lambda: ssm.gdn_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["state"],
+                                           t["cu_seqlens"], t["slot"], t["fresh"], y=y), 10, 3, stream)
+    flops = 7 * PREFILL_T * Hv * D * D
+    tf = flops / (ms * 1e-3) / 1e12
+    out["gdn_prefill_1x4096_Hv32_Hk16_D128"] = {
+        "ms": round(ms, 4), "TFLOPs": round(tf, 2), "frac_fp32": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
+        "frac_unpacked_fp32": round(tf / FP32_VALU_UNPACKED_TFLOPS, 4), "algorithmic_flops": flops}
+    del t, y
+
+    def dec_bytes(n):
+        return 4 * (2 * n * Hv * D * D + n * (2 * Hk * D + 2 * Hv * D + 2 * Hv))
+
+    for n_seq, sets in ((16, 16), (256, 1)):
+        c = ssm_inputs.make_gdn_case(Hv, Hk, D, D, [1] * n_seq, [0] * n_seq, 31,
+                                     n_slots=n_seq * sets)
+        t = {f: torch.from_numpy(getattr(c, f)).to(dev)
+             for f in ("q", "k", "v", "g", "beta", "state", "fresh")}
+        slots = [torch.arange(k * n_seq, (k + 1) * n_seq, dtype=torch.int32, device=dev)
+                 for k in range(sets)]
+        y = torch.empty((n_seq, Hv, D), device=dev)
+        calls = [(lambda k=k: ssm.gdn_decode(t["q"], t["k"], t["v"], t["g"], t["beta"], t["state"],
+                                             slots[k], t["fresh"], y=y)) for k in range(sets)]
+        us = _graph_us(calls, max(2, 320 // sets), stream)
+        gbs = dec_bytes(n_seq) / (us * 1e-6) / 1e9
+        out[f"gdn_decode_{n_seq}x1_Hv32_Hk16_D128"] = {
+            "us": round(us, 2), "GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": dec_bytes(n_seq), "slot_sets_rotated": sets}
+        del t, y, slots, calls
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -529,6 +576,7 @@ def main():
     if not args.no_secondary:
         result["secondary"] = secondary(args, dev, stream)
         result["beside_the_scan"] = beside(args, dev, stream)
+        result["gated_delta_rule"] = gated_delta(args, dev, stream)
 
     if not args.no_cpu_baseline:
         one_set = ssm_inputs.workload("decode16")

@@ -43,6 +43,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ssm {
 
 using f4 = float __attribute__((ext_vector_type(4)));
@@ -112,13 +114,14 @@ struct Shape {
     static constexpr int OFF_Y = OFF_X + CT * RB;
     static constexpr int OFF_DT = OFF_Y + CT * RB;
     static constexpr int OFF_DA = OFF_DT + CT;
-    static constexpr int BUF = ((OFF_DA + CT) + 3) / 4 * 4;
+    static constexpr int OFF_LAZY = OFF_DA + CT;    // 1: the chunk runs with the decay deferred
+    static constexpr int BUF = ((OFF_LAZY + 1) + 3) / 4 * 4;
     static constexpr int TILE = RB * NPT;           // state tile (scalar path), floats
     // register prefetch units per thread
     static constexpr int U_BC = (CT * NP / 4 + kThreads - 1) / kThreads;    // float4 of B (and of C)
     static constexpr int U_X = (CT * RB / 4 + kThreads - 1) / kThreads;     // float4 of x
     static_assert(R == 4 || R == 8 || R == 16 || R == 32 || R == 64, "R must be a power of two in [4, 64]");
-    static_assert(CT <= kThreads, "one thread stages each token's dt");
+    static_assert(CT <= 64, "one lane of wave 0 stages each token's dt");
     static_assert(RB % 4 == 0, "rows per block must be a multiple of 4");
 
     static constexpr int lds_floats(Mode mode, bool vec) {
@@ -165,6 +168,39 @@ __device__ __forceinline__ float row_prefix_product(float v) {
     v *= dpp_or_one<0x118>(v);     // row_shr:8
     return v;
 }
+
+// Inclusive running product over lanes 0..CT-1 of the wavefront (CT <= 64,
+// all 64 lanes active): a DPP product inside each 16-lane row, then each row
+// times the totals of the rows before it.
+template <int CT>
+__device__ __forceinline__ float chunk_prefix_product(float v) {
+    static_assert(CT <= 64, "one wavefront");
+    v = row_prefix_product(v);
+    if constexpr (CT > 16) {
+        const int lane = threadIdx.x & 63;
+        const float t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+        float m = lane >= 16 ? t0 : 1.f;
+        if constexpr (CT > 32) {
+            const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+            m = lane >= 32 ? m * t1 : m;
+            if constexpr (CT > 48) {
+                const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+                m = lane >= 48 ? m * t2 : m;
+            }
+        }
+        v *= m;
+    }
+    return v;
+}
+
+// Deferred decay.  Within a chunk the row is kept as h / sigma_t, with
+// sigma_t the product of dA from the chunk start through token t; then
+//     h / sigma_t = h / sigma_{t-1} + b * (x * dt / sigma_t)
+// is one fused multiply-add per element instead of a multiply and an FMA, y is
+// sigma_t times the row's dot with C, and the chunk ends by multiplying the
+// row by its sigma.  A chunk whose sigma would fall below this floor (so that
+// 1/sigma could overflow the stored row) runs the direct update instead.
+constexpr float kLazyFloor = 0x1p-40f;
 
 // Load 4 consecutive floats, the ones at index >= n_valid read as 0.
 template <bool VEC>
@@ -233,6 +269,27 @@ __device__ __forceinline__ float update_token_pe(float (&h)[4 * J], const f4 (&b
     return acc0 + acc1;
 }
 
+// One token with the decay deferred: h <- h + b * xs (xs = x*dt/sigma);
+// returns the lane's partial dot of the stored row with C.
+template <int J>
+__device__ __forceinline__ float update_token_lazy(float (&h)[4 * J], const f4 (&b)[J],
+                                                   const f4 (&c)[J], float xs) {
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        float *hj = h + 4 * j;
+        hj[0] = __builtin_fmaf(b[j].x, xs, hj[0]);
+        hj[1] = __builtin_fmaf(b[j].y, xs, hj[1]);
+        hj[2] = __builtin_fmaf(b[j].z, xs, hj[2]);
+        hj[3] = __builtin_fmaf(b[j].w, xs, hj[3]);
+        acc0 = __builtin_fmaf(hj[0], c[j].x, acc0);
+        acc1 = __builtin_fmaf(hj[1], c[j].y, acc1);
+        acc0 = __builtin_fmaf(hj[2], c[j].z, acc0);
+        acc1 = __builtin_fmaf(hj[3], c[j].w, acc1);
+    }
+    return acc0 + acc1;
+}
+
 // The lane's J 4-groups of one token's B (or C) row in LDS; p points at the
 // lane's first group, groups are 4*R floats apart.
 template <int R, int J>
@@ -276,6 +333,8 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     constexpr bool SEGMENTED = MODE == Mode::kSegScan || CORRECT;   // grid has a segment axis
     constexpr bool A_PER_STATE = (OPT & OPT_A_PER_STATE) != 0;
     constexpr bool SNAPSHOTS = (OPT & OPT_SNAPSHOTS) != 0;
+    // the deferred-decay update (see kLazyFloor) for plain prefill and segment scans
+    constexpr bool LAZY = (MODE == Mode::kPrefill || MODE == Mode::kSegScan) && OPT == 0;
     static_assert(OPT == 0 || MODE == Mode::kPrefill || MODE == Mode::kDecode,
                   "options are built for whole-sequence prefill and decode only");
 
@@ -481,20 +540,35 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                 const int q = u * kThreads + tid;
                 if (q < CT * RB / 4) Xs4[q] = px[u];
             }
-            if constexpr (SEGMENTED) {
-                static_assert(!SEGMENTED || CT <= 16, "segment chunks fit one DPP row");
+            if constexpr (SEGMENTED || LAZY) {
                 if (tid < 64) {                              // wave 0, all lanes active
                     const float dA = (tid < nt) ? expf(pdt * A_h) : 1.f;
-                    const float cum = run * row_prefix_product(dA);
-                    run = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), 15));
-                    if (tid < CT) {
-                        base[S::OFF_DT + tid] = CORRECT ? cum : pdt;
-                        base[S::OFF_DA + tid] = dA;
+                    const float loc = chunk_prefix_product<CT>(dA);     // from the chunk start
+                    const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(loc), CT - 1));
+                    if constexpr (SEGMENTED) {
+                        const float cum = run * loc;                     // from the segment start
+                        if constexpr (CORRECT) {
+                            if (tid < CT) {
+                                base[S::OFF_DT + tid] = cum;
+                                base[S::OFF_DA + tid] = dA;
+                            }
+                        }
+                        // a split sequence's segment scan also leaves the running
+                        // product for the matrix-core correction (one row block per head)
+                        if (MODE == Mode::kSegScan && split && rb == 0 && tid < nt)
+                            a.ws_dcum[int64_t(t0 + tid) * H + hd] = cum;
+                        run *= total;
                     }
-                    // a split sequence's segment scan also leaves the running
-                    // product for the matrix-core correction (one row block per head)
-                    if (MODE == Mode::kSegScan && split && rb == 0 && tid < nt)
-                        a.ws_dcum[int64_t(t0 + tid) * H + hd] = cum;
+                    if constexpr (LAZY) {
+                        // one-token chunks keep the direct update, so a lone token
+                        // gives the same bits as decode
+                        const bool lazy = nt > 1 && total >= kLazyFloor;
+                        if (tid < CT) {
+                            base[S::OFF_DT + tid] = lazy ? pdt / loc : pdt;
+                            base[S::OFF_DA + tid] = lazy ? loc : dA;
+                        }
+                        if (tid == 0) base[S::OFF_LAZY] = lazy ? 1.f : 0.f;
+                    }
                 }
             } else {
                 if (tid < CT) {
@@ -512,10 +586,15 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         constexpr int KY = R < 16 ? R : 16;
         const int rk = r % KY;
         int chunk_t0 = 0;                                   // first token of the chunk in compute
-        auto token_y = [&](const float *base, int tt) -> float {
+        auto token_y = [&](const float *base, int tt, auto lazy_tag) -> float {
             f4 cv[J];
             lds_groups<R, J>(cv, base + S::OFF_C + 4 * r + tt * NP);
-            if constexpr (CORRECT) {
+            if constexpr (decltype(lazy_tag)::value) {
+                f4 bv[J];
+                lds_groups<R, J>(bv, base + S::OFF_B + 4 * r + tt * NP);
+                const float xs = base[S::OFF_X + tt * RB + i] * base[S::OFF_DT + tt];
+                return base[S::OFF_DA + tt] * row_allreduce<R>(update_token_lazy<J>(h, bv, cv, xs));
+            } else if constexpr (CORRECT) {
                 // y += dcum[t] * (C_t . carry): the carry decayed to token t
                 float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
@@ -545,25 +624,43 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                 return row_allreduce<R>(part);
             }
         };
-        auto compute = [&](int buf, int nt) {
-            const float *base = lds + buf * S::BUF;
-            float *Ys = lds + buf * S::BUF + S::OFF_Y + i;
+        auto run_tokens = [&](const float *base, float *Ys, int nt, auto lazy_tag) {
             float y_keep = 0.f;
             int t0 = 0;
             for (; t0 + KY <= nt; t0 += KY) {
 #pragma unroll
                 for (int kk = 0; kk < KY; ++kk) {
-                    const float yv = token_y(base, t0 + kk);
+                    const float yv = token_y(base, t0 + kk, lazy_tag);
                     y_keep = (rk == kk) ? yv : y_keep;
                 }
                 Ys[(t0 + rk) * RB] = y_keep;
             }
             if (t0 < nt) {
                 for (int tt = t0; tt < nt; ++tt) {
-                    const float yv = token_y(base, tt);
+                    const float yv = token_y(base, tt, lazy_tag);
                     y_keep = (rk == tt - t0) ? yv : y_keep;
                 }
                 if (rk < nt - t0) Ys[(t0 + rk) * RB] = y_keep;
+            }
+        };
+        auto compute = [&](int buf, int nt) {
+            const float *base = lds + buf * S::BUF;
+            float *Ys = lds + buf * S::BUF + S::OFF_Y + i;
+            if constexpr (LAZY) {
+                if (base[S::OFF_LAZY] != 0.f) {                 // chunk-uniform
+                    run_tokens(base, Ys, nt, std::true_type{});
+                    const float sigma = base[S::OFF_DA + nt - 1];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) h[e] *= sigma;
+                    return;
+                }
+                // the rare direct chunk: a plain loop, the row's first lane stores y
+                for (int tt = 0; tt < nt; ++tt) {
+                    const float yv = token_y(base, tt, std::false_type{});
+                    if (r == 0) Ys[tt * RB] = yv;
+                }
+            } else {
+                run_tokens(base, Ys, nt, std::false_type{});
             }
         };
 

@@ -172,8 +172,12 @@ def test_split_resume(ssm, orc):
         y2, st2 = run_gpu(b, "prefill")
         y_split = np.concatenate([y1, y2])
         assert rel_err(y_split, y_all) <= TOL and rel_err(st2, st_all) <= TOL
-        # the per-token arithmetic does not depend on the chunk position
-        assert np.array_equal(y_split, y_all) and np.array_equal(st2, st_all), T1
+        # Within a chunk the decay is deferred (the row is kept divided by the
+        # running product of dA and rescaled at the chunk end), so the rounding
+        # depends on where chunks start; a cut on a chunk boundary keeps every
+        # chunk the same and must give the same bits.
+        if T1 % CT == 0:
+            assert np.array_equal(y_split, y_all) and np.array_equal(st2, st_all), T1
 
 
 def test_empty_and_degenerate(ssm):
