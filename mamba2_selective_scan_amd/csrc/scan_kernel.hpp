@@ -154,6 +154,42 @@ __device__ __forceinline__ float row_allreduce(float v) {
     return v;
 }
 
+// Reduce-scatter of KY per-token partials over KY adjacent lanes (KY = 4, 8
+// or 16, inside one DPP row): lane l ends with the sum over the KY lanes of
+// partial l % KY.  Each stage pairs every lane with one whose index differs in
+// the stage's bit (row_mirror, row_half_mirror, quad xor 2, quad xor 1): the
+// lane keeps the half of its values whose index has the lane's bit and adds
+// the partner's copy of that half.  KY sums cost (KY/2 + KY/4 + ... + 1) DPP
+// adds and twice as many selects, against KY full butterflies of log2(KY)
+// dependent steps.
+template <int CTRL, int BIT, int NV>
+__device__ __forceinline__ void scatter_stage(const float (&in)[NV], float (&out)[NV / 2]) {
+    const bool up = (threadIdx.x & BIT) != 0;
+#pragma unroll
+    for (int j = 0; j < NV / 2; ++j) {
+        const float keep = up ? in[j + NV / 2] : in[j];
+        const float send = up ? in[j] : in[j + NV / 2];
+        out[j] = keep + dpp<CTRL>(send);
+    }
+}
+template <int KY>
+__device__ __forceinline__ float row_reduce_scatter(const float (&p)[KY]) {
+    static_assert(KY == 4 || KY == 8 || KY == 16, "KY lanes inside one DPP row");
+    float q8[8], q4[4], q2[2], q1[1];
+    if constexpr (KY == 16) {
+        scatter_stage<kMirror, 8, 16>(p, q8);
+        scatter_stage<kHalfMirror, 4, 8>(q8, q4);
+    } else if constexpr (KY == 8) {
+        scatter_stage<kHalfMirror, 4, 8>(p, q4);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q4[j] = p[j];
+    }
+    scatter_stage<kQuadXor2, 2, 4>(q4, q2);
+    scatter_stage<kQuadXor1, 1, 2>(q2, q1);
+    return q1[0];
+}
+
 // Inclusive running product over the 16 lanes of each DPP row (lanes past a
 // row's start multiply by 1).  Used on one token's dA per lane.
 template <int CTRL>
@@ -586,29 +622,16 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         constexpr int KY = R < 16 ? R : 16;
         const int rk = r % KY;
         int chunk_t0 = 0;                                   // first token of the chunk in compute
-        auto token_y = [&](const float *base, int tt, auto lazy_tag) -> float {
-            f4 cv[J];
+        // The lane's partial of token tt's y (prefill / segment scan): the row
+        // sum of these, times y_scale(tt), is y.
+        auto token_part = [&](const float *base, int tt, auto lazy_tag) -> float {
+            f4 cv[J], bv[J];
             lds_groups<R, J>(cv, base + S::OFF_C + 4 * r + tt * NP);
+            lds_groups<R, J>(bv, base + S::OFF_B + 4 * r + tt * NP);
             if constexpr (decltype(lazy_tag)::value) {
-                f4 bv[J];
-                lds_groups<R, J>(bv, base + S::OFF_B + 4 * r + tt * NP);
                 const float xs = base[S::OFF_X + tt * RB + i] * base[S::OFF_DT + tt];
-                return base[S::OFF_DA + tt] * row_allreduce<R>(update_token_lazy<J>(h, bv, cv, xs));
-            } else if constexpr (CORRECT) {
-                // y += dcum[t] * (C_t . carry): the carry decayed to token t
-                float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-                for (int j = 0; j < J; ++j) {
-                    acc0 += h[4 * j + 0] * cv[j].x;
-                    acc1 += h[4 * j + 1] * cv[j].y;
-                    acc0 += h[4 * j + 2] * cv[j].z;
-                    acc1 += h[4 * j + 3] * cv[j].w;
-                }
-                const float yc = row_allreduce<R>(acc0 + acc1);
-                return base[S::OFF_X + tt * RB + i] + base[S::OFF_DT + tt] * yc;
+                return update_token_lazy<J>(h, bv, cv, xs);
             } else {
-                f4 bv[J];
-                lds_groups<R, J>(bv, base + S::OFF_B + 4 * r + tt * NP);
                 const float dt = base[S::OFF_DT + tt];
                 const float x_dt = base[S::OFF_X + tt * RB + i] * dt;
                 float part;
@@ -621,19 +644,58 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                     part = update_token<J>(h, bv, cv, base[S::OFF_DA + tt], x_dt);
                 }
                 if constexpr (SNAPSHOTS) snapshot(chunk_t0 + tt);
-                return row_allreduce<R>(part);
+                return part;
+            }
+        };
+        auto y_scale = [&](const float *base, int tt, auto lazy_tag) -> float {
+            if constexpr (decltype(lazy_tag)::value) return base[S::OFF_DA + tt];
+            else return 1.f;
+        };
+        auto token_y = [&](const float *base, int tt, auto lazy_tag) -> float {
+            if constexpr (CORRECT) {
+                // y += dcum[t] * (C_t . carry): the carry decayed to token t
+                f4 cv[J];
+                lds_groups<R, J>(cv, base + S::OFF_C + 4 * r + tt * NP);
+                float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    acc0 += h[4 * j + 0] * cv[j].x;
+                    acc1 += h[4 * j + 1] * cv[j].y;
+                    acc0 += h[4 * j + 2] * cv[j].z;
+                    acc1 += h[4 * j + 3] * cv[j].w;
+                }
+                const float yc = row_allreduce<R>(acc0 + acc1);
+                return base[S::OFF_X + tt * RB + i] + base[S::OFF_DT + tt] * yc;
+            } else {
+                return y_scale(base, tt, lazy_tag) * row_allreduce<R>(token_part(base, tt, lazy_tag));
             }
         };
         auto run_tokens = [&](const float *base, float *Ys, int nt, auto lazy_tag) {
-            float y_keep = 0.f;
             int t0 = 0;
-            for (; t0 + KY <= nt; t0 += KY) {
+            float y_keep = 0.f;
+            if constexpr (!CORRECT && !SNAPSHOTS) {
+                // KY tokens at a time: their partials reduce-scattered over the
+                // row, so lane r ends with token r % KY's y and stores it.
+                // (Snapshot kernels keep the per-token sums: holding KY partials
+                // beside the snapshot stores costs them occupancy.)
+                for (; t0 + KY <= nt; t0 += KY) {
+                    float part[KY];
 #pragma unroll
-                for (int kk = 0; kk < KY; ++kk) {
-                    const float yv = token_y(base, t0 + kk, lazy_tag);
-                    y_keep = (rk == kk) ? yv : y_keep;
+                    for (int kk = 0; kk < KY; ++kk) part[kk] = token_part(base, t0 + kk, lazy_tag);
+                    float yv = row_reduce_scatter<KY>(part);
+                    if constexpr (R >= 32) yv += __shfl_xor(yv, 16, 64);
+                    if constexpr (R >= 64) yv += __shfl_xor(yv, 32, 64);
+                    Ys[(t0 + rk) * RB] = y_scale(base, t0 + rk, lazy_tag) * yv;
                 }
-                Ys[(t0 + rk) * RB] = y_keep;
+            } else {
+                for (; t0 + KY <= nt; t0 += KY) {
+#pragma unroll
+                    for (int kk = 0; kk < KY; ++kk) {
+                        const float yv = token_y(base, t0 + kk, lazy_tag);
+                        y_keep = (rk == kk) ? yv : y_keep;
+                    }
+                    Ys[(t0 + rk) * RB] = y_keep;
+                }
             }
             if (t0 < nt) {
                 for (int tt = t0; tt < nt; ++tt) {
