@@ -24,11 +24,18 @@ namespace ssm {
 
 using f16v = float __attribute__((ext_vector_type(16)));
 
-// KH >= N/2 MFMA steps (N % 8 == 0, vector path).  Grid: n_seqs x n_segs x H x
-// n_tblocks workgroups of 4 wavefronts; workgroup b of a segment takes token
-// tiles b*4 + w, stepping by n_tblocks*4 tiles until the segment ends.
-template <int KH>
+// KH >= N/2 MFMA steps (N % 8 == 0, vector path), taken in chunks of KC = 16:
+// a chunk's C and carry operands are 4 float4 per lane, and the next chunk's
+// loads are in flight while the current chunk's 16 MFMAs run, instead of the
+// wave holding the whole contraction's operands.  Grid: n_seqs x n_segs x H x n_tblocks workgroups of 4 wavefronts;
+// workgroup b of a segment takes token tiles b*4 + w, stepping by
+// n_tblocks*4 tiles until the segment ends.
+// FULL: N/2 == KH, so no chunk reaches past the row and nothing is masked.
+template <int KH, bool FULL>
 __global__ void __launch_bounds__(kThreads) correct_mfma_kernel(ScanArgs a, int n_tblocks) {
+    constexpr int KC = 16;                              // MFMA steps per chunk
+    constexpr int NCH = KH / KC;
+    static_assert(KH % KC == 0, "whole chunks");
     int q = blockIdx.x;
     const int tb = q % n_tblocks;
     q /= n_tblocks;
@@ -50,47 +57,87 @@ __global__ void __launch_bounds__(kThreads) correct_mfma_kernel(ScanArgs a, int 
     const float *carry = a.ws_state + (int64_t(s) * a.n_segs + seg - 1) * hpn + int64_t(hd) * P * N;
     const int stride = n_tblocks * 4 * 32;
 
-    for (int t0 = sr.t_begin + (tb * 4 + w) * 32; t0 < sr.t_end; t0 += stride) {
-        const int t = t0 + li;
-        const bool tok_ok = t < sr.t_end;
-        // A operand: this lane's token row of C, n in [half*nh, half*nh + nh)
-        float av[KH];
-        {
-            const float *crow = a.C + (int64_t(t) * G + g) * N + half * nh;
+    // Chunk c of a row: floats [16c, 16c + 16) of the lane's half.  Rows are
+    // clamped to valid ones and loaded unmasked: a C row of a token past the
+    // segment only feeds output rows that are never stored, a carry row past
+    // P only output columns that are never stored.  Past nh (N/2 < KH) the
+    // carry is zeroed so the C values there add nothing; every load is still
+    // issued (no branch between loads).
+    auto load_chunk = [&](f4 (&v)[4], const float *row, bool zero_pad, int c) {
 #pragma unroll
-            for (int j = 0; j < KH / 4; ++j) {
-                const f4 v = (tok_ok && 4 * j < nh) ? *reinterpret_cast<const f4 *>(crow + 4 * j)
-                                                    : f4{0.f, 0.f, 0.f, 0.f};
-                av[4 * j + 0] = v.x; av[4 * j + 1] = v.y; av[4 * j + 2] = v.z; av[4 * j + 3] = v.w;
+        for (int j = 0; j < 4; ++j) {
+            const int k = KC * c + 4 * j;
+            if constexpr (FULL) {
+                v[j] = *reinterpret_cast<const f4 *>(row + k);
+            } else {
+                const f4 x = *reinterpret_cast<const f4 *>(row + min(k, nh - 4));
+                const bool good = !zero_pad || k < nh;
+                v[j] = f4{good ? x.x : 0.f, good ? x.y : 0.f, good ? x.z : 0.f, good ? x.w : 0.f};
             }
         }
+    };
+
+    for (int t0 = sr.t_begin + (tb * 4 + w) * 32; t0 < sr.t_end; t0 += stride) {
+        const int tc = min(t0 + li, sr.t_end - 1);                 // a token of this tile
+        // A operand: this lane's token row of C, n in [half*nh, half*nh + nh)
+        const float *crow = a.C + (int64_t(tc) * G + g) * N + half * nh;
         // dcum for the tile's tokens, left by the segment scan
-        const float dcum = tok_ok ? a.ws_dcum[int64_t(t) * H + hd] : 0.f;
+        const float dcum = a.ws_dcum[int64_t(tc) * H + hd];
 
         for (int p0 = 0; p0 < P; p0 += 32) {
             const int p = p0 + li;
             const bool row_ok = p < P;
-            float bv[KH];
-            {
-                const float *krow = carry + int64_t(p) * N + half * nh;
-#pragma unroll
-                for (int j = 0; j < KH / 4; ++j) {
-                    const f4 v = (row_ok && 4 * j < nh) ? *reinterpret_cast<const f4 *>(krow + 4 * j)
-                                                        : f4{0.f, 0.f, 0.f, 0.f};
-                    bv[4 * j + 0] = v.x; bv[4 * j + 1] = v.y; bv[4 * j + 2] = v.z; bv[4 * j + 3] = v.w;
-                }
-            }
-            f16v acc = {};
-#pragma unroll
-            for (int k = 0; k < KH; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[k], bv[k], acc, 0, 0, 0);
+            const int pc = min(p, P - 1);                    // a row of this tile
+            const float *krow = carry + int64_t(pc) * N + half * nh;
+            // operands in two ping-pong buffers: the loads of chunk c+1 are
+            // issued before chunk c's MFMAs (the scheduling barriers keep the
+            // compiler from sinking them below the MFMAs, which would leave
+            // every chunk waiting on its own loads)
+            f4 a0[4], b0[4], a1[4], b1[4];
+            load_chunk(a0, crow, false, 0);
+            load_chunk(b0, krow, true, 0);
+            // the tile's y, read after chunk 0's operands (the memory counter
+            // is in order) and before the contraction, which hides them
+            // (addresses clamped into this wave's own tile)
+            float yv[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int i = 8 * (v / 4) + 4 * half + (v % 4);     // token within the tile
-                const float dc = __shfl(dcum, i, 64);
-                if (row_ok && t0 + i < sr.t_end) {
-                    float *yp = a.y + (int64_t(t0 + i) * H + hd) * P + p;
-                    *yp += dc * acc[v];
+                yv[v] = a.y[(int64_t(min(t0 + i, sr.t_end - 1)) * H + hd) * P + pc];
+            }
+            f16v acc = {};
+            auto mfma16 = [&](const f4 (&x)[4], const f4 (&y)[4]) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x[j].x, y[j].x, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x[j].y, y[j].y, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x[j].z, y[j].z, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x[j].w, y[j].w, acc, 0, 0, 0);
                 }
+            };
+#pragma unroll
+            for (int c = 0; c < NCH; c += 2) {
+                if (c + 1 < NCH) {
+                    load_chunk(a1, crow, false, c + 1);
+                    load_chunk(b1, krow, true, c + 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                mfma16(a0, b0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (c + 2 < NCH) {
+                    load_chunk(a0, crow, false, c + 2);
+                    load_chunk(b0, krow, true, c + 2);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (c + 1 < NCH) mfma16(a1, b1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int i = 8 * (v / 4) + 4 * half + (v % 4);
+                const float dc = __shfl(dcum, i, 64);
+                if (row_ok && t0 + i < sr.t_end)
+                    a.y[(int64_t(t0 + i) * H + hd) * P + p] = __builtin_fmaf(dc, acc[v], yv[v]);
             }
         }
     }

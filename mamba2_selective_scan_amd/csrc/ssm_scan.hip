@@ -324,9 +324,13 @@ int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_
         const int64_t grid = int64_t(n_seqs) * plan.n_segs * d->n_heads * n_tblocks;
         if (grid > INT32_MAX) return SSM_ERR_UNSUPPORTED;
         const int nh = d->d_state / 2;
-        const void *kern = nh <= 16 ? reinterpret_cast<const void *>(&ssm::correct_mfma_kernel<16>)
-                         : nh <= 32 ? reinterpret_cast<const void *>(&ssm::correct_mfma_kernel<32>)
-                                    : reinterpret_cast<const void *>(&ssm::correct_mfma_kernel<64>);
+        const void *kern =
+            nh == 16 ? reinterpret_cast<const void *>(&ssm::correct_mfma_kernel<16, true>)
+          : nh < 16  ? reinterpret_cast<const void *>(&ssm::correct_mfma_kernel<16, false>)
+          : nh == 32 ? reinterpret_cast<const void *>(&ssm::correct_mfma_kernel<32, true>)
+          : nh < 32  ? reinterpret_cast<const void *>(&ssm::correct_mfma_kernel<32, false>)
+          : nh == 64 ? reinterpret_cast<const void *>(&ssm::correct_mfma_kernel<64, true>)
+                     : reinterpret_cast<const void *>(&ssm::correct_mfma_kernel<64, false>);
         ScanArgs args = a;
         int tblocks = n_tblocks;
         void *params[] = {&args, &tblocks};
