@@ -60,6 +60,8 @@ def kernel_source_hash():
     import re
     h = hashlib.sha256()
     for rel in ("mamba2_selective_scan_amd/csrc/scan_kernel.hpp",
+                "mamba2_selective_scan_amd/csrc/correct_mfma.hpp",
+                "mamba2_selective_scan_amd/csrc/status.hpp",
                 "mamba2_selective_scan_amd/csrc/ssm_scan.hip", "include/ssm_scan.h"):
         with open(os.path.join(ROOT, rel)) as f:
             text = f.read()
