@@ -27,23 +27,32 @@ using f16v = float __attribute__((ext_vector_type(16)));
 // KH >= N/2 MFMA steps (N % 8 == 0, vector path), taken in chunks of KC = 16:
 // a chunk's C and carry operands are 4 float4 per lane, and the next chunk's
 // loads are in flight while the current chunk's 16 MFMAs run, instead of the
-// wave holding the whole contraction's operands.  Grid: n_seqs x n_segs x H x n_tblocks workgroups of 4 wavefronts;
-// workgroup b of a segment takes token tiles b*4 + w, stepping by
-// n_tblocks*4 tiles until the segment ends.
+// wave holding the whole contraction's operands.  Grid: n_seqs x (n_segs - 1) x
+// H x n_tblocks workgroups of 4 wavefronts (segments 1 and up); workgroup b of
+// a segment takes token tiles b*4 + w, stepping by n_tblocks*4 tiles until the
+// segment ends.
 // FULL: N/2 == KH, so no chunk reaches past the row and nothing is masked.
 template <int KH, bool FULL>
 __global__ void __launch_bounds__(kThreads) correct_mfma_kernel(ScanArgs a, int n_tblocks) {
     constexpr int KC = 16;                              // MFMA steps per chunk
     constexpr int NCH = KH / KC;
     static_assert(KH % KC == 0, "whole chunks");
-    int q = blockIdx.x;
+    // XCD-contiguous order (as the scan's): the hardware deals workgroups to
+    // the XCDs round robin, so consecutive logical blocks -- the token tiles of
+    // one head, then the neighbouring heads that share its C rows -- are given
+    // to one XCD and share its L2.
+    const int bid = blockIdx.x;
+    const int nb = gridDim.x;
+    const int per = nb / kXcds, rem = nb % kXcds;
+    const int xcd = bid % kXcds, kx = bid / kXcds;
+    int q = (xcd < rem) ? xcd * (per + 1) + kx : rem * (per + 1) + (xcd - rem) * per + kx;
     const int tb = q % n_tblocks;
     q /= n_tblocks;
     const int hd = q % a.H;
     q /= a.H;
-    const int seg = q % a.n_segs;
-    const int s = q / a.n_segs;
-    if (seg == 0) return;                              // segment 0 started from the true state
+    // the grid holds segments 1..n_segs-1 only (segment 0 started from the true state)
+    const int seg = q % (a.n_segs - 1) + 1;
+    const int s = q / (a.n_segs - 1);
     const SegRange sr = segment_range(a, s, seg);
     if (seg >= sr.n_real) return;
 

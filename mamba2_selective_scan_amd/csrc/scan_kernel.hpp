@@ -716,11 +716,8 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                     for (int e = 0; e < E; ++e) h[e] *= sigma;
                     return;
                 }
-                // the rare direct chunk: a plain loop, the row's first lane stores y
-                for (int tt = 0; tt < nt; ++tt) {
-                    const float yv = token_y(base, tt, std::false_type{});
-                    if (r == 0) Ys[tt * RB] = yv;
-                }
+                // a direct chunk (one token, or a decay product below the floor)
+                run_tokens(base, Ys, nt, std::false_type{});
             } else {
                 run_tokens(base, Ys, nt, std::false_type{});
             }

@@ -321,7 +321,8 @@ int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_
     // the state rows split into float4 halves (N % 8 == 0, N <= 128).
     if (vec && d->d_state % 8 == 0 && d->d_state <= 128) {
         const int n_tblocks = (plan.seg_len + 127) / 128;
-        const int64_t grid = int64_t(n_seqs) * plan.n_segs * d->n_heads * n_tblocks;
+        // segments 1.. only: segment 0 started from the true state
+        const int64_t grid = int64_t(n_seqs) * (plan.n_segs - 1) * d->n_heads * n_tblocks;
         if (grid > INT32_MAX) return SSM_ERR_UNSUPPORTED;
         const int nh = d->d_state / 2;
         const void *kern =
