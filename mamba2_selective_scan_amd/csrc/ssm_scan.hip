@@ -14,6 +14,7 @@
 
 #include "correct_mfma.hpp"
 #include "scan_kernel.hpp"
+#include "ssd_kernel.hpp"
 #include "status.hpp"
 
 namespace ssm {
@@ -193,14 +194,25 @@ int check_dims(const ssm_scan_dims *d) {
 
 // How a prefill is cut over time.  A single long sequence exposes only
 // H * P rows, one wavefront per SIMD at the headline geometry; cutting it into
-// n_segs segments multiplies the wavefronts by n_segs.  Auto mode cuts when
-// the whole-sequence launch would give fewer than 2 wavefronts per SIMD
-// (1024 SIMDs), aiming at 4, with segments of at least 256 tokens.
+// n_segs segments multiplies the wavefronts by n_segs.  Auto mode, for the
+// register segment scan: cut when the whole-sequence launch would give fewer
+// than 2 wavefronts per SIMD (1024 SIMDs), aiming at 4; for the matrix-core
+// segment scan (shapes it covers): aim at 2 wavefronts per SIMD of its own
+// geometry (4 waves per 64 rows of a head).  Segments have at least 256 tokens.
 struct SegPlan {
     int n_segs, seg_len;
 };
 constexpr int64_t kTargetWaves = 4096;
+constexpr int64_t kSsdTargetWaves = 2048;  // matrix-core segment scans
 constexpr int kMinSegTokens = 256;
+
+// The chunked matrix-core segment scan covers N in {32, 64, 128} with whole
+// 16-row tiles, on the vector path (16-byte aligned arrays).
+bool ssd_shape(const ssm_scan_dims *d) {
+    const int N = d->d_state;
+    return (N == 32 || N == 64 || N == 128) && d->head_dim % 16 == 0;
+}
+bool ssd_eligible(const ssm_scan_dims *d, bool vec) { return vec && ssd_shape(d); }
 
 SegPlan plan_segments(const ssm_scan_dims *d, const ShapeRow &row, int32_t n_seqs,
                       int32_t max_seqlen, int32_t requested) {
@@ -209,6 +221,14 @@ SegPlan plan_segments(const ssm_scan_dims *d, const ShapeRow &row, int32_t n_seq
     int64_t K;
     if (requested > 1) {
         K = requested;
+    } else if (ssd_shape(d)) {
+        // matrix-core segments: a workgroup of four waves per 64 rows of a head;
+        // aim at two waves per SIMD (measured at 1 x 4096, H64 P64 N128: 8
+        // segments 0.237 ms, 12: 0.237, 4: 0.278, 16: 0.243)
+        const int64_t waves = int64_t(n_seqs) * d->n_heads * ((d->head_dim + 63) / 64) * ssm::kWaves;
+        if (waves >= kSsdTargetWaves) return SegPlan{1, 0};
+        K = (kSsdTargetWaves + waves - 1) / waves;
+        K = std::min<int64_t>(K, max_seqlen / kMinSegTokens);
     } else {
         const int RB = ssm::kWaves * (64 / row.R);
         const int64_t waves = int64_t(n_seqs) * d->n_heads * ((d->head_dim + RB - 1) / RB) * ssm::kWaves;
@@ -302,8 +322,29 @@ int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_
     a.ws_state = reinterpret_cast<float *>(ws + w.state);
     a.ws_dtot = reinterpret_cast<float *>(ws + w.dtot);
     a.ws_dcum = reinterpret_cast<float *>(ws + w.dcum);
-    int rc = with_row(*row, Launch{a, vec, Kind::kSegScan, stream, 0});
-    if (rc != SSM_OK) return rc;
+    int rc = SSM_OK;
+    if (ssd_eligible(d, vec)) {
+        // the segment scans in chunked matrix form on the matrix cores
+        ScanArgs sa = a;
+        sa.n_row_blocks = (d->head_dim + 63) / 64;
+        const int64_t nb = int64_t(n_seqs) * plan.n_segs * d->n_heads * sa.n_row_blocks;
+        if (nb > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+        sa.n_blocks = int32_t(nb);
+        const int nt = d->d_state / 16;
+        const void *kern = nt == 2 ? reinterpret_cast<const void *>(&ssm::ssd_segscan_kernel<2>)
+                         : nt == 4 ? reinterpret_cast<const void *>(&ssm::ssd_segscan_kernel<4>)
+                                   : reinterpret_cast<const void *>(&ssm::ssd_segscan_kernel<8>);
+        const int lds = (nt == 2 ? ssm::SsdShape<2>::lds_floats()
+                       : nt == 4 ? ssm::SsdShape<4>::lds_floats()
+                                 : ssm::SsdShape<8>::lds_floats()) * int(sizeof(float));
+        void *params[] = {&sa};
+        const hipError_t err = hipLaunchKernel(kern, dim3(unsigned(nb)), dim3(kThreads), params,
+                                               size_t(lds), stream);
+        if (err != hipSuccess) return hip_fail(err, SSM_ERR_LAUNCH);
+    } else {
+        rc = with_row(*row, Launch{a, vec, Kind::kSegScan, stream, 0});
+        if (rc != SSM_OK) return rc;
+    }
     {
         const int64_t units = int64_t(n_seqs) * d->n_heads * d->head_dim * d->d_state / (vec ? 4 : 1);
         const int64_t grid = (units + kThreads - 1) / kThreads;
@@ -524,10 +565,25 @@ int ssm_scan_query_prefill_plan(const ssm_scan_dims *dims, int32_t n_seqs, int32
     const SegPlan plan = plan_segments(dims, *row, n_seqs, max_seqlen, n_segments);
     if (plan.n_segs > 1) {
         const bool vec = out->vector_path != 0;
-        const Geo geo = geo_for(*row, Kind::kSegScan);
-        out->chunk_tokens = geo.CT;
-        out->lds_bytes = with_row(*row, LdsBytes{vec, Kind::kSegScan});
-        out->blocks *= plan.n_segs;
+        if (ssd_eligible(dims, vec)) {
+            // matrix-core segment scan: 4 lanes hold a row's N values (l % 16 is
+            // the row, l / 16 the quarter of each 16-wide state tile), 64 rows
+            // per workgroup, 16-token chunks
+            const int nt = dims->d_state / 16;
+            out->lanes_per_row = 4;
+            out->elems_per_lane = dims->d_state / 4;
+            out->rows_per_block = 64;
+            out->chunk_tokens = 16;
+            out->lds_bytes = (nt == 2 ? ssm::SsdShape<2>::lds_floats()
+                            : nt == 4 ? ssm::SsdShape<4>::lds_floats()
+                                      : ssm::SsdShape<8>::lds_floats()) * int(sizeof(float));
+            out->blocks = int64_t(n_seqs) * plan.n_segs * dims->n_heads * ((dims->head_dim + 63) / 64);
+        } else {
+            const Geo geo = geo_for(*row, Kind::kSegScan);
+            out->chunk_tokens = geo.CT;
+            out->lds_bytes = with_row(*row, LdsBytes{vec, Kind::kSegScan});
+            out->blocks *= plan.n_segs;
+        }
         out->segments = plan.n_segs;
         out->segment_tokens = plan.seg_len;
     }

@@ -119,10 +119,10 @@ def test_no_kernel_uses_scratch():
     scratch = [int(v) for v in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
     # 7 state-size classes x (vector, scalar) x (4 option sets x (prefill, decode)
     # + segment scan + correction) + 2 combine kernels + 6 matrix-core corrections
-    # (3 contraction lengths, masked or not);
+    # (3 contraction lengths, masked or not) + 3 matrix-core segment scans (N 32, 64, 128);
     # conv1d + SiLU: (vector, scalar) x (4 history lengths x (decode, prefill)
     # + 3 with snapshots); gated RMSNorm: (vector, scalar) x 6 row-length classes
-    n_scan = 7 * 2 * (4 * 2 + 2) + 2 + 6
+    n_scan = 7 * 2 * (4 * 2 + 2) + 2 + 6 + 3
     n_conv = 2 * (4 * 2 + 3)
     n_norm = 2 * 6
     # gated delta rule: 5 key-width classes x (vector, scalar) x (prefill, decode)
@@ -138,15 +138,19 @@ def test_single_hip_runtime():
 
 
 def test_prefill_plan_and_workspace():
-    """The headline prefill (1 x 4096 at H64 P64 N128 G8) fills only 1024
-    wavefronts, so automatic planning cuts it into 4 segments of 1024 tokens;
-    a batch that already fills the GPU is not cut; forcing works; the
-    workspace holds one [H][P][N] state per segment plus the decay arrays."""
+    """The headline prefill (1 x 4096 at H64 P64 N128 G8) gives the matrix-core
+    segment scan 256 wavefronts per segment, so automatic planning cuts it into
+    8 segments of 512 tokens (2048 waves); the register segment scan's shapes
+    aim at 4096 waves; a batch that already fills the GPU is not cut; forcing
+    works; the workspace holds one [H][P][N] state per segment plus the decay
+    arrays."""
     g = m.prefill_plan(64, 64, 128, 8, 1, 4096)
-    assert g["segments"] == 4 and g["segment_tokens"] == 1024 and g["blocks"] == 4 * 256
-    assert g["chunk_tokens"] == 16 and g["lds_bytes"] <= 160 * 1024 // 4
+    assert g["segments"] == 8 and g["segment_tokens"] == 512 and g["blocks"] == 8 * 64
+    assert g["chunk_tokens"] == 16 and g["rows_per_block"] == 64 and g["lds_bytes"] <= 64 * 1024
     ws = m.workspace_size(64, 64, 128, 8, 1, 4096, 4096)
-    assert 4 * 64 * 64 * 128 * 4 + 4096 * 64 * 4 <= ws <= 4 * 64 * 64 * 128 * 4 + 4096 * 64 * 4 + 4096
+    assert 8 * 64 * 64 * 128 * 4 + 4096 * 64 * 4 <= ws <= 8 * 64 * 64 * 128 * 4 + 4096 * 64 * 4 + 4096
+    g = m.prefill_plan(64, 64, 100, 8, 1, 4096)                       # register segment scan
+    assert g["segments"] == 4 and g["segment_tokens"] == 1024 and g["blocks"] == 4 * 256
     assert m.prefill_plan(64, 64, 128, 8, 16, 4096)["segments"] == 1     # 16 seqs fill it
     assert m.workspace_size(64, 64, 128, 8, 16, 65536, 4096) == 0
     assert m.prefill_plan(64, 64, 128, 8, 1, 200)["segments"] == 1        # too short

@@ -251,15 +251,15 @@ def test_graph_replay_matches_eager(ssm):
 
 # ---------------------------------------------------------------- time-split prefill
 def test_split_prefill_headline(ssm, orc):
-    """1 x 4096 at H64 P64 N128 G8: the automatic plan cuts it into 4
-    segments; fresh and resuming start states."""
+    """1 x 4096 at H64 P64 N128 G8: the automatic plan cuts it into 8
+    segments (matrix-core segment scans); fresh and resuming start states."""
     for fresh in (1, 0):
         case = ssm_inputs.workload("prefill4096")
         if not fresh:
             case = ssm_inputs.make_case(64, 64, 128, 8, [4096], [0], seed=12)
         plan = ssm.prefill_plan(case.H, case.P, case.N, case.G, 1, 4096)
         say(f"split prefill 1x4096 fresh={fresh}: plan {plan}")
-        assert plan["segments"] == 4
+        assert plan["segments"] == 8
         y, st = run_gpu(case, "prefill_ws")
         y32, st32 = orc.scan_case(case, precision="f32")
         assert_parity(case, y, st, y32, st32, label=f"split 1x4096 fresh={fresh} vs fp32")
@@ -281,7 +281,8 @@ def test_split_prefill_mixed_batch(ssm, orc, segments, max_seqlen):
     assert_parity(case, y, st, y32, st32)
 
 
-@pytest.mark.parametrize("N,P", [(1, 5), (8, 16), (32, 16), (33, 5), (64, 96), (100, 96), (128, 16), (128, 40), (1024, 16)])
+@pytest.mark.parametrize("N,P", [(1, 5), (8, 16), (32, 16), (32, 48), (33, 5), (64, 80), (64, 96), (100, 96),
+                                 (128, 16), (128, 40), (128, 64), (1024, 16)])
 def test_split_prefill_shapes(ssm, orc, N, P):
     lengths = [0, 1, 77, 200, 31]
     case = ssm_inputs.make_case(4, P, N, 2, lengths, [1, 0, 0, 1, 0], seed=300 + N + P,
