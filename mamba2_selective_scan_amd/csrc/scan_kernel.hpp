@@ -553,13 +553,16 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                 const int nv = ok ? clamp4(rows_valid - pi) : 0;
                 px[u] = load4<VEC>(xsrc + (int64_t(t0 + tt) * H + hd) * P + p0 + pi, nv);
             }
-            pdt = (tid < nt) ? dt_transform(a.dt[int64_t(t0 + tid) * H + hd], bias_h, a.dt_softplus)
-                             : 0.f;
+            // raw dt: its transform waits until the commit, so nothing here
+            // waits for a load to arrive
+            pdt = (tid < nt) ? a.dt[int64_t(t0 + tid) * H + hd] : 0.f;
         };
 
         float run = 1.f;                                    // wave 0: dA product so far
         auto commit = [&](int buf, int t0, int nt) {
             float *base = lds + buf * S::BUF;
+            // the chunk's dt after bias and softplus (0 past its tokens)
+            auto dt_eff = [&] { return (tid < nt) ? dt_transform(pdt, bias_h, a.dt_softplus) : 0.f; };
             f4 *Bs4 = reinterpret_cast<f4 *>(base + S::OFF_B);
             f4 *Cs4 = reinterpret_cast<f4 *>(base + S::OFF_C);
             f4 *Xs4 = reinterpret_cast<f4 *>(base + S::OFF_X);
@@ -578,7 +581,8 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
             }
             if constexpr (SEGMENTED || LAZY) {
                 if (tid < 64) {                              // wave 0, all lanes active
-                    const float dA = (tid < nt) ? expf(pdt * A_h) : 1.f;
+                    const float dtv = dt_eff();
+                    const float dA = (tid < nt) ? expf(dtv * A_h) : 1.f;
                     const float loc = chunk_prefix_product<CT>(dA);     // from the chunk start
                     const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(loc), CT - 1));
                     if constexpr (SEGMENTED) {
@@ -600,7 +604,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                         // gives the same bits as decode
                         const bool lazy = nt > 1 && total >= kLazyFloor;
                         if (tid < CT) {
-                            base[S::OFF_DT + tid] = lazy ? pdt / loc : pdt;
+                            base[S::OFF_DT + tid] = lazy ? dtv / loc : dtv;
                             base[S::OFF_DA + tid] = lazy ? loc : dA;
                         }
                         if (tid == 0) base[S::OFF_LAZY] = lazy ? 1.f : 0.f;
@@ -608,8 +612,9 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                 }
             } else {
                 if (tid < CT) {
-                    base[S::OFF_DT + tid] = pdt;
-                    base[S::OFF_DA + tid] = expf(pdt * A_h);
+                    const float dtv = dt_eff();
+                    base[S::OFF_DT + tid] = dtv;
+                    base[S::OFF_DA + tid] = expf(dtv * A_h);
                 }
             }
         };
@@ -807,11 +812,15 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
 // Combine pass of the time-parallel prefill, one thread per 4 (VEC) or 1 state
 // elements of one (sequence, head, row): walk the sequence's segments in order,
 //     carry <- dtot[k] * carry + local_end[k]
-// starting from segment 0's (true) end state; leave the state carried INTO
-// segment k in entry k-1 for the correction pass, and write the final carry to
-// the sequence's slot.
+// starting from segment 0's (true) end state, and leave the state carried INTO
+// segment k in entry k-1.  With into_slot, every segment's end state is in the
+// workspace and the final carry goes to the sequence's slot (the register
+// segment scan, followed by the corrections).  Without it the last segment's
+// end state is not there yet: the walk stops at the carry into the last
+// segment, which then runs from it (the matrix-core scan pass).
 template <bool VEC>
-__global__ void __launch_bounds__(kThreads) combine_kernel(ScanArgs a, int64_t n_units) {
+__global__ void __launch_bounds__(kThreads) combine_kernel(ScanArgs a, int64_t n_units,
+                                                           int into_slot) {
     const int64_t u = int64_t(blockIdx.x) * kThreads + threadIdx.x;
     if (u >= n_units) return;
     constexpr int W = VEC ? 4 : 1;
@@ -824,23 +833,30 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(ScanArgs a, int64_t n
     const int64_t hpn = int64_t(a.H) * a.P * a.N;
     float *w = a.ws_state + int64_t(s) * a.n_segs * hpn + e;
     float *dst = a.state + int64_t(a.slot[s]) * hpn + e;
+    const int k_end = into_slot ? sr.n_real : sr.n_real - 1;   // local end states folded in
     if constexpr (VEC) {
         f4 carry = *reinterpret_cast<const f4 *>(w);
-        for (int k = 1; k < sr.n_real; ++k) {
+        for (int k = 1; k < k_end; ++k) {
             if (k > 1) *reinterpret_cast<f4 *>(w + (k - 1) * hpn) = carry;
             const float d = a.ws_dtot[(int64_t(s) * a.n_segs + k) * a.H + hd];
             const f4 loc = *reinterpret_cast<const f4 *>(w + k * hpn);
             carry = d * carry + loc;
         }
-        __builtin_nontemporal_store(carry, reinterpret_cast<f4 *>(dst));
+        if (into_slot)
+            __builtin_nontemporal_store(carry, reinterpret_cast<f4 *>(dst));
+        else if (k_end > 1)
+            *reinterpret_cast<f4 *>(w + (k_end - 1) * hpn) = carry;
     } else {
         float carry = w[0];
-        for (int k = 1; k < sr.n_real; ++k) {
+        for (int k = 1; k < k_end; ++k) {
             if (k > 1) w[(k - 1) * hpn] = carry;
             const float d = a.ws_dtot[(int64_t(s) * a.n_segs + k) * a.H + hd];
             carry = d * carry + w[k * hpn];
         }
-        dst[0] = carry;
+        if (into_slot)
+            dst[0] = carry;
+        else if (k_end > 1)
+            w[(k_end - 1) * hpn] = carry;
     }
 }
 

@@ -24,13 +24,19 @@
 // accumulator ever goes through LDS to be transposed.  The emulation of this
 // scheme with these lane rules reproduced the fp64 oracle to rounding.
 //
-// One workgroup per (sequence, time segment, head, block of 64 rows): its four
-// wavefronts own 16 rows each.  B, C and x of a chunk are staged in LDS,
-// double-buffered (rows padded so the strided state-update reads are
-// conflict-free), the per-token scalars are formed once in wave 0.  The kernel
-// leaves exactly what the register segment scan leaves: y of the segment, the
-// segment's end state (workspace entry, or the slot when the sequence was not
-// cut), the running decay product per token and the segment total.
+// Two kernels here serve the time-split prefill.  The state pass
+// (ssd_state_kernel) runs every segment but the last of a cut sequence and
+// leaves only the segment's end state and total decay (segment 0 from the
+// sequence's start state, later ones from zero); the combine pass turns those
+// into the state carried into each segment; the scan pass (ssd_scan_kernel)
+// then runs every segment from its true carried-in state, so the y it writes
+// is final and the last segment's end state is the sequence's.  No y is ever
+// read back.  The scan pass runs one workgroup per (sequence, time segment,
+// head, block of 64 rows): its four wavefronts own 16 rows each.  B, C and x of
+// a chunk are staged in LDS, double-buffered (rows padded so the strided
+// state-update reads are conflict-free), the per-token scalars are formed once
+// in wave 0, and G^T, the same for the four wavefronts, is formed a quarter
+// by each and summed through LDS.
 #pragma once
 
 #include "scan_kernel.hpp"
@@ -56,7 +62,8 @@ struct SsdShape {
     static constexpr int BUF = ((OFF_E15 + 1) + 3) / 4 * 4;
     static constexpr int U_BC = (CT * N / 4 + kThreads - 1) / kThreads;    // float4 units of B (and of C)
     static constexpr int U_X = (CT * RBW / 4 + kThreads - 1) / kThreads;   // float4 units of x
-    static constexpr int lds_floats() { return 2 * BUF; }
+    static constexpr int OFF_GX = 2 * BUF;          // G^T partials [4 waves][64 lanes][4]
+    static constexpr int lds_floats() { return OFF_GX + kWaves * 64 * 4; }
 };
 
 // Sum over lanes 0..l of each 16-lane DPP row (lanes past a row's start add 0).
@@ -72,11 +79,218 @@ __device__ __forceinline__ f4m mfma16(float a, float b, f4m c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Grid: n_seqs x n_segs x H x ceil(P / 64) workgroups (a.n_row_blocks = ceil(P/64),
-// a.n_blocks their product), XCD-contiguous order as the register kernel's.
-// Requires the vector path (16-byte aligned arrays), N = 16 * NT, P % 16 == 0.
+// Running sum over the 64 lanes of a wavefront (inclusive): within each
+// 16-lane DPP row, then row r adds the running total that the last lane of
+// row r - 1 holds by then (rows in order, so each adds every earlier row once).
+__device__ __forceinline__ float wave_prefix_sum(float v, int lane) {
+    v = row_prefix_sum(v);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+        const float before = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r - 1));
+        if ((lane >> 4) == r) v += before;
+    }
+    return v;
+}
+
+// E consecutive floats as one load: a vector for E > 1, a float for E = 1.
+template <int E> struct VecT { using type = float __attribute__((ext_vector_type(E))); };
+template <> struct VecT<1> { using type = float; };
+template <int E> __device__ __forceinline__ float vget(const typename VecT<E>::type &v, int e) {
+    if constexpr (E == 1) return v; else return v[e];
+}
+
+// The state pass: the end state of every segment but a sequence's last, and
+// its total decay, with no y.  Over a window of up to kSsdWindow tokens (S_t
+// the inclusive running log-decay from the window start)
+//     h^T <- e^{S_last} h^T + B^T (w X),   w_t = e^{S_last - S_t} dt_t,
+// a plain contraction over the window's tokens on v_mfma_f32_16x16x4f32.
+// The workgroup first turns the window's dt into the weights w (an LDS array,
+// summed from the window end); after that each wavefront streams its operands
+// from global memory straight into registers, with no LDS staging and no
+// barrier per chunk.  A wavefront owns two 16-row tiles (rows p0 + 16 t + i)
+// and E*16 state columns, so one B load feeds both tiles' products.  To make
+// that load one contiguous vector per lane the columns are taken in a
+// permuted order: lane l%16 = i reads B[t][n_base + E i .. + E - 1] and uses
+// its element e for column tile e, which holds columns n_base + E i + e; the
+// accumulators then hold h[p0 + 16 t + l%16][n_base + E (4 (l/16) + v) + e].
+// The four wavefronts of a workgroup cover 64 rows x 2 column parts; with
+// NS > 1 the grid splits the columns further.  Segment 0 of a resumed
+// sequence starts from the slot, the others from zero.  Grid: n_seqs x
+// (n_segs - 1) x H x ceil(P / 64) x NS workgroups, XCD-contiguous order.
+constexpr int kSsdWindow = 512;          // tokens whose weights one pass of the prologue forms
+template <int NT, int NS, int IT>        // N = 16 NT; NS column parts; IT tokens per load group
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 4)))
+ssd_state_kernel(ScanArgs a) {
+    constexpr int N = 16 * NT;
+    constexpr int NW = N / (2 * NS);                 // state columns per wavefront
+    constexpr int E = NW / 16;                       // columns per lane = column tiles per wave
+    constexpr int KS = IT / 4;                       // MFMA steps per load group
+    constexpr int TPT = kSsdWindow / kThreads;       // prologue tokens per thread
+    static_assert(NW % 16 == 0 && (E == 1 || E == 2 || E == 4 || E == 8) && IT % 4 == 0 &&
+                  kSsdWindow % IT == 0 && (kSsdWindow / IT) % 2 == 0, "state pass shape");
+    using fE = typename VecT<E>::type;
+    __shared__ float w_lds[kSsdWindow];
+    __shared__ float wave_tot[kWaves];
+
+    const int bid = blockIdx.x;
+    const int nb = a.n_blocks;
+    const int per = nb / kXcds, rem = nb % kXcds;
+    const int xcd = bid % kXcds, kx = bid / kXcds;
+    const int L = (xcd < rem) ? xcd * (per + 1) + kx : rem * (per + 1) + (xcd - rem) * per + kx;
+    const int segs = a.n_segs - 1;
+    const int part = L % NS;
+    const int rbw = (L / NS) % a.n_row_blocks;
+    const int hd = (L / (NS * a.n_row_blocks)) % a.H;
+    const int seg = (L / (NS * a.n_row_blocks * a.H)) % segs;
+    const int s = L / (NS * a.n_row_blocks * a.H * segs);
+
+    const int H = a.H, P = a.P, G = a.G;
+    const int g = hd / a.heads_per_group;
+    const SegRange sr = segment_range(a, s, seg);
+    if (seg >= sr.n_real - 1) return;                // the last segment needs no pass
+    const int t_begin = sr.t_begin, t_end = sr.t_end; // at least one token
+    const int t_last = t_end - 1;
+    const bool from_slot = seg == 0 && a.fresh[s] == 0;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int tl = lane & 15, kq = lane >> 4;
+    const int p0 = rbw * 64 + 32 * (w & 1);          // the wave's two row tiles: p0, p0 + 16
+    const bool tile_ok[2] = {p0 < P, p0 + 16 < P};   // P % 16 == 0: whole tiles
+    const int n_base = (2 * part + (w >> 1)) * NW;
+    const int64_t hpn = int64_t(H) * P * N;
+    const float A_h = a.A[hd];
+    const float bias_h = a.dt_bias ? a.dt_bias[hd] : 0.f;
+
+    // hacc[t][e] register v of lane l: h[p0 + 16 t + l%16][n_base + E (4 (l/16) + v) + e]
+    f4m hacc[2][E];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < E; ++e) hacc[t][e] = f4m{0.f, 0.f, 0.f, 0.f};
+    const int64_t head_off = int64_t(hd) * P * N;
+    if (from_slot) {
+        const float *src = a.state + int64_t(a.slot[s]) * hpn + head_off + n_base;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (!tile_ok[t]) continue;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const fE h = *reinterpret_cast<const fE *>(src + int64_t(p0 + 16 * t + tl) * N + E * (4 * kq + v));
+#pragma unroll
+                for (int e = 0; e < E; ++e) hacc[t][e][v] = vget<E>(h, e);
+            }
+        }
+    }
+
+    // operand registers of one load group: step k covers tokens 4 k + l/16
+    float xg[2][KS][2];
+    fE bg[2][KS];
+    const int row1 = tile_ok[1] ? p0 + 16 : p0;      // a tile past P rereads tile 0's rows
+    const float *xrow0 = a.x + int64_t(hd) * P + min(p0, P - 16) + tl;   // + token * H * P
+    const float *xrow1 = a.x + int64_t(hd) * P + row1 + tl;
+    const float *brow = a.B + int64_t(g) * N + n_base + E * tl;          // + token * G * N
+    auto load_group = [&](int r, int t0) {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const int tok = min(t0 + 4 * k + kq, t_last);   // in range; weight 0 past the end
+            xg[r][k][0] = xrow0[int64_t(tok) * H * P];
+            xg[r][k][1] = xrow1[int64_t(tok) * H * P];
+            bg[r][k] = *reinterpret_cast<const fE *>(brow + int64_t(tok) * G * N);
+        }
+    };
+    auto mma_group = [&](int r, int w0) {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const float wk = w_lds[w0 + 4 * k + kq];
+            const float wx0 = wk * xg[r][k][0], wx1 = wk * xg[r][k][1];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                hacc[0][e] = mfma16(vget<E>(bg[r][k], e), wx0, hacc[0][e]);
+                hacc[1][e] = mfma16(vget<E>(bg[r][k], e), wx1, hacc[1][e]);
+            }
+        }
+    };
+
+    float run = 1.f;                                   // product of dA over the segment
+    for (int tw = t_begin; tw < t_end; tw += kSsdWindow) {
+        const int m = min(kSsdWindow, t_end - tw);
+        if (tile_ok[0]) load_group(0, tw);             // first operands in flight during the prologue
+        // ---- prologue: w_t = e^{S_last - S_t} dt_t for the window's tokens.  The
+        // exponent is summed from the window end backwards (thread 0 takes the
+        // last tokens), so it is exact to rounding of its own size where the
+        // weight matters; a difference of two long running sums would not be.
+        __syncthreads();                               // the previous window's weights are read
+        float d[TPT], c[TPT];
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+            const int j = kSsdWindow - 1 - (TPT * tid + i);
+            d[i] = j < m ? dt_transform(a.dt[int64_t(tw + j) * H + hd], bias_h, a.dt_softplus) : 0.f;
+            c[i] = acc;                                // sum over the thread's later tokens
+            acc += d[i] * A_h;
+        }
+        const float incl = wave_prefix_sum(acc, lane);
+        if (lane == 63) wave_tot[w] = incl;
+        __syncthreads();
+        float after = incl - acc, total = 0.f;        // sum over the tokens after the thread's
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) {
+            const float t = wave_tot[k];
+            total += t;
+            if (k < w) after += t;
+        }
+#pragma unroll
+        for (int i = 0; i < TPT; ++i)
+            w_lds[kSsdWindow - 1 - (TPT * tid + i)] = expf(after + c[i]) * d[i];
+        const float e_tot = expf(total);
+        run *= e_tot;
+        __syncthreads();
+        // ---- h^T <- e^{S_last} h^T + B^T (w X) over the window, IT tokens per
+        // group, pairs of groups (tokens past the window end weigh 0), the next
+        // group's loads issued before this group's products; scheduling barriers
+        // keep them there (left alone the compiler sinks loads to their use)
+        if (tile_ok[0]) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < E; ++e) hacc[t][e] *= e_tot;
+            const int n_pairs = (m + 2 * IT - 1) / (2 * IT);
+            for (int q = 0; q < 2 * n_pairs; q += 2) {
+                load_group(1, tw + (q + 1) * IT);
+                __builtin_amdgcn_sched_barrier(0);
+                mma_group(0, q * IT);
+                load_group(0, tw + (q + 2) * IT);
+                __builtin_amdgcn_sched_barrier(0);
+                mma_group(1, (q + 1) * IT);
+            }
+        }
+    }
+    if (rbw == 0 && part == 0 && tid == 0) a.ws_dtot[(int64_t(s) * a.n_segs + seg) * H + hd] = run;
+    float *dst = a.ws_state + (int64_t(s) * a.n_segs + seg) * hpn + head_off + n_base;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        if (!tile_ok[t]) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            fE h;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                if constexpr (E == 1) h = hacc[t][e][v]; else h[e] = hacc[t][e][v];
+            }
+            *reinterpret_cast<fE *>(dst + int64_t(p0 + 16 * t + tl) * N + E * (4 * kq + v)) = h;
+        }
+    }
+}
+
+// The scan pass.  Grid: n_seqs x n_segs x H x ceil(P / 64) workgroups
+// (a.n_row_blocks = ceil(P/64), a.n_blocks their product), XCD-contiguous order
+// as the register kernel's.  Requires the vector path (16-byte aligned arrays),
+// N = 16 * NT, P % 16 == 0.  Segment k > 0 starts from workspace entry k - 1,
+// which the combine pass left holding the state carried into it.
 template <int NT>
-__global__ void __launch_bounds__(kThreads) ssd_segscan_kernel(ScanArgs a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+ssd_scan_kernel(ScanArgs a) {
     using S = SsdShape<NT>;
     constexpr int N = S::N, CT = S::CT, LDN = S::LDN;
     extern __shared__ float4 lds_raw[];
@@ -95,12 +309,15 @@ __global__ void __launch_bounds__(kThreads) ssd_segscan_kernel(ScanArgs a) {
     const int H = a.H, P = a.P, G = a.G;
     const int g = hd / a.heads_per_group;
     const SegRange sr = segment_range(a, s, seg);
-    if (seg >= sr.n_real) return;                    // the sequence is shorter
+    const int last = sr.n_real - 1;
+    if (seg > last) return;                          // past the sequence's segments
     const int t_begin = sr.t_begin, t_end = sr.t_end;
     const int n_tok = t_end - t_begin;
-    const bool split = sr.n_real > 1;
-    const bool fresh = seg > 0 || a.fresh[s] != 0;   // later segments start from zero
-    if (!split && !fresh && n_tok <= 0) return;      // empty resume: slot unchanged
+    // starting state: the slot's for segment 0 of a resumed sequence, the
+    // carried-in state (workspace) for a later segment, else 0
+    const bool from_slot = seg == 0 && a.fresh[s] == 0;
+    const bool from_carry = seg > 0;
+    if (from_slot && n_tok <= 0) return;             // empty resume: slot unchanged
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -110,7 +327,7 @@ __global__ void __launch_bounds__(kThreads) ssd_segscan_kernel(ScanArgs a) {
     const bool wave_ok = p0 < P;                     // P % 16 == 0: whole wave tiles
     const int64_t hpn = int64_t(H) * P * N;
     float *const st_head = a.state + (int64_t(a.slot[s]) * H + hd) * int64_t(P) * N;
-    float *const ws_head = a.ws_state + (int64_t(s) * a.n_segs + seg) * hpn + int64_t(hd) * P * N;
+    float *const ws_head = a.ws_state + int64_t(s) * a.n_segs * hpn + int64_t(hd) * P * N;
     const float A_h = a.A[hd];
     const float bias_h = a.dt_bias ? a.dt_bias[hd] : 0.f;
 
@@ -119,11 +336,12 @@ __global__ void __launch_bounds__(kThreads) ssd_segscan_kernel(ScanArgs a) {
     f4m hacc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) hacc[nt] = f4m{0.f, 0.f, 0.f, 0.f};
-    if (!fresh && wave_ok) {
+    if ((from_slot || from_carry) && wave_ok) {
+        const float *src = from_slot ? st_head : ws_head + int64_t(seg - 1) * hpn;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const f4 v = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(
-                st_head + int64_t(p0 + tl) * N + 16 * nt + 4 * kq));
+                src + int64_t(p0 + tl) * N + 16 * nt + 4 * kq));
             hacc[nt] = f4m{v.x, v.y, v.z, v.w};
         }
     }
@@ -151,11 +369,9 @@ __global__ void __launch_bounds__(kThreads) ssd_segscan_kernel(ScanArgs a) {
             const bool ok = (q < CT * S::RBW / 4) && (tt < nt_) && (prow0 + pi < P);
             px[u] = load4<true>(a.x + (int64_t(t0 + tt) * H + hd) * P + prow0 + pi, ok ? 4 : 0);
         }
-        pdt = (tid < nt_) ? dt_transform(a.dt[int64_t(t0 + tid) * H + hd], bias_h, a.dt_softplus)
-                          : 0.f;
+        pdt = (tid < nt_) ? a.dt[int64_t(t0 + tid) * H + hd] : 0.f;   // transformed at the commit
     };
-    float run = 1.f;                                     // wave 0: decay product so far
-    auto commit = [&](int buf, int t0, int nt_) {
+    auto commit = [&](int buf, int nt_) {
         float *base = lds + buf * S::BUF;
 #pragma unroll
         for (int u = 0; u < S::U_BC; ++u) {
@@ -174,97 +390,140 @@ __global__ void __launch_bounds__(kThreads) ssd_segscan_kernel(ScanArgs a) {
         }
         if (tid < 64) {                                  // wave 0, all lanes active
             // lanes 0..15 hold the chunk's tokens (0 past the segment end)
-            const float dtv = (tid < nt_) ? pdt : 0.f;
+            const float dtv = (tid < nt_) ? dt_transform(pdt, bias_h, a.dt_softplus) : 0.f;
             const float Sv = row_prefix_sum(dtv * A_h);
             const float S15 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Sv), 15));
-            const float eS = expf(Sv);
             const float e15 = expf(S15);
             if (tid < CT) {
                 base[S::OFF_S + tid] = Sv;
                 base[S::OFF_DT + tid] = dtv;
-                base[S::OFF_ES + tid] = eS;
+                base[S::OFF_ES + tid] = expf(Sv);
                 base[S::OFF_W + tid] = expf(S15 - Sv) * dtv;
             }
             if (tid == 0) base[S::OFF_E15] = e15;
-            // a split sequence's segment also leaves the running product for
-            // the correction pass (one row block per head)
-            if (split && rbw == 0 && tid < nt_) a.ws_dcum[int64_t(t0 + tid) * H + hd] = run * eS;
-            run *= e15;
         }
     };
 
-    auto compute = [&](int buf, int t0, int nt_) {
+    // h^T = e^{S_15} h^T + B^T (w X): tile nt, step q, lane l: A = B[4(l/16)+q][16 nt + l%16],
+    // B operand = w_s x[s][p] with s = 4(l/16) + q
+    auto update_state = [&](const float *base, const float (&bup)[4][NT], const float (&xr)[4]) {
+        float wx[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wx[q] = base[S::OFF_W + 4 * kq + q] * xr[q];
+        const float e15 = base[S::OFF_E15];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) hacc[nt] *= e15;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) hacc[nt] = mfma16(bup[q][nt], wx[q], hacc[nt]);
+        }
+    };
+
+    // y of the chunk just computed: stored after the next chunk's commit, so
+    // that commit waits only on loads and the stores drain during the next
+    // chunk's products
+    f4m ypend = {0.f, 0.f, 0.f, 0.f};
+    auto store_y = [&](int t0, int nt_) {
         if (!wave_ok) return;
+        float *const yrow = a.y + (int64_t(t0 + 4 * kq) * H + hd) * P + p0 + tl;
+        const int64_t ystep = int64_t(H) * P;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            if (4 * kq + v < nt_) yrow[v * ystep] = ypend[v];
+    };
+    auto compute = [&](int buf) {
         const float *base = lds + buf * S::BUF;
+        // G^T = B C^T is the same for the four waves: each forms the part over
+        // its quarter of the contraction index n (NT of the 4 NT steps) and the
+        // parts meet in LDS.  Step f = 4 tile + j, lane l: n = 16 tile + 4 (l/16) + j.
+        f4m gpart = {0.f, 0.f, 0.f, 0.f};
+        float gb[NT], gc[NT];
+        if constexpr (NT % 4 == 0) {
+#pragma unroll
+            for (int k = 0; k < NT / 4; ++k) {
+                const int off = tl * LDN + 16 * (w * (NT / 4) + k) + 4 * kq;
+                const f4 bq = *reinterpret_cast<const f4 *>(base + S::OFF_B + off);
+                const f4 cq = *reinterpret_cast<const f4 *>(base + S::OFF_C + off);
+                gb[4 * k + 0] = bq.x; gb[4 * k + 1] = bq.y; gb[4 * k + 2] = bq.z; gb[4 * k + 3] = bq.w;
+                gc[4 * k + 0] = cq.x; gc[4 * k + 1] = cq.y; gc[4 * k + 2] = cq.z; gc[4 * k + 3] = cq.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                const int f = w * NT + i;
+                const int off = tl * LDN + 16 * (f / 4) + 4 * kq + f % 4;
+                gb[i] = base[S::OFF_B + off];
+                gc[i] = base[S::OFF_C + off];
+            }
+        }
+        float xr[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) xr[v] = base[S::OFF_X + (4 * kq + v) * S::RBW + 16 * w + tl];
+        // the state update's A operands, B[4(l/16) + q][16 nt + l%16]
+        float bup[4][NT];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                bup[q][nt] = base[S::OFF_B + (4 * kq + q) * LDN + 16 * nt + tl];
         // per-lane scalars: own token t = l%16; rows s = 4(l/16) + v
         const float S_t = base[S::OFF_S + tl];
-        float Ss[4], dts[4], eSr[4], wq[4], xr[4];
+        float Ss[4], dts[4], eSr[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int sv = 4 * kq + v;
             Ss[v] = base[S::OFF_S + sv];
             dts[v] = base[S::OFF_DT + sv];
             eSr[v] = base[S::OFF_ES + sv];
-            wq[v] = base[S::OFF_W + sv];
-            xr[v] = base[S::OFF_X + sv * S::RBW + 16 * w + tl];
         }
-        const float e15 = base[S::OFF_E15];
-        // operands: C and B rows of token l%16, n = 16 nt + 4 (l/16) + v
-        f4 creg[NT], breg[NT];
+        // C rows of token l%16 for Y = C h^T, n = 16 nt + 4 (l/16) + v
+        f4 creg[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+        for (int nt = 0; nt < NT; ++nt)
             creg[nt] = *reinterpret_cast<const f4 *>(base + S::OFF_C + tl * LDN + 16 * nt + 4 * kq);
-            breg[nt] = *reinterpret_cast<const f4 *>(base + S::OFF_B + tl * LDN + 16 * nt + 4 * kq);
-        }
-        // G^T = B C^T and Y = C h^T, interleaved (independent chains)
-        f4m gacc = {0.f, 0.f, 0.f, 0.f}, yacc = {0.f, 0.f, 0.f, 0.f};
+        // keep every operand read issued ahead of the products (the scheduler
+        // would otherwise reuse a few registers and wait on each group)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            gacc = mfma16(breg[nt].x, creg[nt].x, gacc);
-            yacc = mfma16(creg[nt].x, hacc[nt][0], yacc);
-            gacc = mfma16(breg[nt].y, creg[nt].y, gacc);
-            yacc = mfma16(creg[nt].y, hacc[nt][1], yacc);
-            gacc = mfma16(breg[nt].z, creg[nt].z, gacc);
-            yacc = mfma16(creg[nt].z, hacc[nt][2], yacc);
-            gacc = mfma16(breg[nt].w, creg[nt].w, gacc);
-            yacc = mfma16(creg[nt].w, hacc[nt][3], yacc);
+        for (int i = 0; i < NT; ++i) gpart = mfma16(gb[i], gc[i], gpart);
+        reinterpret_cast<f4m *>(lds + S::OFF_GX)[w * 64 + lane] = gpart;
+        __builtin_amdgcn_sched_barrier(0);
+        f4m yacc = {0.f, 0.f, 0.f, 0.f};
+        if (wave_ok) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                yacc = mfma16(creg[nt].x, hacc[nt][0], yacc);
+                yacc = mfma16(creg[nt].y, hacc[nt][1], yacc);
+                yacc = mfma16(creg[nt].z, hacc[nt][2], yacc);
+                yacc = mfma16(creg[nt].w, hacc[nt][3], yacc);
+            }
         }
+        __syncthreads();                                 // the four parts of G^T are in
+        if (!wave_ok) return;
+        f4m gacc = reinterpret_cast<const f4m *>(lds + S::OFF_GX)[lane];
+#pragma unroll
+        for (int k = 1; k < kWaves; ++k) gacc += reinterpret_cast<const f4m *>(lds + S::OFF_GX)[k * 64 + lane];
         // G'^T[s][t] = G^T[s][t] e^{S_t - S_s} dt_s for s <= t, else 0
         // (lane l, register v: s = 4(l/16) + v, t = l%16); Y rows t = 4(l/16) + v
         // take the carried-in state's decay e^{S_t}
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int sv = 4 * kq + v;
-            gacc[v] = (sv <= tl) ? gacc[v] * expf(S_t - Ss[v]) * dts[v] : 0.f;
+            gacc[v] = (sv <= tl) ? gacc[v] * __expf(S_t - Ss[v]) * dts[v] : 0.f;
             yacc[v] *= eSr[v];
         }
         // Y += G' X
 #pragma unroll
         for (int v = 0; v < 4; ++v) yacc = mfma16(gacc[v], xr[v], yacc);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int tt = 4 * kq + v;
-            if (tt < nt_) a.y[(int64_t(t0 + tt) * H + hd) * P + p0 + tl] = yacc[v];
-        }
-        // h^T = e^{S_15} h^T + B^T (w X): tile nt, step q, lane l: A = B[4(l/16)+q][16 nt + l%16],
-        // B operand = w_s x[s][p] with s = 4(l/16) + q
-        float wx[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) wx[q] = wq[q] * xr[q];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) hacc[nt] *= e15;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                hacc[nt] = mfma16(base[S::OFF_B + (4 * kq + q) * LDN + 16 * nt + tl], wx[q], hacc[nt]);
-        }
+        ypend = yacc;                                    // stored after the next commit
+        update_state(base, bup, xr);
     };
 
     const int n_chunks = (n_tok + CT - 1) / CT;
     if (n_chunks > 0) {
         issue_loads(t_begin, min(CT, n_tok));
-        commit(0, t_begin, min(CT, n_tok));
+        commit(0, min(CT, n_tok));
     }
     __syncthreads();
     for (int c = 0; c < n_chunks; ++c) {
@@ -273,20 +532,18 @@ __global__ void __launch_bounds__(kThreads) ssd_segscan_kernel(ScanArgs a) {
         const int nt_ = min(CT, t_end - t0);
         const bool has_next = c + 1 < n_chunks;
         if (has_next) issue_loads(t0 + CT, min(CT, t_end - t0 - CT));
-        compute(buf, t0, nt_);
-        if (has_next) commit(buf ^ 1, t0 + CT, min(CT, t_end - t0 - CT));
+        compute(buf);
+        if (has_next) commit(buf ^ 1, min(CT, t_end - t0 - CT));
+        store_y(t0, nt_);
         __syncthreads();
     }
-    // a split sequence's segment records its total decay once per head
-    if (split && rbw == 0 && tid == 0) a.ws_dtot[(int64_t(s) * a.n_segs + seg) * H + hd] = run;
 
-    // ---- h^T -> the segment's workspace entry (or the slot if not split)
-    if (wave_ok) {
-        float *dst = split ? ws_head : st_head;
+    // ---- the sequence's end state after its last segment
+    if (seg == last && wave_ok) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             __builtin_nontemporal_store(f4{hacc[nt][0], hacc[nt][1], hacc[nt][2], hacc[nt][3]},
-                                        reinterpret_cast<f4 *>(dst + int64_t(p0 + tl) * N + 16 * nt + 4 * kq));
+                                        reinterpret_cast<f4 *>(st_head + int64_t(p0 + tl) * N + 16 * nt + 4 * kq));
     }
 }
 

@@ -205,6 +205,8 @@ struct SegPlan {
 constexpr int64_t kTargetWaves = 4096;
 constexpr int64_t kSsdTargetWaves = 2048;  // matrix-core segment scans
 constexpr int kMinSegTokens = 256;
+constexpr int kSsdStateGroup = 32;         // tokens per operand group of the state pass
+constexpr int kSsdStateSplit128 = 1;       // N = 128: workgroups per state-column range
 
 // The chunked matrix-core segment scan covers N in {32, 64, 128} with whole
 // 16-row tiles, on the vector path (16-byte aligned arrays).
@@ -263,8 +265,10 @@ WsLayout ws_layout(const ssm_scan_dims *d, int32_t n_seqs, int32_t n_tokens, int
 
 // Shared body of every scan once the arguments are known valid.  With
 // plan.n_segs > 1, `ws` (256-byte aligned, ws_layout() bytes) receives the
-// segment end states, their total and running decays, and three kernels run:
-// segment scans, the combine pass and the corrections.
+// segment end states and their total (and, for the register path, running)
+// decays, and three kernels run: on the matrix-core path the segment state
+// pass, the combine pass and the segment scans from the carried-in states;
+// otherwise the segment scans, the combine pass and the corrections.
 int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_seqs,
                 int32_t n_tokens, const int32_t *cu_seqlens, const int32_t *slot,
                 const uint8_t *fresh, const float *x, const float *dt, const float *A,
@@ -322,30 +326,7 @@ int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_
     a.ws_state = reinterpret_cast<float *>(ws + w.state);
     a.ws_dtot = reinterpret_cast<float *>(ws + w.dtot);
     a.ws_dcum = reinterpret_cast<float *>(ws + w.dcum);
-    int rc = SSM_OK;
-    if (ssd_eligible(d, vec)) {
-        // the segment scans in chunked matrix form on the matrix cores
-        ScanArgs sa = a;
-        sa.n_row_blocks = (d->head_dim + 63) / 64;
-        const int64_t nb = int64_t(n_seqs) * plan.n_segs * d->n_heads * sa.n_row_blocks;
-        if (nb > INT32_MAX) return SSM_ERR_UNSUPPORTED;
-        sa.n_blocks = int32_t(nb);
-        const int nt = d->d_state / 16;
-        const void *kern = nt == 2 ? reinterpret_cast<const void *>(&ssm::ssd_segscan_kernel<2>)
-                         : nt == 4 ? reinterpret_cast<const void *>(&ssm::ssd_segscan_kernel<4>)
-                                   : reinterpret_cast<const void *>(&ssm::ssd_segscan_kernel<8>);
-        const int lds = (nt == 2 ? ssm::SsdShape<2>::lds_floats()
-                       : nt == 4 ? ssm::SsdShape<4>::lds_floats()
-                                 : ssm::SsdShape<8>::lds_floats()) * int(sizeof(float));
-        void *params[] = {&sa};
-        const hipError_t err = hipLaunchKernel(kern, dim3(unsigned(nb)), dim3(kThreads), params,
-                                               size_t(lds), stream);
-        if (err != hipSuccess) return hip_fail(err, SSM_ERR_LAUNCH);
-    } else {
-        rc = with_row(*row, Launch{a, vec, Kind::kSegScan, stream, 0});
-        if (rc != SSM_OK) return rc;
-    }
-    {
+    auto combine = [&](int into_slot) -> int {
         const int64_t units = int64_t(n_seqs) * d->n_heads * d->head_dim * d->d_state / (vec ? 4 : 1);
         const int64_t grid = (units + kThreads - 1) / kThreads;
         if (grid > INT32_MAX) return SSM_ERR_UNSUPPORTED;
@@ -353,11 +334,62 @@ int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_
                                : reinterpret_cast<const void *>(&ssm::combine_kernel<false>);
         ScanArgs args = a;
         int64_t n_units = units;
-        void *params[] = {&args, &n_units};
+        int slot_flag = into_slot;
+        void *params[] = {&args, &n_units, &slot_flag};
         const hipError_t err =
             hipLaunchKernel(kern, dim3(unsigned(grid)), dim3(kThreads), params, 0, stream);
-        if (err != hipSuccess) return hip_fail(err, SSM_ERR_LAUNCH);
+        return err == hipSuccess ? SSM_OK : hip_fail(err, SSM_ERR_LAUNCH);
+    };
+    if (ssd_eligible(d, vec)) {
+        // Matrix-core path: (1) the end state of every segment but the last,
+        // (2) the combine pass turns them into carried-in states, (3) every
+        // segment scanned in chunked form from its carried-in state: y final,
+        // the last segment's end state to the slot.
+        ScanArgs sa = a;
+        sa.n_row_blocks = (d->head_dim + 63) / 64;
+        const int64_t per_seg = int64_t(n_seqs) * d->n_heads * sa.n_row_blocks;
+        if (per_seg * plan.n_segs > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+        const int nt = d->d_state / 16;
+        auto pass = [&](bool states) -> int {
+            const void *kern;
+            int lds;
+            int64_t blocks = per_seg * plan.n_segs;
+            if (states) {
+                blocks = per_seg * (plan.n_segs - 1);
+                lds = 0;                         // static LDS only
+                // N = 128 splits its state columns over two workgroups
+                if (nt == 8) {
+                    kern = reinterpret_cast<const void *>(
+                        &ssm::ssd_state_kernel<8, kSsdStateSplit128, kSsdStateGroup>);
+                    blocks *= kSsdStateSplit128;
+                } else if (nt == 4) {
+                    kern = reinterpret_cast<const void *>(&ssm::ssd_state_kernel<4, 1, kSsdStateGroup>);
+                } else {
+                    kern = reinterpret_cast<const void *>(&ssm::ssd_state_kernel<2, 1, kSsdStateGroup>);
+                }
+            } else {
+                kern = nt == 2 ? reinterpret_cast<const void *>(&ssm::ssd_scan_kernel<2>)
+                     : nt == 4 ? reinterpret_cast<const void *>(&ssm::ssd_scan_kernel<4>)
+                               : reinterpret_cast<const void *>(&ssm::ssd_scan_kernel<8>);
+                lds = nt == 2 ? ssm::SsdShape<2>::lds_floats()
+                    : nt == 4 ? ssm::SsdShape<4>::lds_floats()
+                              : ssm::SsdShape<8>::lds_floats();
+            }
+            if (blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+            sa.n_blocks = int32_t(blocks);
+            void *params[] = {&sa};
+            const hipError_t err = hipLaunchKernel(kern, dim3(unsigned(blocks)), dim3(kThreads),
+                                                   params, size_t(lds) * sizeof(float), stream);
+            return err == hipSuccess ? SSM_OK : hip_fail(err, SSM_ERR_LAUNCH);
+        };
+        int rc = pass(true);
+        if (rc == SSM_OK) rc = combine(0);
+        if (rc == SSM_OK) rc = pass(false);
+        return rc;
     }
+    int rc = with_row(*row, Launch{a, vec, Kind::kSegScan, stream, 0});
+    if (rc == SSM_OK) rc = combine(1);
+    if (rc != SSM_OK) return rc;
     // Corrections: a dense contraction per segment, on the matrix cores when
     // the state rows split into float4 halves (N % 8 == 0, N <= 128).
     if (vec && d->d_state % 8 == 0 && d->d_state <= 128) {

@@ -119,10 +119,11 @@ def test_no_kernel_uses_scratch():
     scratch = [int(v) for v in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
     # 7 state-size classes x (vector, scalar) x (4 option sets x (prefill, decode)
     # + segment scan + correction) + 2 combine kernels + 6 matrix-core corrections
-    # (3 contraction lengths, masked or not) + 3 matrix-core segment scans (N 32, 64, 128);
+    # (3 contraction lengths, masked or not) + 3 x 2 matrix-core segment kernels
+    # (N 32, 64, 128; state pass and scan pass);
     # conv1d + SiLU: (vector, scalar) x (4 history lengths x (decode, prefill)
     # + 3 with snapshots); gated RMSNorm: (vector, scalar) x 6 row-length classes
-    n_scan = 7 * 2 * (4 * 2 + 2) + 2 + 6 + 3
+    n_scan = 7 * 2 * (4 * 2 + 2) + 2 + 6 + 3 * 2
     n_conv = 2 * (4 * 2 + 3)
     n_norm = 2 * 6
     # gated delta rule: 5 key-width classes x (vector, scalar) x (prefill, decode)
