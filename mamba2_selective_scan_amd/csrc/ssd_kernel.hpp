@@ -99,6 +99,34 @@ template <int E> __device__ __forceinline__ float vget(const typename VecT<E>::t
     if constexpr (E == 1) return v; else return v[e];
 }
 
+// Raw buffer loads.  A descriptor covers [base, base + bytes); a load at byte
+// offset voffset + soffset past that range returns zeros without touching
+// memory, so a window's operands need no clamping, and the per-step advance
+// goes in the scalar offset: no vector address arithmetic per load.
+constexpr int kBufferFlags = 0x00020000;   // raw (stride 0) 32-bit elements, gfx9 descriptor word 3
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const float *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, bytes, kBufferFlags);
+}
+template <int E>
+__device__ __forceinline__ typename VecT<E>::type buffer_load(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
+    using T = typename VecT<E>::type;
+    if constexpr (E == 1) {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voffset, soffset, 0));
+    } else if constexpr (E == 2) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, voffset, soffset, 0));
+    } else if constexpr (E == 4) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0));
+    } else {
+        static_assert(E == 8, "1, 2, 4 or 8 floats");
+        const auto lo = __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0);
+        const auto hi = __builtin_amdgcn_raw_buffer_load_b128(r, voffset + 16, soffset, 0);
+        T v;
+        v.lo = __builtin_bit_cast(typename VecT<4>::type, lo);
+        v.hi = __builtin_bit_cast(typename VecT<4>::type, hi);
+        return v;
+    }
+}
+
 // The state pass: the end state of every segment but a sequence's last, and
 // its total decay, with no y.  Over a window of up to kSsdWindow tokens (S_t
 // the inclusive running log-decay from the window start)
@@ -149,7 +177,6 @@ ssd_state_kernel(ScanArgs a) {
     const SegRange sr = segment_range(a, s, seg);
     if (seg >= sr.n_real - 1) return;                // the last segment needs no pass
     const int t_begin = sr.t_begin, t_end = sr.t_end; // at least one token
-    const int t_last = t_end - 1;
     const bool from_slot = seg == 0 && a.fresh[s] == 0;
 
     const int tid = threadIdx.x;
@@ -183,20 +210,22 @@ ssd_state_kernel(ScanArgs a) {
         }
     }
 
-    // operand registers of one load group: step k covers tokens 4 k + l/16
+    // operand registers of one load group: step k covers tokens 4 k + l/16.
+    // Buffer descriptors cover the window's tokens; the lane's byte offsets
+    // are fixed, the group and step advance in the scalar offset.  (A tile
+    // past P reads rows of the next head or zeros: it is never stored.)
     float xg[2][KS][2];
     fE bg[2][KS];
-    const int row1 = tile_ok[1] ? p0 + 16 : p0;      // a tile past P rereads tile 0's rows
-    const float *xrow0 = a.x + int64_t(hd) * P + min(p0, P - 16) + tl;   // + token * H * P
-    const float *xrow1 = a.x + int64_t(hd) * P + row1 + tl;
-    const float *brow = a.B + int64_t(g) * N + n_base + E * tl;          // + token * G * N
-    auto load_group = [&](int r, int t0) {
+    const int x_tok = H * P * int(sizeof(float)), b_tok = G * N * int(sizeof(float));
+    const int vo_x = (kq * H * P + hd * P + p0 + tl) * int(sizeof(float));
+    const int vo_b = (kq * G * N + g * N + n_base + E * tl) * int(sizeof(float));
+    __amdgpu_buffer_rsrc_t rx, rb;
+    auto load_group = [&](int r, int j0) {           // j0: first token of the group in the window
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-            const int tok = min(t0 + 4 * k + kq, t_last);   // in range; weight 0 past the end
-            xg[r][k][0] = xrow0[int64_t(tok) * H * P];
-            xg[r][k][1] = xrow1[int64_t(tok) * H * P];
-            bg[r][k] = *reinterpret_cast<const fE *>(brow + int64_t(tok) * G * N);
+            xg[r][k][0] = buffer_load<1>(rx, vo_x, (j0 + 4 * k) * x_tok);
+            xg[r][k][1] = buffer_load<1>(rx, vo_x + 16 * int(sizeof(float)), (j0 + 4 * k) * x_tok);
+            bg[r][k] = buffer_load<E>(rb, vo_b, (j0 + 4 * k) * b_tok);
         }
     };
     auto mma_group = [&](int r, int w0) {
@@ -215,7 +244,9 @@ ssd_state_kernel(ScanArgs a) {
     float run = 1.f;                                   // product of dA over the segment
     for (int tw = t_begin; tw < t_end; tw += kSsdWindow) {
         const int m = min(kSsdWindow, t_end - tw);
-        if (tile_ok[0]) load_group(0, tw);             // first operands in flight during the prologue
+        rx = buffer_of(a.x + int64_t(tw) * H * P, m * x_tok);
+        rb = buffer_of(a.B + int64_t(tw) * G * N, m * b_tok);
+        if (tile_ok[0]) load_group(0, 0);              // first operands in flight during the prologue
         // ---- prologue: w_t = e^{S_last - S_t} dt_t for the window's tokens.  The
         // exponent is summed from the window end backwards (thread 0 takes the
         // last tokens), so it is exact to rounding of its own size where the
@@ -257,10 +288,10 @@ ssd_state_kernel(ScanArgs a) {
                 for (int e = 0; e < E; ++e) hacc[t][e] *= e_tot;
             const int n_pairs = (m + 2 * IT - 1) / (2 * IT);
             for (int q = 0; q < 2 * n_pairs; q += 2) {
-                load_group(1, tw + (q + 1) * IT);
+                load_group(1, (q + 1) * IT);
                 __builtin_amdgcn_sched_barrier(0);
                 mma_group(0, q * IT);
-                load_group(0, tw + (q + 2) * IT);
+                load_group(0, (q + 2) * IT);
                 __builtin_amdgcn_sched_barrier(0);
                 mma_group(1, (q + 1) * IT);
             }

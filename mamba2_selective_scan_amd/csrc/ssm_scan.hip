@@ -212,7 +212,11 @@ constexpr int kSsdStateSplit128 = 1;       // N = 128: workgroups per state-colu
 // 16-row tiles, on the vector path (16-byte aligned arrays).
 bool ssd_shape(const ssm_scan_dims *d) {
     const int N = d->d_state;
-    return (N == 32 || N == 64 || N == 128) && d->head_dim % 16 == 0;
+    // a window of tokens' x and B must fit 32-bit buffer offsets
+    const int64_t span = int64_t(ssm::kSsdWindow + 64) * int64_t(sizeof(float));
+    return (N == 32 || N == 64 || N == 128) && d->head_dim % 16 == 0 &&
+           int64_t(d->n_heads) * d->head_dim * span < INT32_MAX &&
+           int64_t(d->n_groups) * N * span < INT32_MAX;
 }
 bool ssd_eligible(const ssm_scan_dims *d, bool vec) { return vec && ssd_shape(d); }
 
