@@ -58,8 +58,10 @@ struct SsdShape {
     static constexpr int OFF_DT = OFF_S + CT;       // dt_t (0 past the segment)
     static constexpr int OFF_ES = OFF_DT + CT;      // e^{S_t}
     static constexpr int OFF_W = OFF_ES + CT;       // e^{S_15 - S_t} dt_t
-    static constexpr int OFF_E15 = OFF_W + CT;      // e^{S_15}
-    static constexpr int BUF = ((OFF_E15 + 1) + 3) / 4 * 4;
+    static constexpr int OFF_E15 = OFF_W + CT;      // e^{S_15} (exact chunks), else 1
+    static constexpr int OFF_PRE = OFF_E15 + 1;     // factor the state takes before the chunk
+    static constexpr int OFF_MODE = OFF_PRE + 1;    // 1: deferred-decay chunk, 0: exact chunk
+    static constexpr int BUF = ((OFF_MODE + 1) + 3) / 4 * 4;
     static constexpr int U_BC = (CT * N / 4 + kThreads - 1) / kThreads;    // float4 units of B (and of C)
     static constexpr int U_X = (CT * RBW / 4 + kThreads - 1) / kThreads;   // float4 units of x
     static constexpr int OFF_GX = 2 * BUF;          // G^T partials [4 waves][64 lanes][4]
@@ -146,6 +148,8 @@ __device__ __forceinline__ typename VecT<E>::type buffer_load(__amdgpu_buffer_rs
 // sequence starts from the slot, the others from zero.  Grid: n_seqs x
 // (n_segs - 1) x H x ceil(P / 64) x NS workgroups, XCD-contiguous order.
 constexpr int kSsdWindow = 512;          // tokens whose weights one pass of the prologue forms
+constexpr float kSsdFastDecay = 40.f;    // a scan chunk decaying less than e^-40 runs deferred
+constexpr float kSsdFloor = 0x1p-30f;    // the deferred factor is folded in before passing this
 template <int NT, int NS, int IT>        // N = 16 NT; NS column parts; IT tokens per load group
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 4)))
 ssd_state_kernel(ScanArgs a) {
@@ -378,40 +382,59 @@ ssd_scan_kernel(ScanArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0);
 
-    // ---- chunk staging: global -> registers -> LDS (double-buffered)
+    // ---- chunk staging: buffer loads -> registers -> LDS (double-buffered).
+    // Each thread's byte offsets into a chunk are fixed; a chunk's descriptors
+    // cover its tokens only, so the units past the segment end read zeros.
+    constexpr int kNone = 0x7ffffff0;                // an offset past every descriptor
+    const int x_tok = H * P * int(sizeof(float));
+    int vo_bc[S::U_BC], lo_bc[S::U_BC], vo_x[S::U_X];
+#pragma unroll
+    for (int u = 0; u < S::U_BC; ++u) {
+        const int q = u * kThreads + tid;            // unit = (token, 4-group)
+        const int tt = q / (N / 4), n0 = 4 * (q - tt * (N / 4));
+        vo_bc[u] = q < CT * N / 4 ? ((tt * G + g) * N + n0) * int(sizeof(float)) : kNone;
+        lo_bc[u] = q < CT * N / 4 ? tt * LDN + n0 : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < S::U_X; ++u) {
+        const int q = u * kThreads + tid;            // unit = (token, 4 rows); rows past P unused
+        const int tt = q / (S::RBW / 4), pi = 4 * (q - tt * (S::RBW / 4));
+        vo_x[u] = q < CT * S::RBW / 4 ? (tt * H * P + hd * P + prow0 + pi) * int(sizeof(float)) : kNone;
+    }
+    const int vo_dt = tid < CT ? (tid * H + hd) * int(sizeof(float)) : kNone;
     f4 pb[S::U_BC], pc[S::U_BC], px[S::U_X];
     float pdt = 0.f;
     auto issue_loads = [&](int t0, int nt_) {
+        const __amdgpu_buffer_rsrc_t rb = buffer_of(a.B + int64_t(t0) * G * N, nt_ * G * N * int(sizeof(float)));
+        const __amdgpu_buffer_rsrc_t rc = buffer_of(a.C + int64_t(t0) * G * N, nt_ * G * N * int(sizeof(float)));
+        const __amdgpu_buffer_rsrc_t rx = buffer_of(a.x + int64_t(t0) * H * P, nt_ * x_tok);
+        const __amdgpu_buffer_rsrc_t rd = buffer_of(a.dt + int64_t(t0) * H, nt_ * H * int(sizeof(float)));
 #pragma unroll
         for (int u = 0; u < S::U_BC; ++u) {
-            const int q = u * kThreads + tid;                 // unit = (token, 4-group)
-            const int tt = q / (N / 4);
-            const int n0 = 4 * (q - tt * (N / 4));
-            const bool ok = (q < CT * N / 4) && (tt < nt_);
-            const int64_t off = (int64_t(t0 + tt) * G + g) * N + n0;
-            pb[u] = load4<true>(a.B + off, ok ? 4 : 0);
-            pc[u] = load4<true>(a.C + off, ok ? 4 : 0);
+            pb[u] = buffer_load<4>(rb, vo_bc[u], 0);
+            pc[u] = buffer_load<4>(rc, vo_bc[u], 0);
         }
 #pragma unroll
-        for (int u = 0; u < S::U_X; ++u) {
-            const int q = u * kThreads + tid;                 // unit = (token, 4 rows)
-            const int tt = q / (S::RBW / 4);
-            const int pi = 4 * (q - tt * (S::RBW / 4));
-            const bool ok = (q < CT * S::RBW / 4) && (tt < nt_) && (prow0 + pi < P);
-            px[u] = load4<true>(a.x + (int64_t(t0 + tt) * H + hd) * P + prow0 + pi, ok ? 4 : 0);
-        }
-        pdt = (tid < nt_) ? a.dt[int64_t(t0 + tid) * H + hd] : 0.f;   // transformed at the commit
+        for (int u = 0; u < S::U_X; ++u) px[u] = buffer_load<4>(rx, vo_x[u], 0);
+        pdt = buffer_load<1>(rd, vo_dt, 0);         // raw dt: transformed at the commit
     };
+    // Deferred decay: the accumulators hold h / sigma.  A chunk whose decay
+    // stays within e^{-kSsdFastDecay} runs in "deferred" form: the state is not
+    // rescaled, the update's weights are e^{-S_s} dt_s / sigma and sigma takes
+    // the chunk's decay; once sigma would fall below kSsdFloor the state first
+    // takes sigma (renormalised, sigma = 1).  A chunk that decays further runs
+    // the exact form (the state renormalised first, then scaled by e^{S_15}).
+    // In the deferred form the masked intra-chunk term factorises,
+    //     e^{S_t - S_s} dt_s = e^{S_t} sigma * (e^{-S_s} dt_s / sigma),
+    // so one weighted x serves both products and y takes e^{S_t} sigma per row.
+    float sigma = 1.f;                               // wave 0's copy is the one used
     auto commit = [&](int buf, int nt_) {
         float *base = lds + buf * S::BUF;
 #pragma unroll
         for (int u = 0; u < S::U_BC; ++u) {
-            const int q = u * kThreads + tid;
-            if (q < CT * N / 4) {
-                const int tt = q / (N / 4);
-                const int n0 = 4 * (q - tt * (N / 4));
-                *reinterpret_cast<f4 *>(base + S::OFF_B + tt * LDN + n0) = pb[u];
-                *reinterpret_cast<f4 *>(base + S::OFF_C + tt * LDN + n0) = pc[u];
+            if (lo_bc[u] >= 0) {
+                *reinterpret_cast<f4 *>(base + S::OFF_B + lo_bc[u]) = pb[u];
+                *reinterpret_cast<f4 *>(base + S::OFF_C + lo_bc[u]) = pc[u];
             }
         }
 #pragma unroll
@@ -425,43 +448,43 @@ ssd_scan_kernel(ScanArgs a) {
             const float Sv = row_prefix_sum(dtv * A_h);
             const float S15 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Sv), 15));
             const float e15 = expf(S15);
-            if (tid < CT) {
-                base[S::OFF_S + tid] = Sv;
-                base[S::OFF_DT + tid] = dtv;
-                base[S::OFF_ES + tid] = expf(Sv);
-                base[S::OFF_W + tid] = expf(S15 - Sv) * dtv;
+            const bool fast = S15 >= -kSsdFastDecay;
+            float pre = 1.f;
+            if (!fast || sigma * e15 < kSsdFloor) {      // renormalise before the chunk
+                pre = sigma;
+                sigma = 1.f;
             }
-            if (tid == 0) base[S::OFF_E15] = e15;
+            if (tid < CT) {
+                if (fast) {
+                    base[S::OFF_W + tid] = __expf(-Sv) * dtv / sigma;
+                    base[S::OFF_ES + tid] = __expf(Sv) * sigma;
+                } else {
+                    base[S::OFF_S + tid] = Sv;
+                    base[S::OFF_DT + tid] = dtv;
+                    base[S::OFF_ES + tid] = expf(Sv);
+                    base[S::OFF_W + tid] = expf(S15 - Sv) * dtv;
+                }
+            }
+            if (tid == 0) {
+                base[S::OFF_E15] = fast ? 1.f : e15;
+                base[S::OFF_PRE] = pre;
+                base[S::OFF_MODE] = fast ? 1.f : 0.f;
+            }
+            sigma = fast ? sigma * e15 : 1.f;
         }
     };
 
-    // h^T = e^{S_15} h^T + B^T (w X): tile nt, step q, lane l: A = B[4(l/16)+q][16 nt + l%16],
-    // B operand = w_s x[s][p] with s = 4(l/16) + q
-    auto update_state = [&](const float *base, const float (&bup)[4][NT], const float (&xr)[4]) {
-        float wx[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) wx[q] = base[S::OFF_W + 4 * kq + q] * xr[q];
-        const float e15 = base[S::OFF_E15];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) hacc[nt] *= e15;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) hacc[nt] = mfma16(bup[q][nt], wx[q], hacc[nt]);
-        }
-    };
-
-    // y of the chunk just computed: stored after the next chunk's commit, so
-    // that commit waits only on loads and the stores drain during the next
-    // chunk's products
+    // y of the chunk just computed: stored after the next chunk's commit (so
+    // that commit waits only on loads; the stores drain during the next
+    // chunk's products), through a descriptor covering the chunk's tokens
     f4m ypend = {0.f, 0.f, 0.f, 0.f};
+    const int vo_y = ((4 * kq) * H * P + hd * P + p0 + tl) * int(sizeof(float));
     auto store_y = [&](int t0, int nt_) {
         if (!wave_ok) return;
-        float *const yrow = a.y + (int64_t(t0 + 4 * kq) * H + hd) * P + p0 + tl;
-        const int64_t ystep = int64_t(H) * P;
+        const __amdgpu_buffer_rsrc_t ry = buffer_of(a.y + int64_t(t0) * H * P, nt_ * x_tok);
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-            if (4 * kq + v < nt_) yrow[v * ystep] = ypend[v];
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ypend[v]), ry, vo_y, v * x_tok, 0);
     };
     auto compute = [&](int buf) {
         const float *base = lds + buf * S::BUF;
@@ -498,21 +521,13 @@ ssd_scan_kernel(ScanArgs a) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
                 bup[q][nt] = base[S::OFF_B + (4 * kq + q) * LDN + 16 * nt + tl];
-        // per-lane scalars: own token t = l%16; rows s = 4(l/16) + v
-        const float S_t = base[S::OFF_S + tl];
-        float Ss[4], dts[4], eSr[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int sv = 4 * kq + v;
-            Ss[v] = base[S::OFF_S + sv];
-            dts[v] = base[S::OFF_DT + sv];
-            eSr[v] = base[S::OFF_ES + sv];
-        }
         // C rows of token l%16 for Y = C h^T, n = 16 nt + 4 (l/16) + v
         f4 creg[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             creg[nt] = *reinterpret_cast<const f4 *>(base + S::OFF_C + tl * LDN + 16 * nt + 4 * kq);
+        const float pre = base[S::OFF_PRE];
+        const bool fast = base[S::OFF_MODE] != 0.f;
         // keep every operand read issued ahead of the products (the scheduler
         // would otherwise reuse a few registers and wait on each group)
         __builtin_amdgcn_sched_barrier(0);
@@ -522,6 +537,10 @@ ssd_scan_kernel(ScanArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         f4m yacc = {0.f, 0.f, 0.f, 0.f};
         if (wave_ok) {
+            if (pre != 1.f) {                            // renormalise the deferred state
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) hacc[nt] *= pre;
+            }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 yacc = mfma16(creg[nt].x, hacc[nt][0], yacc);
@@ -535,20 +554,43 @@ ssd_scan_kernel(ScanArgs a) {
         f4m gacc = reinterpret_cast<const f4m *>(lds + S::OFF_GX)[lane];
 #pragma unroll
         for (int k = 1; k < kWaves; ++k) gacc += reinterpret_cast<const f4m *>(lds + S::OFF_GX)[k * 64 + lane];
-        // G'^T[s][t] = G^T[s][t] e^{S_t - S_s} dt_s for s <= t, else 0
-        // (lane l, register v: s = 4(l/16) + v, t = l%16); Y rows t = 4(l/16) + v
-        // take the carried-in state's decay e^{S_t}
+        // gacc register v of lane l: G^T[s][t] with s = 4(l/16) + v, t = l%16;
+        // yacc register v: row t = 4(l/16) + v
+        float wx[4];
+        if (fast) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int sv = 4 * kq + v;
-            gacc[v] = (sv <= tl) ? gacc[v] * __expf(S_t - Ss[v]) * dts[v] : 0.f;
-            yacc[v] *= eSr[v];
+            for (int v = 0; v < 4; ++v) {
+                wx[v] = base[S::OFF_W + 4 * kq + v] * xr[v];
+                gacc[v] = (4 * kq + v <= tl) ? gacc[v] : 0.f;
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) yacc = mfma16(gacc[v], wx[v], yacc);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) yacc[v] *= base[S::OFF_ES + 4 * kq + v];
+        } else {
+            const float S_t = base[S::OFF_S + tl];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int sv = 4 * kq + v;
+                gacc[v] = (sv <= tl) ? gacc[v] * __expf(S_t - base[S::OFF_S + sv]) * base[S::OFF_DT + sv] : 0.f;
+                yacc[v] *= base[S::OFF_ES + sv];
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) yacc = mfma16(gacc[v], xr[v], yacc);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) wx[v] = base[S::OFF_W + 4 * kq + v] * xr[v];
+            const float e15 = base[S::OFF_E15];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) hacc[nt] *= e15;
         }
-        // Y += G' X
-#pragma unroll
-        for (int v = 0; v < 4; ++v) yacc = mfma16(gacc[v], xr[v], yacc);
         ypend = yacc;                                    // stored after the next commit
-        update_state(base, bup, xr);
+        // h^T += B^T (w X): tile nt, step q, lane l: A = B[4(l/16)+q][16 nt + l%16],
+        // B operand = the weighted x of token s = 4(l/16) + q
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) hacc[nt] = mfma16(bup[q][nt], wx[q], hacc[nt]);
+        }
     };
 
     const int n_chunks = (n_tok + CT - 1) / CT;
@@ -569,12 +611,18 @@ ssd_scan_kernel(ScanArgs a) {
         __syncthreads();
     }
 
-    // ---- the sequence's end state after its last segment
-    if (seg == last && wave_ok) {
+    // ---- the sequence's end state after its last segment: h = sigma * accumulators
+    if (seg == last) {
+        float *const sig_lds = lds + S::OFF_GX;          // free after the last barrier
+        if (tid == 0) sig_lds[0] = sigma;
+        __syncthreads();
+        const float sg = sig_lds[0];
+        if (wave_ok) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-            __builtin_nontemporal_store(f4{hacc[nt][0], hacc[nt][1], hacc[nt][2], hacc[nt][3]},
-                                        reinterpret_cast<f4 *>(st_head + int64_t(p0 + tl) * N + 16 * nt + 4 * kq));
+            for (int nt = 0; nt < NT; ++nt)
+                __builtin_nontemporal_store(f4{hacc[nt][0] * sg, hacc[nt][1] * sg, hacc[nt][2] * sg, hacc[nt][3] * sg},
+                                            reinterpret_cast<f4 *>(st_head + int64_t(p0 + tl) * N + 16 * nt + 4 * kq));
+        }
     }
 }
 

@@ -267,6 +267,41 @@ def test_split_prefill_headline(ssm, orc):
         assert_parity(case, y, st, y64, st64, label=f"split 1x4096 fresh={fresh} vs fp64")
 
 
+def decay_regimes_case():
+    """16 heads in four decay regimes over two long sequences (one resumed):
+    almost none (the deferred factor never needs folding in), moderate (it
+    is folded in every few chunks), steep (every 16-token chunk decays past
+    e^-40 and runs the exact form) and bursts (large dt on a few tokens, so
+    the two forms alternate)."""
+    import dataclasses
+    case = ssm_inputs.make_case(16, 32, 128, 2, [700, 333], [1, 0], seed=41)
+    rng = np.random.Generator(np.random.PCG64(4141))
+    A = case.A.copy()
+    dt = case.dt.copy()
+    T = dt.shape[0]
+    A[0:4], dt[:, 0:4] = -0.01, 0.05
+    A[4:8], dt[:, 4:8] = -2.0, rng.uniform(0.05, 0.5, size=(T, 4))
+    A[8:12], dt[:, 8:12] = -16.0, rng.uniform(0.3, 1.0, size=(T, 4))
+    A[12:16] = -4.0
+    dt[:, 12:16] = np.where(rng.uniform(size=(T, 4)) < 0.05, 3.0, 0.01)
+    return dataclasses.replace(case, A=A.astype(np.float32), dt=dt.astype(np.float32),
+                               name="decay_regimes")
+
+
+@pytest.mark.parametrize("segments", [0, 3])
+def test_split_prefill_decay_regimes(ssm, orc, segments):
+    case = decay_regimes_case()
+    say(f"decay regimes, segments={segments}: "
+        f"{ssm.prefill_plan(case.H, case.P, case.N, case.G, 2, 700, segments)}")
+    y, st = run_gpu(case, "prefill_ws", segments=segments)
+    # Pinned to the fp64 oracle: over 700 barely decaying tokens the fp32
+    # oracle's own sequential rounding exceeds the bar (printed below).
+    y64, st64 = orc.scan_case(case, precision="f64")
+    y32, _ = orc.scan_case(case, precision="f32")
+    say(f"  (fp32 oracle vs fp64: max rel err y={rel_err(y32, y64):.3e})")
+    assert_parity(case, y, st, y64, st64, label=f"decay regimes segments={segments} vs fp64")
+
+
 @pytest.mark.parametrize("segments", [2, 3, 7])
 @pytest.mark.parametrize("max_seqlen", [150, 40])
 def test_split_prefill_mixed_batch(ssm, orc, segments, max_seqlen):
