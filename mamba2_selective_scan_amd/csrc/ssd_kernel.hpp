@@ -428,7 +428,8 @@ ssd_scan_kernel(ScanArgs a) {
     //     e^{S_t - S_s} dt_s = e^{S_t} sigma * (e^{-S_s} dt_s / sigma),
     // so one weighted x serves both products and y takes e^{S_t} sigma per row.
     float sigma = 1.f;                               // wave 0's copy is the one used
-    auto commit = [&](int buf, int nt_) {
+    auto commit = [&](auto bufc, int nt_) {
+        constexpr int buf = decltype(bufc)::value;
         float *base = lds + buf * S::BUF;
 #pragma unroll
         for (int u = 0; u < S::U_BC; ++u) {
@@ -486,7 +487,8 @@ ssd_scan_kernel(ScanArgs a) {
         for (int v = 0; v < 4; ++v)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ypend[v]), ry, vo_y, v * x_tok, 0);
     };
-    auto compute = [&](int buf) {
+    auto compute = [&](auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
         const float *base = lds + buf * S::BUF;
         // G^T = B C^T is the same for the four waves: each forms the part over
         // its quarter of the contraction index n (NT of the 4 NT steps) and the
@@ -579,11 +581,15 @@ ssd_scan_kernel(ScanArgs a) {
             for (int v = 0; v < 4; ++v) yacc = mfma16(gacc[v], xr[v], yacc);
 #pragma unroll
             for (int v = 0; v < 4; ++v) wx[v] = base[S::OFF_W + 4 * kq + v] * xr[v];
-            const float e15 = base[S::OFF_E15];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) hacc[nt] *= e15;
         }
         ypend = yacc;                                    // stored after the next commit
+        // an exact chunk scales the state by e^{S_15} before its update (kept
+        // out of the branches above so the state stays in place in both)
+        const float mid = base[S::OFF_E15];
+        if (mid != 1.f) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) hacc[nt] *= mid;
+        }
         // h^T += B^T (w X): tile nt, step q, lane l: A = B[4(l/16)+q][16 nt + l%16],
         // B operand = the weighted x of token s = 4(l/16) + q
 #pragma unroll
@@ -593,22 +599,30 @@ ssd_scan_kernel(ScanArgs a) {
         }
     };
 
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
     const int n_chunks = (n_tok + CT - 1) / CT;
     if (n_chunks > 0) {
         issue_loads(t_begin, min(CT, n_tok));
-        commit(0, min(CT, n_tok));
+        commit(B0{}, min(CT, n_tok));
     }
     __syncthreads();
-    for (int c = 0; c < n_chunks; ++c) {
-        const int buf = c & 1;
+    // chunk c in LDS buffer c & 1; unrolled by two so each buffer's LDS
+    // addresses are compile-time offsets
+    auto step = [&](int c, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
         const int t0 = t_begin + c * CT;
         const int nt_ = min(CT, t_end - t0);
         const bool has_next = c + 1 < n_chunks;
         if (has_next) issue_loads(t0 + CT, min(CT, t_end - t0 - CT));
-        compute(buf);
-        if (has_next) commit(buf ^ 1, min(CT, t_end - t0 - CT));
+        compute(bufc);
+        if (has_next) commit(std::integral_constant<int, buf ^ 1>{}, min(CT, t_end - t0 - CT));
         store_y(t0, nt_);
         __syncthreads();
+    };
+    for (int c = 0; c < n_chunks; c += 2) {
+        step(c, B0{});
+        if (c + 1 < n_chunks) step(c + 1, B1{});
     }
 
     // ---- the sequence's end state after its last segment: h = sigma * accumulators
