@@ -95,17 +95,27 @@ int launch(const ScanArgs &a, hipStream_t stream) {
     return err == hipSuccess ? SSM_OK : hip_fail(err, SSM_ERR_LAUNCH);
 }
 
-// Calls f.template run<R, J, CT, DR, DJ>() for the table row (its compile-time shapes).
+// Calls f.template run<R, J, CT, DR, DJ>() for the table row: the compile-time
+// shapes are read from kShapes itself, so the kernels and the host geometry
+// (geo_for) cannot disagree.
+template <int IDX, class F>
+int run_row(F &&f) {
+    constexpr ShapeRow r = kShapes[IDX];
+    return f.template run<r.R, r.J, r.CT, r.DR, r.DJ>();
+}
 template <class F>
 int with_row(const ShapeRow &row, F &&f) {
-    switch (row.n_max) {
-    case 16: return f.template run<4, 1, 32, 4, 1>();
-    case 32: return f.template run<8, 1, 32, 8, 1>();
-    case 64: return f.template run<16, 1, 32, 16, 1>();
-    case 128: return f.template run<16, 2, 32, 8, 4>();
-    case 256: return f.template run<16, 4, 16, 16, 4>();
-    case 512: return f.template run<32, 4, 8, 32, 4>();
-    case 1024: return f.template run<64, 4, 4, 64, 4>();
+    constexpr int n_rows = int(sizeof(kShapes) / sizeof(kShapes[0]));
+    static_assert(n_rows == 7, "one case per table row below");
+    const int idx = int(&row - kShapes);
+    switch (idx) {
+    case 0: return run_row<0>(f);
+    case 1: return run_row<1>(f);
+    case 2: return run_row<2>(f);
+    case 3: return run_row<3>(f);
+    case 4: return run_row<4>(f);
+    case 5: return run_row<5>(f);
+    case 6: return run_row<6>(f);
     default: return SSM_ERR_UNSUPPORTED;
     }
 }
