@@ -90,6 +90,17 @@ def load_traffic(name):
     return t.get("bytes_per_launch")
 
 
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def host_cores():
     try:
         return len(os.sched_getaffinity(0))
@@ -116,7 +127,7 @@ def cpu_baseline_decode(case, seconds):
     n, el = rate(threads, seconds)
     n1, el1 = rate(1, max(1.0, seconds / 3))
     return {"value": round(el / n * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle",
-            "value_1_thread": round(el1 / n1 * 1e6, 1),
+            "value_1_thread": round(el1 / n1 * 1e6, 1), "cpu_model": host_cpu_model(),
             "sample": f"{n} repetitions of the full decode 16x1 step (16 seqs x 64 heads x 64 "
                       f"rows x 128 state, fp32, resuming) on {threads} threads, {el:.1f} s; "
                       f"{n1} on 1 thread, {el1:.1f} s"}
