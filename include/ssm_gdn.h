@@ -75,6 +75,46 @@ int ssm_gdn_prefill(const ssm_gdn_dims *dims, int32_t n_seqs, int32_t n_tokens,
                     float *snapshots, void *stream);
 
 /*
+ * The same recurrence over a packed batch, with the prefill of long sequences
+ * in chunked matrix form on the matrix cores.  Over a chunk of 16 tokens the
+ * per-token updates regroup into dense products ("ssm_gated_delta.cu" runs
+ * them one token at a time; the regrouping is exact in real arithmetic, so
+ * results agree with ssm_gdn_prefill to rounding):
+ *     Delta = T diag(beta) (V - diag(gamma) K S0^T),  T = (I + A)^-1,
+ *     A[t][s] = beta_t (gamma_t / gamma_s) (k_t . k_s) for s < t,
+ *     y = scale (diag(gamma) Q S0^T + M Delta),  S' = gamma_15 S0 + Delta^T diag(gamma_15/gamma) K,
+ * with gamma the running product of exp(g) from the chunk start and M the
+ * decayed q . k for s <= t.  Two kernels on `stream`: per (sequence, chunk, key
+ * head) T, M and the weights go to the workspace; then the chunks are scanned.
+ *   max_seqlen  host int >= every sequence's length (precondition: chunks past
+ *               ceil(max_seqlen/16) are not run, and no memory outside the
+ *               arrays and the workspace is touched)
+ *   workspace   DEVICE memory of at least ssm_gdn_prefill_workspace_size()
+ *               bytes, 16-byte aligned, owned by the caller; its contents are
+ *               scratch between calls.  Two calls in flight at once need two.
+ * The chunked form runs for Dk in {64, 128}, Dv a multiple of 16, max_seqlen
+ * >= 32 and 16-byte aligned float arrays; otherwise (and then the workspace
+ * may be NULL) this is ssm_gdn_prefill without snapshots.  Errors as for
+ * ssm_gdn_prefill, plus SSM_ERR_NULL for a missing workspace the chunked form
+ * needs, SSM_ERR_DIMS for max_seqlen < 0 or a workspace below the size.
+ */
+int ssm_gdn_prefill_ws(const ssm_gdn_dims *dims, int32_t n_seqs, int32_t n_tokens,
+                       const int32_t *cu_seqlens, const int32_t *slot, const uint8_t *fresh,
+                       const float *q, const float *k, const float *v, const float *g,
+                       const float *beta, float scale, float *state, int32_t n_slots, float *y,
+                       int32_t max_seqlen, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * Bytes of workspace ssm_gdn_prefill_ws needs for n_seqs sequences of at most
+ * max_seqlen tokens (0 when it would not use the chunked form).  Host only.
+ * Errors: SSM_ERR_NULL, SSM_ERR_DIMS (sizes as for ssm_gdn_prefill, n_seqs or
+ * max_seqlen < 0).
+ */
+int ssm_gdn_prefill_workspace_size(const ssm_gdn_dims *dims, int32_t n_seqs, int32_t max_seqlen,
+                                   size_t *bytes);
+
+/*
  * One token for each of n_seqs sequences (fc_ssm_recurrence_slots): the same
  * as ssm_gdn_prefill with every length 1 and no cu_seqlens; the token arrays
  * are indexed by sequence.

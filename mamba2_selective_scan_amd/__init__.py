@@ -139,6 +139,13 @@ MAX_GDN_DK = 256
 _lib.ssm_gdn_prefill.argtypes = ([ctypes.POINTER(GdnDims), _i32, _i32] + [_vp] * 8
                                  + [ctypes.c_float, _vp, _i32, _vp, _vp, _vp])
 _lib.ssm_gdn_prefill.restype = ctypes.c_int
+_lib.ssm_gdn_prefill_ws.argtypes = ([ctypes.POINTER(GdnDims), _i32, _i32] + [_vp] * 8
+                                    + [ctypes.c_float, _vp, _i32, _vp, _i32, _vp, ctypes.c_size_t,
+                                       _vp])
+_lib.ssm_gdn_prefill_ws.restype = ctypes.c_int
+_lib.ssm_gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(GdnDims), _i32, _i32,
+                                                ctypes.POINTER(ctypes.c_size_t)]
+_lib.ssm_gdn_prefill_workspace_size.restype = ctypes.c_int
 _lib.ssm_gdn_decode.argtypes = ([ctypes.POINTER(GdnDims), _i32] + [_vp] * 7
                                 + [ctypes.c_float, _vp, _i32, _vp, _vp, _vp])
 _lib.ssm_gdn_decode.restype = ctypes.c_int
@@ -515,6 +522,49 @@ def gdn_prefill(q, k, v, g, beta, state, cu_seqlens, slot, fresh, scale=None, y=
                               _dev_ptr(snapshots, torch.float32, "snapshots", dev),
                               _stream_handle(stream, dev))
     _check(rc, "ssm_gdn_prefill")
+    return y
+
+
+def gdn_workspace_size(Hv, Hk, Dk, Dv, n_seqs, max_seqlen) -> int:
+    """Bytes of device workspace ``gdn_prefill_ws`` needs (0: it would run the
+    per-token kernel)."""
+    b = ctypes.c_size_t()
+    _check(_lib.ssm_gdn_prefill_workspace_size(ctypes.byref(GdnDims(Hv, Hk, Dk, Dv)), int(n_seqs),
+                                               int(max_seqlen), ctypes.byref(b)),
+           "ssm_gdn_prefill_workspace_size")
+    return int(b.value)
+
+
+def gdn_prefill_ws(q, k, v, g, beta, state, cu_seqlens, slot, fresh, max_seqlen, scale=None,
+                   y=None, workspace=None, stream=None):
+    """``ssm_gdn_prefill_ws``: the recurrence with long sequences in chunked
+    matrix form.  ``max_seqlen`` (host int) bounds every length;
+    ``workspace`` (a uint8 CUDA tensor of at least ``gdn_workspace_size(...)``
+    bytes) is allocated here when not given.  Otherwise as ``gdn_prefill``
+    (no snapshots)."""
+    import math
+    import torch
+    T = int(v.shape[0])
+    n_seqs = int(slot.shape[0])
+    dims, n_slots, dev, y, ptrs = _gdn_args(q, k, v, g, beta, state, y, None, T)
+    if tuple(cu_seqlens.shape) != (n_seqs + 1,) or tuple(fresh.shape) != (n_seqs,):
+        raise ValueError("cu_seqlens or fresh has the wrong shape")
+    sc = 1.0 / math.sqrt(dims.d_k) if scale is None else float(scale)
+    need = gdn_workspace_size(dims.n_v_heads, dims.n_k_heads, dims.d_k, dims.d_v, n_seqs,
+                              max_seqlen)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device != dev:
+        raise ValueError("workspace must be a uint8 tensor on the device of the state")
+    rc = _lib.ssm_gdn_prefill_ws(ctypes.byref(dims), n_seqs, T,
+                                 _dev_ptr(cu_seqlens, torch.int32, "cu_seqlens", dev),
+                                 _dev_ptr(slot, torch.int32, "slot", dev),
+                                 _dev_ptr(fresh, torch.uint8, "fresh", dev), *ptrs, sc,
+                                 _dev_ptr(state, torch.float32, "state", dev), n_slots,
+                                 _dev_ptr(y, torch.float32, "y", dev), int(max_seqlen),
+                                 ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                 _stream_handle(stream, dev))
+    _check(rc, "ssm_gdn_prefill_ws")
     return y
 
 

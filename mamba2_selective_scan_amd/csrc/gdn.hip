@@ -1,7 +1,9 @@
-// gdn.hip -- the C ABI (include/ssm_gdn.h) over the gated delta-rule kernel.
+// gdn.hip -- the C ABI (include/ssm_gdn.h) over the gated delta-rule kernels.
 //
 // Host side only: validate, pick the compiled shape for the key width, enqueue
-// one launch on the caller's stream.  No allocation, no synchronisation.
+// the launches on the caller's stream (one per-token kernel, or the chunked
+// prep and scan kernels with a caller's workspace).  No allocation, no
+// synchronisation.
 #include "ssm_gdn.h"
 
 #include <hip/hip_runtime.h>
@@ -9,6 +11,7 @@
 #include <atomic>
 #include <cstdint>
 
+#include "gdn_chunk.hpp"
 #include "gdn_kernel.hpp"
 #include "status.hpp"
 
@@ -95,10 +98,45 @@ int dispatch(const GdnArgs &a, int64_t units, bool vec, bool decode, hipStream_t
     return SSM_ERR_UNSUPPORTED;
 }
 
+// The chunked matrix-core prefill: key widths 64 and 128, whole 16-row value
+// tiles, sequences of at least kGdnChunkMinLen tokens (shorter ones gain
+// nothing from chunks of 16), no snapshots, 16-byte aligned arrays.
+constexpr int kGdnChunkMinLen = 32;
+bool chunk_shape(const ssm_gdn_dims *d) {
+    return (d->d_k == 64 || d->d_k == 128) && d->d_v % 16 == 0;
+}
+size_t chunk_ws_bytes(const ssm_gdn_dims *d, int32_t n_seqs, int32_t max_seqlen) {
+    const size_t chunks = (size_t(max_seqlen) + 15) / 16;
+    return size_t(n_seqs) * chunks * size_t(d->n_v_heads) * ssm::GdnUnit::FLOATS * sizeof(float);
+}
+
+template <int NKT>
+int launch_chunked(ssm::GdnChunkArgs ca, int32_t n_seqs, hipStream_t stream) {
+    const GdnArgs &a = ca.a;
+    const int64_t prep_units = int64_t(n_seqs) * ca.max_chunks * a.Hk;
+    const int64_t scan_blocks = int64_t(n_seqs) * a.Hv * (a.Dv / 16);
+    if (prep_units > INT32_MAX - 3 || scan_blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+    ssm::GdnChunkArgs prep = ca;
+    prep.a.n_blocks = int32_t(prep_units);
+    void *pp[] = {&prep};
+    hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&ssm::gdn_chunk_prep_kernel<NKT>),
+                                     dim3(unsigned((prep_units + ssm::kWaves - 1) / ssm::kWaves)), dim3(kThreads),
+                                     pp, 0, stream);
+    if (err != hipSuccess) return ssm::hip_fail(err, SSM_ERR_LAUNCH);
+    ssm::GdnChunkArgs scan = ca;
+    scan.a.n_row_blocks = a.Dv / 16;
+    scan.a.n_blocks = int32_t(scan_blocks);
+    void *sp[] = {&scan};
+    err = hipLaunchKernel(reinterpret_cast<const void *>(&ssm::gdn_chunk_scan_kernel<NKT>),
+                          dim3(unsigned(scan_blocks)), dim3(kThreads), sp, 0, stream);
+    return err == hipSuccess ? SSM_OK : ssm::hip_fail(err, SSM_ERR_LAUNCH);
+}
+
 int gdn_common(const ssm_gdn_dims *d, int32_t n_seqs, int32_t n_tokens, const int32_t *cu,
                const int32_t *slot, const uint8_t *fresh, const float *q, const float *k,
                const float *v, const float *g, const float *beta, float scale, float *state,
-               int32_t n_slots, float *y, float *snapshots, bool decode, void *stream) {
+               int32_t n_slots, float *y, float *snapshots, bool decode, void *stream,
+               int32_t max_seqlen = 0, void *ws = nullptr, size_t ws_bytes = 0) {
     if (!d) return SSM_ERR_NULL;
     if (d->n_v_heads < 1 || d->n_k_heads < 1 || d->d_k < 1 || d->d_v < 1 || n_seqs < 0 ||
         n_tokens < 0 || d->n_v_heads % d->n_k_heads != 0)
@@ -137,6 +175,17 @@ int gdn_common(const ssm_gdn_dims *d, int32_t n_seqs, int32_t n_tokens, const in
     a.Dk = d->d_k;
     a.Dv = d->d_v;
     a.heads_per_key = d->n_v_heads / d->n_k_heads;
+    if (!decode && !snapshots && vec && chunk_shape(d) && max_seqlen >= kGdnChunkMinLen) {
+        if (!ws) return SSM_ERR_NULL;
+        if (ws_bytes < chunk_ws_bytes(d, n_seqs, max_seqlen)) return SSM_ERR_DIMS;
+        if (!aligned(ws, 16)) return SSM_ERR_ALIGN;
+        ssm::GdnChunkArgs ca{};
+        ca.a = a;
+        ca.ws = static_cast<float *>(ws);
+        ca.max_chunks = int32_t((int64_t(max_seqlen) + 15) / 16);
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        return d->d_k == 64 ? launch_chunked<4>(ca, n_seqs, st) : launch_chunked<8>(ca, n_seqs, st);
+    }
     const int64_t units = int64_t(n_seqs) * d->n_v_heads;   // times the row blocks, per shape
     return dispatch(a, units, vec, decode, static_cast<hipStream_t>(stream));
 }
@@ -152,6 +201,29 @@ int ssm_gdn_prefill(const ssm_gdn_dims *dims, int32_t n_seqs, int32_t n_tokens,
                     float *snapshots, void *stream) {
     return gdn_common(dims, n_seqs, n_tokens, cu_seqlens, slot, fresh, q, k, v, g, beta, scale,
                       state, n_slots, y, snapshots, false, stream);
+}
+
+int ssm_gdn_prefill_workspace_size(const ssm_gdn_dims *dims, int32_t n_seqs, int32_t max_seqlen,
+                                   size_t *bytes) {
+    if (!dims || !bytes) return SSM_ERR_NULL;
+    if (dims->n_v_heads < 1 || dims->n_k_heads < 1 || dims->d_k < 1 || dims->d_v < 1 ||
+        n_seqs < 0 || max_seqlen < 0 || dims->n_v_heads % dims->n_k_heads != 0)
+        return SSM_ERR_DIMS;
+    *bytes = chunk_shape(dims) && max_seqlen >= kGdnChunkMinLen
+                 ? chunk_ws_bytes(dims, n_seqs, max_seqlen) : 0;
+    return SSM_OK;
+}
+
+int ssm_gdn_prefill_ws(const ssm_gdn_dims *dims, int32_t n_seqs, int32_t n_tokens,
+                       const int32_t *cu_seqlens, const int32_t *slot, const uint8_t *fresh,
+                       const float *q, const float *k, const float *v, const float *g,
+                       const float *beta, float scale, float *state, int32_t n_slots, float *y,
+                       int32_t max_seqlen, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    if (max_seqlen < 0) return SSM_ERR_DIMS;
+    return gdn_common(dims, n_seqs, n_tokens, cu_seqlens, slot, fresh, q, k, v, g, beta, scale,
+                      state, n_slots, y, nullptr, false, stream, max_seqlen, workspace,
+                      workspace_bytes);
 }
 
 int ssm_gdn_decode(const ssm_gdn_dims *dims, int32_t n_seqs, const int32_t *slot,

@@ -166,7 +166,8 @@ def run_norm_gpu(case, device="cuda:0", offset_floats=0, eps=None):
     return out.cpu().numpy()
 
 
-def run_gdn_gpu(case, mode="prefill", device="cuda:0", offset_floats=0, snapshots=False):
+def run_gdn_gpu(case, mode="prefill", device="cuda:0", offset_floats=0, snapshots=False,
+                max_seqlen=None):
     """Run an ``ssm_inputs.GdnCase`` through the delta-rule ABI; returns (y,
     state) or (y, state, snapshots) as numpy."""
     import torch
@@ -181,6 +182,11 @@ def run_gdn_gpu(case, mode="prefill", device="cuda:0", offset_floats=0, snapshot
     if mode == "prefill":
         ssm.gdn_prefill(q, k, v, g, beta, st, put(case.cu_seqlens), slot, fresh, scale=case.scale,
                         y=y, snapshots=sn)
+    elif mode == "prefill_ws":
+        assert not snapshots
+        ms = int(case.lengths.max()) if max_seqlen is None and case.n_seqs else int(max_seqlen or 0)
+        ssm.gdn_prefill_ws(q, k, v, g, beta, st, put(case.cu_seqlens), slot, fresh, ms,
+                           scale=case.scale, y=y)
     elif mode == "decode":
         assert np.all(case.lengths == 1)
         ssm.gdn_decode(q, k, v, g, beta, st, slot, fresh, scale=case.scale, y=y, snapshots=sn)

@@ -23,7 +23,8 @@ def test_exports_every_declared_symbol():
                           "ssm_scan_prefill_workspace_size", "ssm_scan_query_prefill_plan",
                           "ssm_scan_prefill_opt", "ssm_scan_decode_opt",
                           "ssm_conv1d_silu_prefill", "ssm_conv1d_silu_decode",
-                          "ssm_gated_rmsnorm", "ssm_gdn_prefill", "ssm_gdn_decode"}
+                          "ssm_gated_rmsnorm", "ssm_gdn_prefill", "ssm_gdn_decode",
+                          "ssm_gdn_prefill_ws", "ssm_gdn_prefill_workspace_size"}
     for n in names:
         assert hasattr(m.lib(), n), n
 
@@ -128,7 +129,8 @@ def test_no_kernel_uses_scratch():
     n_norm = 2 * 6
     # gated delta rule: 5 key-width classes x (vector, scalar) x (prefill, decode)
     # x (snapshots or not)
-    n_gdn = 5 * 2 * 2 * 2
+    # + the chunked prefill: (prep, scan) x key widths 64 and 128
+    n_gdn = 5 * 2 * 2 * 2 + 2 * 2
     assert len(names) == n_scan + n_conv + n_norm + n_gdn and len(scratch) == len(names)
     assert all(v == 0 for v in scratch), dict(zip(names, scratch))
 
@@ -263,3 +265,38 @@ def test_gdn_argument_errors(decode):
     if not decode:
         assert call(ok, n_tokens=-1) == m.SSM_ERR_DIMS
         assert call(ok, ptrs={"cu": None}) == m.SSM_ERR_NULL
+
+
+def test_gdn_workspace_size():
+    size = lambda *a: m.gdn_workspace_size(*a)
+    # one unit of 592 floats per (sequence, 16-token chunk, value head)
+    assert size(32, 16, 128, 128, 1, 4096) == 256 * 32 * 592 * 4
+    assert size(4, 2, 64, 32, 3, 33) == 3 * 3 * 4 * 592 * 4
+    assert size(4, 2, 128, 64, 3, 31) == 0       # short sequences: per-token kernel
+    assert size(4, 2, 100, 64, 3, 500) == 0      # key width without a chunked form
+    assert size(4, 2, 128, 24, 3, 500) == 0      # value rows not in 16-row tiles
+    b = ctypes.c_size_t()
+    lib = m.lib()
+    assert lib.ssm_gdn_prefill_workspace_size(None, 1, 64, ctypes.byref(b)) == m.SSM_ERR_NULL
+    assert lib.ssm_gdn_prefill_workspace_size(ctypes.byref(GD(4, 2, 128, 64)), 1, 64, None) == m.SSM_ERR_NULL
+    assert lib.ssm_gdn_prefill_workspace_size(ctypes.byref(GD(4, 2, 128, 64)), -1, 64, ctypes.byref(b)) == m.SSM_ERR_DIMS
+    assert lib.ssm_gdn_prefill_workspace_size(ctypes.byref(GD(4, 2, 128, 64)), 1, -1, ctypes.byref(b)) == m.SSM_ERR_DIMS
+    assert lib.ssm_gdn_prefill_workspace_size(ctypes.byref(GD(6, 4, 128, 64)), 1, 64, ctypes.byref(b)) == m.SSM_ERR_DIMS
+
+
+def test_gdn_prefill_ws_argument_errors():
+    """Errors the chunked entry point reports before anything is enqueued."""
+    lib = m.lib()
+    d = GD(4, 2, 128, 64)
+    need = m.gdn_workspace_size(4, 2, 128, 64, 1, 64)
+
+    def call(max_seqlen=64, ws=FAKE, ws_bytes=need, dims=d, n_seqs=1):
+        return lib.ssm_gdn_prefill_ws(None if dims is None else ctypes.byref(dims), n_seqs, 64,
+                                      FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, FAKE,
+                                      1, FAKE, max_seqlen, ws, ws_bytes, None)
+    assert call(dims=None) == m.SSM_ERR_NULL
+    assert call(max_seqlen=-1) == m.SSM_ERR_DIMS
+    assert call(ws=None) == m.SSM_ERR_NULL
+    assert call(ws_bytes=need - 1) == m.SSM_ERR_DIMS
+    assert call(ws=FAKE + 4) == m.SSM_ERR_ALIGN
+    assert call(n_seqs=0) == m.SSM_OK
