@@ -254,12 +254,14 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
         xch[par][0][w][lane] = ks;
         xch[par][1][w][lane] = qs;
         __syncthreads();
+        // every wave needs all of K S0^T (for Delta); Q S0^T only the wave that writes y
         ks = xch[par][0][0][lane];
-        qs = xch[par][1][0][lane];
 #pragma unroll
-        for (int k = 1; k < kWaves; ++k) {
-            ks += xch[par][0][k][lane];
-            qs += xch[par][1][k][lane];
+        for (int k = 1; k < kWaves; ++k) ks += xch[par][0][k][lane];
+        if (w == 0) {
+            qs = xch[par][1][0][lane];
+#pragma unroll
+            for (int k = 1; k < kWaves; ++k) qs += xch[par][1][k][lane];
         }
         // register v of lane l: token t = 4 (l/16) + v, value row j0 + l%16
         const float gam[4] = {o.gam.x, o.gam.y, o.gam.z, o.gam.w};
@@ -274,10 +276,10 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
         f4m dl = {0.f, 0.f, 0.f, 0.f};                // Delta = T R
 #pragma unroll
         for (int v = 0; v < 4; ++v) dl = mfma16(tr[v], rv[v], dl);
-        f4m ym = {0.f, 0.f, 0.f, 0.f};                // M Delta
-#pragma unroll
-        for (int v = 0; v < 4; ++v) ym = mfma16(mr[v], dl[v], ym);
         if (w == 0) {
+            f4m ym = {0.f, 0.f, 0.f, 0.f};            // M Delta
+#pragma unroll
+            for (int v = 0; v < 4; ++v) ym = mfma16(mr[v], dl[v], ym);
             const int t0 = c0 + 16 * ch;
             const __amdgpu_buffer_rsrc_t ry = buffer_of(a.y + int64_t(t0) * Hv * Dv, min(16, len - 16 * ch) * v_bytes);
 #pragma unroll
@@ -296,19 +298,20 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
     };
 
     const int n_chunks = (len + 15) / 16;
-    // (scheduling barriers keep each chunk's loads ahead of the previous
-    // chunk's products; left alone the compiler sinks loads to their use)
+    // The next chunk's loads are issued before this chunk's products, always
+    // (the last chunk's again past the end), so the same number of loads is
+    // in flight on every path and a chunk waits only for its own; scheduling
+    // barriers keep them there (left alone the compiler sinks loads to their use).
     Ops o0, o1;
+    const int last = n_chunks - 1;
     if (n_chunks > 0) load(o0, 0);
     for (int ch = 0; ch < n_chunks; ch += 2) {
-        if (ch + 1 < n_chunks) load(o1, ch + 1);
+        load(o1, min(ch + 1, last));
         __builtin_amdgcn_sched_barrier(0);
         chunk_step(o0, ch, 0);
-        if (ch + 1 < n_chunks) {
-            if (ch + 2 < n_chunks) load(o0, ch + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            chunk_step(o1, ch + 1, 1);
-        }
+        load(o0, min(ch + 2, last));
+        __builtin_amdgcn_sched_barrier(0);
+        if (ch + 1 < n_chunks) chunk_step(o1, ch + 1, 1);
     }
 #pragma unroll
     for (int cc = 0; cc < CW; ++cc)
