@@ -381,10 +381,13 @@ def beside(args, dev, stream):
 
 def gated_delta(args, dev, stream):
     """The gated delta-rule recurrence at the page's model geometry (Hv 32,
-    Hk 16, Dk = Dv = 128): prefill 1 x 4096 (VALU-bound; algorithmic work 7
-    flop per state value per token: decay, the two dots, the write) and decode
-    16 x 1 / 256 x 1 (HBM-bound; the state read and written once).  Decode 16
-    rotates 16 slot sets through a replayed HIP graph, as the scan's."""
+    Hk 16, Dk = Dv = 128): prefill 1 x 4096 (algorithmic work 7 flop per state
+    value per token: decay, the two dots, the write), timed in the chunked
+    matrix form (``gdn_prefill_ws``, workspace allocated once outside the timed
+    calls) and, as context, in the per-token VALU kernel (``gdn_prefill``); and
+    decode 16 x 1 / 256 x 1 (HBM-bound; the state read and written once).
+    Decode 16 rotates 16 slot sets through a replayed HIP graph, as the
+    scan's."""
     import torch
 
     import mamba2_selective_scan_amd as ssm
@@ -395,14 +398,28 @@ def gated_delta(args, dev, stream):
     t = {f: torch.from_numpy(getattr(c, f)).to(dev)
          for f in ("q", "k", "v", "g", "beta", "state", "cu_seqlens", "slot", "fresh")}
     y = torch.empty((c.n_tokens, Hv, D), device=dev)
+    max_len = int((c.cu_seqlens[1:] - c.cu_seqlens[:-1]).max())
+    n_seqs = int(c.slot.shape[0])
+    ws = torch.empty(max(ssm.gdn_workspace_size(Hv, Hk, D, D, n_seqs, max_len), 1),
+                     dtype=torch.uint8, device=dev)
+    flops = 7 * PREFILL_T * Hv * D * D
+    ms_c = _event_ms(lambda: ssm.gdn_prefill_ws(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                                t["state"], t["cu_seqlens"], t["slot"],
+                                                t["fresh"], max_len, y=y, workspace=ws),
+                     10, 3, stream)
     ms = _event_ms(lambda: ssm.gdn_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["state"],
                                            t["cu_seqlens"], t["slot"], t["fresh"], y=y), 10, 3, stream)
-    flops = 7 * PREFILL_T * Hv * D * D
+    tf_c = flops / (ms_c * 1e-3) / 1e12
     tf = flops / (ms * 1e-3) / 1e12
     out["gdn_prefill_1x4096_Hv32_Hk16_D128"] = {
-        "ms": round(ms, 4), "TFLOPs": round(tf, 2), "frac_fp32": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
-        "frac_unpacked_fp32": round(tf / FP32_VALU_UNPACKED_TFLOPS, 4), "algorithmic_flops": flops}
-    del t, y
+        "ms": round(ms_c, 4), "entry": "ssm_gdn_prefill_ws (chunks of 16 tokens, matrix cores)",
+        "TFLOPs": round(tf_c, 2), "frac_fp32_mfma": round(tf_c / FP32_MFMA_PEAK_TFLOPS, 4),
+        "workspace_bytes": int(ws.numel()), "algorithmic_flops": flops,
+        "per_token_kernel": {
+            "ms": round(ms, 4), "entry": "ssm_gdn_prefill", "TFLOPs": round(tf, 2),
+            "frac_fp32": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
+            "frac_unpacked_fp32": round(tf / FP32_VALU_UNPACKED_TFLOPS, 4)}}
+    del t, y, ws
 
     def dec_bytes(n):
         return 4 * (2 * n * Hv * D * D + n * (2 * Hk * D + 2 * Hv * D + 2 * Hv))
