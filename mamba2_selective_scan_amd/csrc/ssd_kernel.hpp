@@ -36,7 +36,9 @@
 // a chunk are staged in LDS, double-buffered (rows padded so the strided
 // state-update reads are conflict-free), the per-token scalars are formed once
 // in wave 0, and G^T, the same for the four wavefronts, is formed a quarter
-// by each and summed through LDS.
+// by each and summed through LDS.  G^T only feeds the chunk's own y (never the
+// state), so a chunk's y is finished during the next chunk, after the one
+// barrier per chunk that the staging needs anyway.
 #pragma once
 
 #include "scan_kernel.hpp"
@@ -64,8 +66,10 @@ struct SsdShape {
     static constexpr int BUF = ((OFF_MODE + 1) + 3) / 4 * 4;
     static constexpr int U_BC = (CT * N / 4 + kThreads - 1) / kThreads;    // float4 units of B (and of C)
     static constexpr int U_X = (CT * RBW / 4 + kThreads - 1) / kThreads;   // float4 units of x
-    static constexpr int OFF_GX = 2 * BUF;          // G^T partials [4 waves][64 lanes][4]
-    static constexpr int lds_floats() { return OFF_GX + kWaves * 64 * 4; }
+    static constexpr int OFF_GX = 2 * BUF;          // G^T partials [2 chunk parities][4 waves][64 lanes][4]
+    static constexpr int GX = kWaves * 64 * 4;
+    static constexpr int OFF_SIG = OFF_GX + 2 * GX; // sigma at the end
+    static constexpr int lds_floats() { return OFF_SIG + 4; }
 };
 
 // Sum over lanes 0..l of each 16-lane DPP row (lanes past a row's start add 0).
@@ -385,6 +389,7 @@ ssd_scan_kernel(ScanArgs a) {
     // ---- chunk staging: buffer loads -> registers -> LDS (double-buffered).
     // Each thread's byte offsets into a chunk are fixed; a chunk's descriptors
     // cover its tokens only, so the units past the segment end read zeros.
+    // Loads run two chunks ahead: chunk k lands in register set k & 1.
     constexpr int kNone = 0x7ffffff0;                // an offset past every descriptor
     const int x_tok = H * P * int(sizeof(float));
     int vo_bc[S::U_BC], lo_bc[S::U_BC], vo_x[S::U_X];
@@ -402,21 +407,24 @@ ssd_scan_kernel(ScanArgs a) {
         vo_x[u] = q < CT * S::RBW / 4 ? (tt * H * P + hd * P + prow0 + pi) * int(sizeof(float)) : kNone;
     }
     const int vo_dt = tid < CT ? (tid * H + hd) * int(sizeof(float)) : kNone;
-    f4 pb[S::U_BC], pc[S::U_BC], px[S::U_X];
-    float pdt = 0.f;
-    auto issue_loads = [&](int t0, int nt_) {
+    struct Stage {
+        f4 pb[S::U_BC], pc[S::U_BC], px[S::U_X];
+        float pdt;
+    };
+    Stage stg[2];
+    auto issue_loads = [&](Stage &sg, int t0, int nt_) {
         const __amdgpu_buffer_rsrc_t rb = buffer_of(a.B + int64_t(t0) * G * N, nt_ * G * N * int(sizeof(float)));
         const __amdgpu_buffer_rsrc_t rc = buffer_of(a.C + int64_t(t0) * G * N, nt_ * G * N * int(sizeof(float)));
         const __amdgpu_buffer_rsrc_t rx = buffer_of(a.x + int64_t(t0) * H * P, nt_ * x_tok);
         const __amdgpu_buffer_rsrc_t rd = buffer_of(a.dt + int64_t(t0) * H, nt_ * H * int(sizeof(float)));
 #pragma unroll
         for (int u = 0; u < S::U_BC; ++u) {
-            pb[u] = buffer_load<4>(rb, vo_bc[u], 0);
-            pc[u] = buffer_load<4>(rc, vo_bc[u], 0);
+            sg.pb[u] = buffer_load<4>(rb, vo_bc[u], 0);
+            sg.pc[u] = buffer_load<4>(rc, vo_bc[u], 0);
         }
 #pragma unroll
-        for (int u = 0; u < S::U_X; ++u) px[u] = buffer_load<4>(rx, vo_x[u], 0);
-        pdt = buffer_load<1>(rd, vo_dt, 0);         // raw dt: transformed at the commit
+        for (int u = 0; u < S::U_X; ++u) sg.px[u] = buffer_load<4>(rx, vo_x[u], 0);
+        sg.pdt = buffer_load<1>(rd, vo_dt, 0);      // raw dt: transformed at the commit
     };
     // Deferred decay: the accumulators hold h / sigma.  A chunk whose decay
     // stays within e^{-kSsdFastDecay} runs in "deferred" form: the state is not
@@ -429,23 +437,24 @@ ssd_scan_kernel(ScanArgs a) {
     // so one weighted x serves both products and y takes e^{S_t} sigma per row.
     float sigma = 1.f;                               // wave 0's copy is the one used
     auto commit = [&](auto bufc, int nt_) {
-        constexpr int buf = decltype(bufc)::value;
+        constexpr int buf = decltype(bufc)::value;   // chunk parity: LDS buffer and register set
         float *base = lds + buf * S::BUF;
+        const Stage &sg = stg[buf];
 #pragma unroll
         for (int u = 0; u < S::U_BC; ++u) {
             if (lo_bc[u] >= 0) {
-                *reinterpret_cast<f4 *>(base + S::OFF_B + lo_bc[u]) = pb[u];
-                *reinterpret_cast<f4 *>(base + S::OFF_C + lo_bc[u]) = pc[u];
+                *reinterpret_cast<f4 *>(base + S::OFF_B + lo_bc[u]) = sg.pb[u];
+                *reinterpret_cast<f4 *>(base + S::OFF_C + lo_bc[u]) = sg.pc[u];
             }
         }
 #pragma unroll
         for (int u = 0; u < S::U_X; ++u) {
             const int q = u * kThreads + tid;
-            if (q < CT * S::RBW / 4) reinterpret_cast<f4 *>(base + S::OFF_X)[q] = px[u];
+            if (q < CT * S::RBW / 4) reinterpret_cast<f4 *>(base + S::OFF_X)[q] = sg.px[u];
         }
         if (tid < 64) {                                  // wave 0, all lanes active
             // lanes 0..15 hold the chunk's tokens (0 past the segment end)
-            const float dtv = (tid < nt_) ? dt_transform(pdt, bias_h, a.dt_softplus) : 0.f;
+            const float dtv = (tid < nt_) ? dt_transform(sg.pdt, bias_h, a.dt_softplus) : 0.f;
             const float Sv = row_prefix_sum(dtv * A_h);
             const float S15 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Sv), 15));
             const float e15 = expf(S15);
@@ -475,20 +484,30 @@ ssd_scan_kernel(ScanArgs a) {
         }
     };
 
-    // y of the chunk just computed: stored after the next chunk's commit (so
-    // that commit waits only on loads; the stores drain during the next
-    // chunk's products), through a descriptor covering the chunk's tokens
-    f4m ypend = {0.f, 0.f, 0.f, 0.f};
+    // y of a chunk is finished during the next one: the G^T parts (written to
+    // LDS slot c & 1) are summed after the barrier that ends chunk c, scaled by
+    // the coefficients kept here and multiplied into the operand kept here,
+    // then added to the carried-in term:  y = (ysave + G' X) * yscale.
+    f4m ysave = {0.f, 0.f, 0.f, 0.f};
+    float gcoef[4] = {0.f, 0.f, 0.f, 0.f}, gopnd[4] = {0.f, 0.f, 0.f, 0.f}, yscale[4] = {0.f, 0.f, 0.f, 0.f};
     const int vo_y = ((4 * kq) * H * P + hd * P + p0 + tl) * int(sizeof(float));
-    auto store_y = [&](int t0, int nt_) {
-        if (!wave_ok) return;
-        const __amdgpu_buffer_rsrc_t ry = buffer_of(a.y + int64_t(t0) * H * P, nt_ * x_tok);
+    auto finish_y = [&](int par, int c) {             // y of chunk c (wave_ok only)
+        const f4m *gx = reinterpret_cast<const f4m *>(lds + S::OFF_GX + par * S::GX);
+        f4m gacc = gx[lane];
+#pragma unroll
+        for (int k = 1; k < kWaves; ++k) gacc += gx[k * 64 + lane];
+        // gacc register v of lane l: G^T[s][t] with s = 4(l/16) + v, t = l%16
+        f4m y = ysave;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) y = mfma16(gacc[v] * gcoef[v], gopnd[v], y);
+        const int t0 = t_begin + c * CT;
+        const __amdgpu_buffer_rsrc_t ry = buffer_of(a.y + int64_t(t0) * H * P, min(CT, t_end - t0) * x_tok);
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ypend[v]), ry, vo_y, v * x_tok, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[v] * yscale[v]), ry, vo_y, v * x_tok, 0);
     };
-    auto compute = [&](auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
+    auto compute = [&](auto bufc, int c) {
+        constexpr int buf = decltype(bufc)::value;   // chunk c's LDS buffer and G^T slot: c & 1
         const float *base = lds + buf * S::BUF;
         // G^T = B C^T is the same for the four waves: each forms the part over
         // its quarter of the contraction index n (NT of the 4 NT steps) and the
@@ -535,54 +554,45 @@ ssd_scan_kernel(ScanArgs a) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < NT; ++i) gpart = mfma16(gb[i], gc[i], gpart);
-        reinterpret_cast<f4m *>(lds + S::OFF_GX)[w * 64 + lane] = gpart;
+        reinterpret_cast<f4m *>(lds + S::OFF_GX + buf * S::GX)[w * 64 + lane] = gpart;
         __builtin_amdgcn_sched_barrier(0);
-        f4m yacc = {0.f, 0.f, 0.f, 0.f};
-        if (wave_ok) {
-            if (pre != 1.f) {                            // renormalise the deferred state
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) hacc[nt] *= pre;
-            }
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                yacc = mfma16(creg[nt].x, hacc[nt][0], yacc);
-                yacc = mfma16(creg[nt].y, hacc[nt][1], yacc);
-                yacc = mfma16(creg[nt].z, hacc[nt][2], yacc);
-                yacc = mfma16(creg[nt].w, hacc[nt][3], yacc);
-            }
-        }
-        __syncthreads();                                 // the four parts of G^T are in
         if (!wave_ok) return;
-        f4m gacc = reinterpret_cast<const f4m *>(lds + S::OFF_GX)[lane];
+        if (c > 0) finish_y(buf ^ 1, c - 1);         // the previous chunk's parts are all in
+        if (pre != 1.f) {                            // renormalise the deferred state
 #pragma unroll
-        for (int k = 1; k < kWaves; ++k) gacc += reinterpret_cast<const f4m *>(lds + S::OFF_GX)[k * 64 + lane];
-        // gacc register v of lane l: G^T[s][t] with s = 4(l/16) + v, t = l%16;
-        // yacc register v: row t = 4(l/16) + v
+            for (int nt = 0; nt < NT; ++nt) hacc[nt] *= pre;
+        }
+        f4m yacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            yacc = mfma16(creg[nt].x, hacc[nt][0], yacc);
+            yacc = mfma16(creg[nt].y, hacc[nt][1], yacc);
+            yacc = mfma16(creg[nt].z, hacc[nt][2], yacc);
+            yacc = mfma16(creg[nt].w, hacc[nt][3], yacc);
+        }
+        // what y of this chunk still needs (yacc register v: row t = 4(l/16) + v)
         float wx[4];
         if (fast) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 wx[v] = base[S::OFF_W + 4 * kq + v] * xr[v];
-                gacc[v] = (4 * kq + v <= tl) ? gacc[v] : 0.f;
+                gcoef[v] = (4 * kq + v <= tl) ? 1.f : 0.f;
+                gopnd[v] = wx[v];
+                yscale[v] = base[S::OFF_ES + 4 * kq + v];
             }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) yacc = mfma16(gacc[v], wx[v], yacc);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) yacc[v] *= base[S::OFF_ES + 4 * kq + v];
+            ysave = yacc;
         } else {
             const float S_t = base[S::OFF_S + tl];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int sv = 4 * kq + v;
-                gacc[v] = (sv <= tl) ? gacc[v] * __expf(S_t - base[S::OFF_S + sv]) * base[S::OFF_DT + sv] : 0.f;
-                yacc[v] *= base[S::OFF_ES + sv];
+                gcoef[v] = (sv <= tl) ? __expf(S_t - base[S::OFF_S + sv]) * base[S::OFF_DT + sv] : 0.f;
+                gopnd[v] = xr[v];
+                yscale[v] = 1.f;
+                ysave[v] = yacc[v] * base[S::OFF_ES + sv];
+                wx[v] = base[S::OFF_W + sv] * xr[v];
             }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) yacc = mfma16(gacc[v], xr[v], yacc);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) wx[v] = base[S::OFF_W + 4 * kq + v] * xr[v];
         }
-        ypend = yacc;                                    // stored after the next commit
         // an exact chunk scales the state by e^{S_15} before its update (kept
         // out of the branches above so the state stays in place in both)
         const float mid = base[S::OFF_E15];
@@ -602,8 +612,15 @@ ssd_scan_kernel(ScanArgs a) {
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
     const int n_chunks = (n_tok + CT - 1) / CT;
+    // chunk k's loads (k clamped to the last chunk, so every step issues the
+    // same loads and each commit waits only for its own)
+    auto issue_chunk = [&](Stage &sg, int k) {
+        const int t0 = t_begin + min(k, n_chunks - 1) * CT;
+        issue_loads(sg, t0, min(CT, t_end - t0));
+    };
     if (n_chunks > 0) {
-        issue_loads(t_begin, min(CT, n_tok));
+        issue_chunk(stg[0], 0);
+        issue_chunk(stg[1], 1);
         commit(B0{}, min(CT, n_tok));
     }
     __syncthreads();
@@ -611,23 +628,22 @@ ssd_scan_kernel(ScanArgs a) {
     // addresses are compile-time offsets
     auto step = [&](int c, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
-        const int t0 = t_begin + c * CT;
-        const int nt_ = min(CT, t_end - t0);
-        const bool has_next = c + 1 < n_chunks;
-        if (has_next) issue_loads(t0 + CT, min(CT, t_end - t0 - CT));
-        compute(bufc);
-        if (has_next) commit(std::integral_constant<int, buf ^ 1>{}, min(CT, t_end - t0 - CT));
-        store_y(t0, nt_);
+        const int t1 = t_begin + (c + 1) * CT;
+        issue_chunk(stg[buf], c + 2);                // into the set chunk c just left
+        __builtin_amdgcn_sched_barrier(0);
+        compute(bufc, c);
+        if (c + 1 < n_chunks) commit(std::integral_constant<int, buf ^ 1>{}, min(CT, t_end - t1));
         __syncthreads();
     };
     for (int c = 0; c < n_chunks; c += 2) {
         step(c, B0{});
         if (c + 1 < n_chunks) step(c + 1, B1{});
     }
+    if (n_chunks > 0 && wave_ok) finish_y((n_chunks - 1) & 1, n_chunks - 1);
 
     // ---- the sequence's end state after its last segment: h = sigma * accumulators
     if (seg == last) {
-        float *const sig_lds = lds + S::OFF_GX;          // free after the last barrier
+        float *const sig_lds = lds + S::OFF_SIG;
         if (tid == 0) sig_lds[0] = sigma;
         __syncthreads();
         const float sg = sig_lds[0];
