@@ -229,6 +229,12 @@ bool ssd_shape(const ssm_scan_dims *d) {
            int64_t(d->n_groups) * N * span < INT32_MAX;
 }
 bool ssd_eligible(const ssm_scan_dims *d, bool vec) { return vec && ssd_shape(d); }
+// The wide scan pass (two 16-row tiles per wave, 128 rows per workgroup) needs
+// each wave's 32 rows in one head and each group's rows in whole 128-row blocks.
+bool ssd_wide(const ssm_scan_dims *d) {
+    const int64_t group_rows = int64_t(d->n_heads / d->n_groups) * d->head_dim;
+    return d->head_dim % 32 == 0 && group_rows % ssm::SsdWideShape<8>::RBW == 0;
+}
 
 SegPlan plan_segments(const ssm_scan_dims *d, const ShapeRow &row, int32_t n_seqs,
                       int32_t max_seqlen, int32_t requested) {
@@ -238,10 +244,14 @@ SegPlan plan_segments(const ssm_scan_dims *d, const ShapeRow &row, int32_t n_seq
     if (requested > 1) {
         K = requested;
     } else if (ssd_shape(d)) {
-        // matrix-core segments: a workgroup of four waves per 64 rows of a head;
-        // aim at two waves per SIMD (measured at 1 x 4096, H64 P64 N128: 8
-        // segments 0.237 ms, 12: 0.237, 4: 0.278, 16: 0.243)
-        const int64_t waves = int64_t(n_seqs) * d->n_heads * ((d->head_dim + 63) / 64) * ssm::kWaves;
+        // matrix-core segments: a scan-pass workgroup of four waves per 128 rows
+        // (wide) or per 64 rows of a head; aim at two waves per SIMD (measured
+        // at 1 x 4096, H64 P64 N128 with the wide scan pass: 16 segments 0.169
+        // ms, 12: 0.194, 8: 0.176)
+        const int64_t rows = int64_t(d->n_heads) * d->head_dim;
+        const int64_t waves = int64_t(n_seqs) * ssm::kWaves *
+                              (ssd_wide(d) ? rows / ssm::SsdWideShape<8>::RBW
+                                           : d->n_heads * ((d->head_dim + 63) / 64));
         if (waves >= kSsdTargetWaves) return SegPlan{1, 0};
         K = (kSsdTargetWaves + waves - 1) / waves;
         K = std::min<int64_t>(K, max_seqlen / kMinSegTokens);
@@ -368,6 +378,7 @@ int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_
             const void *kern;
             int lds;
             int64_t blocks = per_seg * plan.n_segs;
+            int64_t slabs = sa.n_row_blocks;     // row blocks per head, or 128-row slabs
             if (states) {
                 blocks = per_seg * (plan.n_segs - 1);
                 lds = 0;                         // static LDS only
@@ -381,6 +392,15 @@ int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_
                 } else {
                     kern = reinterpret_cast<const void *>(&ssm::ssd_state_kernel<2, 1, kSsdStateGroup>);
                 }
+            } else if (ssd_wide(d)) {
+                kern = nt == 2 ? reinterpret_cast<const void *>(&ssm::ssd_scan_wide_kernel<2>)
+                     : nt == 4 ? reinterpret_cast<const void *>(&ssm::ssd_scan_wide_kernel<4>)
+                               : reinterpret_cast<const void *>(&ssm::ssd_scan_wide_kernel<8>);
+                lds = nt == 2 ? ssm::SsdWideShape<2>::lds_floats()
+                    : nt == 4 ? ssm::SsdWideShape<4>::lds_floats()
+                              : ssm::SsdWideShape<8>::lds_floats();
+                slabs = int64_t(d->n_heads) * d->head_dim / ssm::SsdWideShape<8>::RBW;
+                blocks = int64_t(n_seqs) * plan.n_segs * slabs;
             } else {
                 kern = nt == 2 ? reinterpret_cast<const void *>(&ssm::ssd_scan_kernel<2>)
                      : nt == 4 ? reinterpret_cast<const void *>(&ssm::ssd_scan_kernel<4>)
@@ -390,8 +410,10 @@ int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_
                               : ssm::SsdShape<8>::lds_floats();
             }
             if (blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
-            sa.n_blocks = int32_t(blocks);
-            void *params[] = {&sa};
+            ScanArgs la = sa;
+            la.n_row_blocks = int32_t(slabs);
+            la.n_blocks = int32_t(blocks);
+            void *params[] = {&la};
             const hipError_t err = hipLaunchKernel(kern, dim3(unsigned(blocks)), dim3(kThreads),
                                                    params, size_t(lds) * sizeof(float), stream);
             return err == hipSuccess ? SSM_OK : hip_fail(err, SSM_ERR_LAUNCH);
@@ -618,12 +640,21 @@ int ssm_scan_query_prefill_plan(const ssm_scan_dims *dims, int32_t n_seqs, int32
             const int nt = dims->d_state / 16;
             out->lanes_per_row = 4;
             out->elems_per_lane = dims->d_state / 4;
-            out->rows_per_block = 64;
             out->chunk_tokens = 16;
-            out->lds_bytes = (nt == 2 ? ssm::SsdShape<2>::lds_floats()
-                            : nt == 4 ? ssm::SsdShape<4>::lds_floats()
-                                      : ssm::SsdShape<8>::lds_floats()) * int(sizeof(float));
-            out->blocks = int64_t(n_seqs) * plan.n_segs * dims->n_heads * ((dims->head_dim + 63) / 64);
+            if (ssd_wide(dims)) {       // the scan pass: 128 rows (two tiles per wave)
+                out->rows_per_block = ssm::SsdWideShape<8>::RBW;
+                out->lds_bytes = (nt == 2 ? ssm::SsdWideShape<2>::lds_floats()
+                                : nt == 4 ? ssm::SsdWideShape<4>::lds_floats()
+                                          : ssm::SsdWideShape<8>::lds_floats()) * int(sizeof(float));
+                out->blocks = int64_t(n_seqs) * plan.n_segs * dims->n_heads * dims->head_dim /
+                              ssm::SsdWideShape<8>::RBW;
+            } else {
+                out->rows_per_block = 64;
+                out->lds_bytes = (nt == 2 ? ssm::SsdShape<2>::lds_floats()
+                                : nt == 4 ? ssm::SsdShape<4>::lds_floats()
+                                          : ssm::SsdShape<8>::lds_floats()) * int(sizeof(float));
+                out->blocks = int64_t(n_seqs) * plan.n_segs * dims->n_heads * ((dims->head_dim + 63) / 64);
+            }
         } else {
             const Geo geo = geo_for(*row, Kind::kSegScan);
             out->chunk_tokens = geo.CT;

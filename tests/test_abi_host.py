@@ -120,11 +120,11 @@ def test_no_kernel_uses_scratch():
     scratch = [int(v) for v in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
     # 7 state-size classes x (vector, scalar) x (4 option sets x (prefill, decode)
     # + segment scan + correction) + 2 combine kernels + 6 matrix-core corrections
-    # (3 contraction lengths, masked or not) + 3 x 2 matrix-core segment kernels
-    # (N 32, 64, 128; state pass and scan pass);
+    # (3 contraction lengths, masked or not) + 3 x 3 matrix-core segment kernels
+    # (N 32, 64, 128; state pass, scan pass and the wide scan pass);
     # conv1d + SiLU: (vector, scalar) x (4 history lengths x (decode, prefill)
     # + 3 with snapshots); gated RMSNorm: (vector, scalar) x 6 row-length classes
-    n_scan = 7 * 2 * (4 * 2 + 2) + 2 + 6 + 3 * 2
+    n_scan = 7 * 2 * (4 * 2 + 2) + 2 + 6 + 3 * 3
     n_conv = 2 * (4 * 2 + 3)
     n_norm = 2 * 6
     # gated delta rule: 5 key-width classes x (vector, scalar) x (prefill, decode)
@@ -141,17 +141,19 @@ def test_single_hip_runtime():
 
 
 def test_prefill_plan_and_workspace():
-    """The headline prefill (1 x 4096 at H64 P64 N128 G8) gives the matrix-core
-    segment scan 256 wavefronts per segment, so automatic planning cuts it into
-    8 segments of 512 tokens (2048 waves); the register segment scan's shapes
-    aim at 4096 waves; a batch that already fills the GPU is not cut; forcing
-    works; the workspace holds one [H][P][N] state per segment plus the decay
-    arrays."""
+    """The headline prefill (1 x 4096 at H64 P64 N128 G8) gives the wide
+    matrix-core scan pass 128 wavefronts per segment, so automatic planning
+    cuts it into 16 segments of 256 tokens (2048 waves); the register segment
+    scan's shapes aim at 4096 waves; a batch that already fills the GPU is not
+    cut; forcing works; the workspace holds one [H][P][N] state per segment
+    plus the decay arrays."""
     g = m.prefill_plan(64, 64, 128, 8, 1, 4096)
-    assert g["segments"] == 8 and g["segment_tokens"] == 512 and g["blocks"] == 8 * 64
-    assert g["chunk_tokens"] == 16 and g["rows_per_block"] == 64 and g["lds_bytes"] <= 64 * 1024
+    assert g["segments"] == 16 and g["segment_tokens"] == 256 and g["blocks"] == 16 * 32
+    # the scan pass of this shape is the wide one: 128 rows (two heads) per workgroup
+    assert g["chunk_tokens"] == 16 and g["rows_per_block"] == 128 and g["lds_bytes"] <= 64 * 1024
     ws = m.workspace_size(64, 64, 128, 8, 1, 4096, 4096)
-    assert 8 * 64 * 64 * 128 * 4 + 4096 * 64 * 4 <= ws <= 8 * 64 * 64 * 128 * 4 + 4096 * 64 * 4 + 4096
+    # + per-segment decay totals [1][16][64] and alignment
+    assert 16 * 64 * 64 * 128 * 4 + 4096 * 64 * 4 <= ws <= 16 * 64 * 64 * 128 * 4 + 4096 * 64 * 4 + 16 * 64 * 4 + 512
     g = m.prefill_plan(64, 64, 100, 8, 1, 4096)                       # register segment scan
     assert g["segments"] == 4 and g["segment_tokens"] == 1024 and g["blocks"] == 4 * 256
     assert m.prefill_plan(64, 64, 128, 8, 16, 4096)["segments"] == 1     # 16 seqs fill it

@@ -251,15 +251,16 @@ def test_graph_replay_matches_eager(ssm):
 
 # ---------------------------------------------------------------- time-split prefill
 def test_split_prefill_headline(ssm, orc):
-    """1 x 4096 at H64 P64 N128 G8: the automatic plan cuts it into 8
-    segments (matrix-core segment scans); fresh and resuming start states."""
+    """1 x 4096 at H64 P64 N128 G8: the automatic plan cuts it into 16
+    segments (matrix-core segment scans, the wide scan pass); fresh and
+    resuming start states."""
     for fresh in (1, 0):
         case = ssm_inputs.workload("prefill4096")
         if not fresh:
             case = ssm_inputs.make_case(64, 64, 128, 8, [4096], [0], seed=12)
         plan = ssm.prefill_plan(case.H, case.P, case.N, case.G, 1, 4096)
         say(f"split prefill 1x4096 fresh={fresh}: plan {plan}")
-        assert plan["segments"] == 8
+        assert plan["segments"] == 16 and plan["rows_per_block"] == 128
         y, st = run_gpu(case, "prefill_ws")
         y32, st32 = orc.scan_case(case, precision="f32")
         assert_parity(case, y, st, y32, st32, label=f"split 1x4096 fresh={fresh} vs fp32")
@@ -324,6 +325,26 @@ def test_split_prefill_shapes(ssm, orc, N, P):
                                 slots=[6, 0, 2, 5, 3], n_slots=8, poison_fresh=True,
                                 sentinel_unused=True, name=f"split_N{N}_P{P}")
     say(f"split shape N={N} P={P}")
+    y, st = run_gpu(case, "prefill_ws", segments=4)
+    y32, st32 = orc.scan_case(case, precision="f32")
+    assert_parity(case, y, st, y32, st32)
+    assert not np.any(st[6])
+
+
+@pytest.mark.parametrize("H,P,N,G", [(4, 96, 64, 1), (8, 32, 32, 2), (2, 256, 32, 1), (4, 64, 128, 2),
+                                     (4, 128, 64, 2)])
+def test_split_prefill_wide_layouts(ssm, orc, H, P, N, G):
+    """Shapes whose scan pass runs 128 rows per workgroup (P % 32 == 0 and each
+    group's rows in whole blocks of 128): windows that straddle two heads
+    (P 96), four heads per workgroup (P 32), two workgroups per head (P 256),
+    every state size; fresh, resumed and empty sequences."""
+    lengths = [0, 1, 77, 200, 31]
+    case = ssm_inputs.make_case(H, P, N, G, lengths, [1, 0, 0, 1, 0], seed=500 + H + P + N,
+                                slots=[6, 0, 2, 5, 3], n_slots=8, poison_fresh=True,
+                                sentinel_unused=True, name=f"wide_H{H}_P{P}_N{N}_G{G}")
+    plan = ssm.prefill_plan(H, P, N, G, len(lengths), 200, 4)
+    say(f"wide layout H={H} P={P} N={N} G={G}: {plan}")
+    assert plan["rows_per_block"] == 128
     y, st = run_gpu(case, "prefill_ws", segments=4)
     y32, st32 = orc.scan_case(case, precision="f32")
     assert_parity(case, y, st, y32, st32)
