@@ -155,7 +155,7 @@ constexpr int kSsdWindow = 512;          // tokens whose weights one pass of the
 constexpr float kSsdFastDecay = 40.f;    // a scan chunk decaying less than e^-40 runs deferred
 constexpr float kSsdFloor = 0x1p-30f;    // the deferred factor is folded in before passing this
 template <int NT, int NS, int IT>        // N = 16 NT; NS column parts; IT tokens per load group
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 4)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 ssd_state_kernel(ScanArgs a) {
     constexpr int N = 16 * NT;
     constexpr int NW = N / (2 * NS);                 // state columns per wavefront

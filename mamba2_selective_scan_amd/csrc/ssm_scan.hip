@@ -215,7 +215,7 @@ struct SegPlan {
 constexpr int64_t kTargetWaves = 4096;
 constexpr int64_t kSsdTargetWaves = 2048;  // matrix-core segment scans
 constexpr int kMinSegTokens = 256;
-constexpr int kSsdStateGroup = 32;         // tokens per operand group of the state pass
+constexpr int kSsdStateGroup = 16;         // tokens per operand group of the state pass (4 waves/SIMD)
 constexpr int kSsdStateSplit128 = 1;       // N = 128: workgroups per state-column range
 
 // The chunked matrix-core segment scan covers N in {32, 64, 128} with whole
