@@ -351,6 +351,24 @@ def test_split_prefill_wide_layouts(ssm, orc, H, P, N, G):
     assert not np.any(st[6])
 
 
+@pytest.mark.parametrize("segments", [16, 40])
+def test_split_prefill_wide_many_segments(ssm, orc, segments):
+    """The wide scan pass over many short segments of a ragged batch: segment
+    boundaries inside chunks, sequences shorter than a segment, an empty
+    sequence, fresh and resumed starts."""
+    lengths = [1000, 300, 17, 0, 700]
+    case = ssm_inputs.make_case(4, 64, 128, 2, lengths, [1, 0, 0, 1, 0], seed=600 + segments,
+                                slots=[6, 0, 2, 5, 3], n_slots=8, poison_fresh=True,
+                                sentinel_unused=True, name=f"wide_segs{segments}")
+    plan = ssm.prefill_plan(4, 64, 128, 2, len(lengths), max(lengths), segments)
+    say(f"wide, {segments} segments requested: {plan}")
+    assert plan["rows_per_block"] == 128 and plan["segments"] > 8
+    y, st = run_gpu(case, "prefill_ws", segments=segments)
+    y32, st32 = orc.scan_case(case, precision="f32")
+    assert_parity(case, y, st, y32, st32)
+    assert not np.any(st[5])                 # the fresh empty sequence's slot is zeroed
+
+
 def test_split_prefill_scalar_path(ssm, orc):
     case = ssm_inputs.workload("mixed")
     y, st = run_gpu(case, "prefill_ws", offset_floats=1, segments=3)
