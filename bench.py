@@ -590,9 +590,9 @@ def main():
             "workload": "prefill 1 seq x 4096 tokens, fresh", "ms": round(pf_ms, 4),
             "ms_min": round(min(ms), 4), "ms_max": round(max(ms), 4),
             "iterations": args.prefill_steps,
-            "path": "ssm_scan_prefill_ws, automatic time split: matrix-core state pass over "
-                    "segments 1..n-1, carry combine, matrix-core chunked scans of every segment "
-                    "from its carried-in state (3 kernels)",
+            "path": "ssm_scan_prefill_ws, automatic time split: matrix-core state pass (end "
+                    "states of segments 0..n-2), carry combine, matrix-core chunked scans of every "
+                    "segment from its carried-in state, two 16-row tiles per wave (3 kernels)",
             "plan": ssm.prefill_plan(H, P, N, G, 1, PREFILL_T),
             "ms_unsplit": round(float(np.mean(ms_unsplit)), 4),
             "geometry_unsplit": ssm.geometry(H, P, N, G, 1),

@@ -47,29 +47,35 @@ namespace ssm {
 
 using f4m = float __attribute__((ext_vector_type(4)));
 
-template <int NT>                       // N = 16 * NT state elements
-struct SsdShape {
+// LDS layout and staging of the scan pass: a workgroup owns RBW = 64 TW rows
+// of the flattened (head, row) space, TW 16-row tiles per wave.
+template <int NT, int TW>               // N = 16 NT state elements; TW tiles per wave
+struct SsdScanShape {
     static constexpr int N = 16 * NT;
     static constexpr int CT = 16;                   // tokens per chunk
-    static constexpr int RBW = 64;                  // rows per workgroup (4 waves x 16)
+    static constexpr int RBW = 64 * TW;             // rows per workgroup (4 waves x 16 TW)
+    static constexpr int MH = 4;                    // heads per workgroup at most (16 TW | P)
     static constexpr int LDN = N + 4;               // padded LDS row of B / C
     static constexpr int OFF_C = 0;
     static constexpr int OFF_B = OFF_C + CT * LDN;
-    static constexpr int OFF_X = OFF_B + CT * LDN;  // x[CT][64]
-    static constexpr int OFF_S = OFF_X + CT * RBW;  // S_t
-    static constexpr int OFF_DT = OFF_S + CT;       // dt_t (0 past the segment)
-    static constexpr int OFF_ES = OFF_DT + CT;      // e^{S_t}
-    static constexpr int OFF_W = OFF_ES + CT;       // e^{S_15 - S_t} dt_t
-    static constexpr int OFF_E15 = OFF_W + CT;      // e^{S_15} (exact chunks), else 1
-    static constexpr int OFF_PRE = OFF_E15 + 1;     // factor the state takes before the chunk
-    static constexpr int OFF_MODE = OFF_PRE + 1;    // 1: deferred-decay chunk, 0: exact chunk
-    static constexpr int BUF = ((OFF_MODE + 1) + 3) / 4 * 4;
+    static constexpr int OFF_X = OFF_B + CT * LDN;  // x[CT][RBW]
+    static constexpr int OFF_S = OFF_X + CT * RBW;  // [MH][CT] S_t
+    static constexpr int OFF_DT = OFF_S + MH * CT;  // [MH][CT] dt_t (0 past the segment)
+    static constexpr int OFF_ES = OFF_DT + MH * CT; // [MH][CT] e^{S_t} (times sigma when deferred)
+    static constexpr int OFF_W = OFF_ES + MH * CT;  // [MH][CT] the update's weights
+    static constexpr int OFF_E15 = OFF_W + MH * CT; // [MH] e^{S_15} (exact chunks), else 1
+    static constexpr int OFF_PRE = OFF_E15 + MH;    // [MH] factor the state takes before the chunk
+    static constexpr int OFF_MODE = OFF_PRE + MH;   // [MH] 1: deferred-decay chunk, 0: exact chunk
+    static constexpr int BUF = (OFF_MODE + MH + 3) / 4 * 4;
     static constexpr int U_BC = (CT * N / 4 + kThreads - 1) / kThreads;    // float4 units of B (and of C)
-    static constexpr int U_X = (CT * RBW / 4 + kThreads - 1) / kThreads;   // float4 units of x
-    static constexpr int OFF_GX = 2 * BUF;          // G^T partials [2 chunk parities][4 waves][64 lanes][4]
+    static constexpr int U_X = CT * RBW / 4 / kThreads;                    // float4 units of x
+    static constexpr int PF = TW == 1 ? 2 : 1;      // chunks loaded ahead (register sets)
+    static constexpr int OFF_GX = 2 * BUF;          // G^T parts [2 chunk parities][4 waves][64 lanes][4]
     static constexpr int GX = kWaves * 64 * 4;
-    static constexpr int OFF_SIG = OFF_GX + 2 * GX; // sigma at the end
-    static constexpr int lds_floats() { return OFF_SIG + 4; }
+    static constexpr int OFF_SIG = OFF_GX + 2 * GX; // [MH] sigma at the end
+    static constexpr int lds_floats() { return OFF_SIG + MH; }
+    static_assert(TW == 1 || TW == 2, "one or two tiles per wave");
+    static_assert(CT * RBW / 4 % kThreads == 0, "whole x units per thread");
 };
 
 // Sum over lanes 0..l of each 16-lane DPP row (lanes past a row's start add 0).
@@ -322,15 +328,21 @@ ssd_state_kernel(ScanArgs a) {
     }
 }
 
-// The scan pass.  Grid: n_seqs x n_segs x H x ceil(P / 64) workgroups
-// (a.n_row_blocks = ceil(P/64), a.n_blocks their product), XCD-contiguous order
-// as the register kernel's.  Requires the vector path (16-byte aligned arrays),
-// N = 16 * NT, P % 16 == 0.  Segment k > 0 starts from workspace entry k - 1,
-// which the combine pass left holding the state carried into it.
-template <int NT>
+// The scan pass.  A workgroup owns a window of 64 TW consecutive rows of the
+// flattened (head, row) space inside one B/C group (rows of consecutive heads
+// sit next to each other in x, y, the state and the workspace), cut at the
+// group's end; wave w owns rows 16 TW w .. 16 TW w + 16 TW - 1, TW tiles of one
+// head.  With TW = 2 a wave reads B and C out of LDS once per chunk for 32
+// rows, and G^T is formed once for every head of the window; wave 0 forms the
+// per-token scalars of up to four heads, one 16-lane DPP row per head.  Grid:
+// n_seqs x n_segs x G x (windows per group, a.n_row_blocks) workgroups,
+// XCD-contiguous order.  Requires the vector path, N = 16 NT and P % (16 TW)
+// == 0.  Segment k > 0 starts from workspace entry k - 1, which the combine
+// pass left holding the state carried into it.
+template <int NT, int TW>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 ssd_scan_kernel(ScanArgs a) {
-    using S = SsdShape<NT>;
+    using S = SsdScanShape<NT, TW>;
     constexpr int N = S::N, CT = S::CT, LDN = S::LDN;
     extern __shared__ float4 lds_raw[];
     float *const lds = reinterpret_cast<float *>(lds_raw);
@@ -340,20 +352,18 @@ ssd_scan_kernel(ScanArgs a) {
     const int per = nb / kXcds, rem = nb % kXcds;
     const int xcd = bid % kXcds, kx = bid / kXcds;
     const int L = (xcd < rem) ? xcd * (per + 1) + kx : rem * (per + 1) + (xcd - rem) * per + kx;
-    const int rbw = L % a.n_row_blocks;
-    const int hd = (L / a.n_row_blocks) % a.H;
-    const int seg = (L / (a.n_row_blocks * a.H)) % a.n_segs;
-    const int s = L / (a.n_row_blocks * a.H * a.n_segs);
+    const int wpg = a.n_row_blocks;                  // windows per group
+    const int wb = L % wpg;
+    const int g = (L / wpg) % a.G;
+    const int seg = (L / (wpg * a.G)) % a.n_segs;
+    const int s = L / (wpg * a.G * a.n_segs);
 
     const int H = a.H, P = a.P, G = a.G;
-    const int g = hd / a.heads_per_group;
     const SegRange sr = segment_range(a, s, seg);
     const int last = sr.n_real - 1;
     if (seg > last) return;                          // past the sequence's segments
     const int t_begin = sr.t_begin, t_end = sr.t_end;
     const int n_tok = t_end - t_begin;
-    // starting state: the slot's for segment 0 of a resumed sequence, the
-    // carried-in state (workspace) for a later segment, else 0
     const bool from_slot = seg == 0 && a.fresh[s] == 0;
     const bool from_carry = seg > 0;
     if (from_slot && n_tok <= 0) return;             // empty resume: slot unchanged
@@ -361,36 +371,49 @@ ssd_scan_kernel(ScanArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int tl = lane & 15, kq = lane >> 4;        // lane % 16, lane / 16
-    const int prow0 = rbw * S::RBW;                  // first row of the workgroup
-    const int p0 = prow0 + 16 * w;                   // first row of this wave
-    const bool wave_ok = p0 < P;                     // P % 16 == 0: whole wave tiles
-    const int64_t hpn = int64_t(H) * P * N;
-    float *const st_head = a.state + (int64_t(a.slot[s]) * H + hd) * int64_t(P) * N;
-    float *const ws_head = a.ws_state + int64_t(s) * a.n_segs * hpn + int64_t(hd) * P * N;
-    const float A_h = a.A[hd];
-    const float bias_h = a.dt_bias ? a.dt_bias[hd] : 0.f;
+    const int group_end = (g + 1) * a.heads_per_group * P;   // one past the group's last row
+    const int fr_wg = g * a.heads_per_group * P + wb * S::RBW;  // first row h P + p of the window
+    const int rows_wg = min(S::RBW, group_end - fr_wg);       // rows of the window (a multiple of 16 TW)
+    const int h_wg = fr_wg / P;                      // its first head
+    const int n_heads_wg = (fr_wg + rows_wg - 1) / P - h_wg + 1;   // heads it touches (<= MH)
+    const int fr0 = fr_wg + 16 * TW * w;             // first row of this wave
+    const bool wave_ok = fr0 < fr_wg + rows_wg;      // whole waves: P % (16 TW) == 0
+    const int hw = wave_ok ? fr0 / P - h_wg : 0;     // this wave's head, relative to h_wg
+    const int64_t HPN = int64_t(H) * P * N;
+    float *const st_w = a.state + int64_t(a.slot[s]) * HPN + int64_t(fr0) * N;
+    float *const ws_w = a.ws_state + int64_t(s) * a.n_segs * HPN + int64_t(fr0) * N;
+    // wave 0, DPP row j = lane / 16: the scalars of head h_wg + j
+    const bool hrow_ok = kq < n_heads_wg;
+    const float A_j = (tid < 64 && hrow_ok) ? a.A[h_wg + kq] : 0.f;
+    const float bias_j = (tid < 64 && hrow_ok && a.dt_bias) ? a.dt_bias[h_wg + kq] : 0.f;
 
-    // ---- state h^T in accumulators: hacc[nt] register v of lane l holds
-    // h[p0 + l%16][16 nt + 4 (l/16) + v]
-    f4m hacc[NT];
+    // ---- state h^T in accumulators: hacc[i][nt] register v of lane l holds
+    // h[row fr0 + 16 i + l%16][16 nt + 4 (l/16) + v]
+    f4m hacc[TW][NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) hacc[nt] = f4m{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < TW; ++i)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) hacc[i][nt] = f4m{0.f, 0.f, 0.f, 0.f};
     if ((from_slot || from_carry) && wave_ok) {
-        const float *src = from_slot ? st_head : ws_head + int64_t(seg - 1) * hpn;
+        const float *src = from_slot ? st_w : ws_w + int64_t(seg - 1) * HPN;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const f4 v = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(
-                src + int64_t(p0 + tl) * N + 16 * nt + 4 * kq));
-            hacc[nt] = f4m{v.x, v.y, v.z, v.w};
-        }
+        for (int i = 0; i < TW; ++i)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const f4 v = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(
+                    src + int64_t(16 * i + tl) * N + 16 * nt + 4 * kq));
+                hacc[i][nt] = f4m{v.x, v.y, v.z, v.w};
+            }
     }
     __builtin_amdgcn_s_waitcnt(0);
 
     // ---- chunk staging: buffer loads -> registers -> LDS (double-buffered).
     // Each thread's byte offsets into a chunk are fixed; a chunk's descriptors
     // cover its tokens only, so the units past the segment end read zeros.
-    // Loads run two chunks ahead: chunk k lands in register set k & 1.
-    constexpr int kNone = 0x7ffffff0;                // an offset past every descriptor
+    // Loads run PF chunks ahead (chunk k lands in register set k % PF: two with
+    // one tile per wave; with two tiles, two waves per SIMD leave room for one)
+    // and chunk k is committed to LDS buffer k & 1.
+    constexpr int kNone = 0x7ffffff0;
     const int x_tok = H * P * int(sizeof(float));
     int vo_bc[S::U_BC], lo_bc[S::U_BC], vo_x[S::U_X];
 #pragma unroll
@@ -402,16 +425,17 @@ ssd_scan_kernel(ScanArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < S::U_X; ++u) {
-        const int q = u * kThreads + tid;            // unit = (token, 4 rows); rows past P unused
+        const int q = u * kThreads + tid;            // unit = (token, 4 rows)
         const int tt = q / (S::RBW / 4), pi = 4 * (q - tt * (S::RBW / 4));
-        vo_x[u] = q < CT * S::RBW / 4 ? (tt * H * P + hd * P + prow0 + pi) * int(sizeof(float)) : kNone;
+        vo_x[u] = pi < rows_wg ? (tt * H * P + fr_wg + pi) * int(sizeof(float)) : kNone;
     }
-    const int vo_dt = tid < CT ? (tid * H + hd) * int(sizeof(float)) : kNone;
+    // dt: lane 16 j + t of wave 0 takes token t of head h_wg + j
+    const int vo_dt = (tid < 64 && hrow_ok) ? (tl * H + h_wg + kq) * int(sizeof(float)) : kNone;
     struct Stage {
         f4 pb[S::U_BC], pc[S::U_BC], px[S::U_X];
         float pdt;
     };
-    Stage stg[2];
+    Stage stg[S::PF];
     auto issue_loads = [&](Stage &sg, int t0, int nt_) {
         const __amdgpu_buffer_rsrc_t rb = buffer_of(a.B + int64_t(t0) * G * N, nt_ * G * N * int(sizeof(float)));
         const __amdgpu_buffer_rsrc_t rc = buffer_of(a.C + int64_t(t0) * G * N, nt_ * G * N * int(sizeof(float)));
@@ -435,378 +459,12 @@ ssd_scan_kernel(ScanArgs a) {
     // In the deferred form the masked intra-chunk term factorises,
     //     e^{S_t - S_s} dt_s = e^{S_t} sigma * (e^{-S_s} dt_s / sigma),
     // so one weighted x serves both products and y takes e^{S_t} sigma per row.
-    float sigma = 1.f;                               // wave 0's copy is the one used
-    auto commit = [&](auto bufc, int nt_) {
-        constexpr int buf = decltype(bufc)::value;   // chunk parity: LDS buffer and register set
-        float *base = lds + buf * S::BUF;
-        const Stage &sg = stg[buf];
-#pragma unroll
-        for (int u = 0; u < S::U_BC; ++u) {
-            if (lo_bc[u] >= 0) {
-                *reinterpret_cast<f4 *>(base + S::OFF_B + lo_bc[u]) = sg.pb[u];
-                *reinterpret_cast<f4 *>(base + S::OFF_C + lo_bc[u]) = sg.pc[u];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < S::U_X; ++u) {
-            const int q = u * kThreads + tid;
-            if (q < CT * S::RBW / 4) reinterpret_cast<f4 *>(base + S::OFF_X)[q] = sg.px[u];
-        }
-        if (tid < 64) {                                  // wave 0, all lanes active
-            // lanes 0..15 hold the chunk's tokens (0 past the segment end)
-            const float dtv = (tid < nt_) ? dt_transform(sg.pdt, bias_h, a.dt_softplus) : 0.f;
-            const float Sv = row_prefix_sum(dtv * A_h);
-            const float S15 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Sv), 15));
-            const float e15 = expf(S15);
-            const bool fast = S15 >= -kSsdFastDecay;
-            float pre = 1.f;
-            if (!fast || sigma * e15 < kSsdFloor) {      // renormalise before the chunk
-                pre = sigma;
-                sigma = 1.f;
-            }
-            if (tid < CT) {
-                if (fast) {
-                    base[S::OFF_W + tid] = __expf(-Sv) * dtv / sigma;
-                    base[S::OFF_ES + tid] = __expf(Sv) * sigma;
-                } else {
-                    base[S::OFF_S + tid] = Sv;
-                    base[S::OFF_DT + tid] = dtv;
-                    base[S::OFF_ES + tid] = expf(Sv);
-                    base[S::OFF_W + tid] = expf(S15 - Sv) * dtv;
-                }
-            }
-            if (tid == 0) {
-                base[S::OFF_E15] = fast ? 1.f : e15;
-                base[S::OFF_PRE] = pre;
-                base[S::OFF_MODE] = fast ? 1.f : 0.f;
-            }
-            sigma = fast ? sigma * e15 : 1.f;
-        }
-    };
-
-    // y of a chunk is finished during the next one: the G^T parts (written to
-    // LDS slot c & 1) are summed after the barrier that ends chunk c, scaled by
-    // the coefficients kept here and multiplied into the operand kept here,
-    // then added to the carried-in term:  y = (ysave + G' X) * yscale.
-    f4m ysave = {0.f, 0.f, 0.f, 0.f};
-    float gcoef[4] = {0.f, 0.f, 0.f, 0.f}, gopnd[4] = {0.f, 0.f, 0.f, 0.f}, yscale[4] = {0.f, 0.f, 0.f, 0.f};
-    const int vo_y = ((4 * kq) * H * P + hd * P + p0 + tl) * int(sizeof(float));
-    auto finish_y = [&](int par, int c) {             // y of chunk c (wave_ok only)
-        const f4m *gx = reinterpret_cast<const f4m *>(lds + S::OFF_GX + par * S::GX);
-        f4m gacc = gx[lane];
-#pragma unroll
-        for (int k = 1; k < kWaves; ++k) gacc += gx[k * 64 + lane];
-        // gacc register v of lane l: G^T[s][t] with s = 4(l/16) + v, t = l%16
-        f4m y = ysave;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) y = mfma16(gacc[v] * gcoef[v], gopnd[v], y);
-        const int t0 = t_begin + c * CT;
-        const __amdgpu_buffer_rsrc_t ry = buffer_of(a.y + int64_t(t0) * H * P, min(CT, t_end - t0) * x_tok);
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[v] * yscale[v]), ry, vo_y, v * x_tok, 0);
-    };
-    auto compute = [&](auto bufc, int c) {
-        constexpr int buf = decltype(bufc)::value;   // chunk c's LDS buffer and G^T slot: c & 1
-        const float *base = lds + buf * S::BUF;
-        // G^T = B C^T is the same for the four waves: each forms the part over
-        // its quarter of the contraction index n (NT of the 4 NT steps) and the
-        // parts meet in LDS.  Step f = 4 tile + j, lane l: n = 16 tile + 4 (l/16) + j.
-        f4m gpart = {0.f, 0.f, 0.f, 0.f};
-        float gb[NT], gc[NT];
-        if constexpr (NT % 4 == 0) {
-#pragma unroll
-            for (int k = 0; k < NT / 4; ++k) {
-                const int off = tl * LDN + 16 * (w * (NT / 4) + k) + 4 * kq;
-                const f4 bq = *reinterpret_cast<const f4 *>(base + S::OFF_B + off);
-                const f4 cq = *reinterpret_cast<const f4 *>(base + S::OFF_C + off);
-                gb[4 * k + 0] = bq.x; gb[4 * k + 1] = bq.y; gb[4 * k + 2] = bq.z; gb[4 * k + 3] = bq.w;
-                gc[4 * k + 0] = cq.x; gc[4 * k + 1] = cq.y; gc[4 * k + 2] = cq.z; gc[4 * k + 3] = cq.w;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < NT; ++i) {
-                const int f = w * NT + i;
-                const int off = tl * LDN + 16 * (f / 4) + 4 * kq + f % 4;
-                gb[i] = base[S::OFF_B + off];
-                gc[i] = base[S::OFF_C + off];
-            }
-        }
-        float xr[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) xr[v] = base[S::OFF_X + (4 * kq + v) * S::RBW + 16 * w + tl];
-        // the state update's A operands, B[4(l/16) + q][16 nt + l%16]
-        float bup[4][NT];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                bup[q][nt] = base[S::OFF_B + (4 * kq + q) * LDN + 16 * nt + tl];
-        // C rows of token l%16 for Y = C h^T, n = 16 nt + 4 (l/16) + v
-        f4 creg[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-            creg[nt] = *reinterpret_cast<const f4 *>(base + S::OFF_C + tl * LDN + 16 * nt + 4 * kq);
-        const float pre = base[S::OFF_PRE];
-        const bool fast = base[S::OFF_MODE] != 0.f;
-        // keep every operand read issued ahead of the products (the scheduler
-        // would otherwise reuse a few registers and wait on each group)
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < NT; ++i) gpart = mfma16(gb[i], gc[i], gpart);
-        reinterpret_cast<f4m *>(lds + S::OFF_GX + buf * S::GX)[w * 64 + lane] = gpart;
-        __builtin_amdgcn_sched_barrier(0);
-        if (!wave_ok) return;
-        if (c > 0) finish_y(buf ^ 1, c - 1);         // the previous chunk's parts are all in
-        if (pre != 1.f) {                            // renormalise the deferred state
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) hacc[nt] *= pre;
-        }
-        f4m yacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            yacc = mfma16(creg[nt].x, hacc[nt][0], yacc);
-            yacc = mfma16(creg[nt].y, hacc[nt][1], yacc);
-            yacc = mfma16(creg[nt].z, hacc[nt][2], yacc);
-            yacc = mfma16(creg[nt].w, hacc[nt][3], yacc);
-        }
-        // what y of this chunk still needs (yacc register v: row t = 4(l/16) + v)
-        float wx[4];
-        if (fast) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                wx[v] = base[S::OFF_W + 4 * kq + v] * xr[v];
-                gcoef[v] = (4 * kq + v <= tl) ? 1.f : 0.f;
-                gopnd[v] = wx[v];
-                yscale[v] = base[S::OFF_ES + 4 * kq + v];
-            }
-            ysave = yacc;
-        } else {
-            const float S_t = base[S::OFF_S + tl];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int sv = 4 * kq + v;
-                gcoef[v] = (sv <= tl) ? __expf(S_t - base[S::OFF_S + sv]) * base[S::OFF_DT + sv] : 0.f;
-                gopnd[v] = xr[v];
-                yscale[v] = 1.f;
-                ysave[v] = yacc[v] * base[S::OFF_ES + sv];
-                wx[v] = base[S::OFF_W + sv] * xr[v];
-            }
-        }
-        // an exact chunk scales the state by e^{S_15} before its update (kept
-        // out of the branches above so the state stays in place in both)
-        const float mid = base[S::OFF_E15];
-        if (mid != 1.f) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) hacc[nt] *= mid;
-        }
-        // h^T += B^T (w X): tile nt, step q, lane l: A = B[4(l/16)+q][16 nt + l%16],
-        // B operand = the weighted x of token s = 4(l/16) + q
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) hacc[nt] = mfma16(bup[q][nt], wx[q], hacc[nt]);
-        }
-    };
-
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
-    const int n_chunks = (n_tok + CT - 1) / CT;
-    // chunk k's loads (k clamped to the last chunk, so every step issues the
-    // same loads and each commit waits only for its own)
-    auto issue_chunk = [&](Stage &sg, int k) {
-        const int t0 = t_begin + min(k, n_chunks - 1) * CT;
-        issue_loads(sg, t0, min(CT, t_end - t0));
-    };
-    if (n_chunks > 0) {
-        issue_chunk(stg[0], 0);
-        issue_chunk(stg[1], 1);
-        commit(B0{}, min(CT, n_tok));
-    }
-    __syncthreads();
-    // chunk c in LDS buffer c & 1; unrolled by two so each buffer's LDS
-    // addresses are compile-time offsets
-    auto step = [&](int c, auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
-        const int t1 = t_begin + (c + 1) * CT;
-        issue_chunk(stg[buf], c + 2);                // into the set chunk c just left
-        __builtin_amdgcn_sched_barrier(0);
-        compute(bufc, c);
-        if (c + 1 < n_chunks) commit(std::integral_constant<int, buf ^ 1>{}, min(CT, t_end - t1));
-        __syncthreads();
-    };
-    for (int c = 0; c < n_chunks; c += 2) {
-        step(c, B0{});
-        if (c + 1 < n_chunks) step(c + 1, B1{});
-    }
-    if (n_chunks > 0 && wave_ok) finish_y((n_chunks - 1) & 1, n_chunks - 1);
-
-    // ---- the sequence's end state after its last segment: h = sigma * accumulators
-    if (seg == last) {
-        float *const sig_lds = lds + S::OFF_SIG;
-        if (tid == 0) sig_lds[0] = sigma;
-        __syncthreads();
-        const float sg = sig_lds[0];
-        if (wave_ok) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                __builtin_nontemporal_store(f4{hacc[nt][0] * sg, hacc[nt][1] * sg, hacc[nt][2] * sg, hacc[nt][3] * sg},
-                                            reinterpret_cast<f4 *>(st_head + int64_t(p0 + tl) * N + 16 * nt + 4 * kq));
-        }
-    }
-}
-
-// ---- The wide scan pass: the same chunked form with two 16-row tiles per wave.
-// A workgroup owns 128 consecutive rows of the flattened (head, row) space, all
-// in one B/C group (rows of consecutive heads sit next to each other in x, y,
-// the state and the workspace); wave w owns rows 32 w .. 32 w + 31, two tiles of
-// one head.  Each wave reads B and C out of LDS once per chunk for 32 rows
-// instead of 16, halving the LDS traffic per row, and holds two independent
-// Y chains.  Per-head scalars for up to four heads are formed by wave 0, one
-// 16-lane DPP row per head.  Used when P % 32 == 0 and a group's rows come in
-// whole blocks of 128; one wavefront per SIMD.
-template <int NT>
-struct SsdWideShape {
-    static constexpr int N = 16 * NT;
-    static constexpr int CT = 16;                   // tokens per chunk
-    static constexpr int RBW = 128;                 // rows per workgroup (4 waves x 32)
-    static constexpr int MH = 4;                    // heads per workgroup at most (P >= 32)
-    static constexpr int LDN = N + 4;               // padded LDS row of B / C
-    static constexpr int OFF_C = 0;
-    static constexpr int OFF_B = OFF_C + CT * LDN;
-    static constexpr int OFF_X = OFF_B + CT * LDN;  // x[CT][128]
-    static constexpr int OFF_S = OFF_X + CT * RBW;  // [MH][CT] S_t
-    static constexpr int OFF_DT = OFF_S + MH * CT;  // [MH][CT] dt_t (0 past the segment)
-    static constexpr int OFF_ES = OFF_DT + MH * CT; // [MH][CT] e^{S_t} (times sigma when deferred)
-    static constexpr int OFF_W = OFF_ES + MH * CT;  // [MH][CT] the update's weights
-    static constexpr int OFF_E15 = OFF_W + MH * CT; // [MH] e^{S_15} (exact chunks), else 1
-    static constexpr int OFF_PRE = OFF_E15 + MH;    // [MH] factor the state takes before the chunk
-    static constexpr int OFF_MODE = OFF_PRE + MH;   // [MH] 1: deferred-decay chunk, 0: exact chunk
-    static constexpr int BUF = (OFF_MODE + MH + 3) / 4 * 4;
-    static constexpr int U_BC = (CT * N / 4 + kThreads - 1) / kThreads;    // float4 units of B (and of C)
-    static constexpr int U_X = CT * RBW / 4 / kThreads;                    // float4 units of x
-    static constexpr int OFF_GX = 2 * BUF;          // G^T parts [2 chunk parities][4 waves][64 lanes][4]
-    static constexpr int GX = kWaves * 64 * 4;
-    static constexpr int OFF_SIG = OFF_GX + 2 * GX; // [MH] sigma at the end
-    static constexpr int lds_floats() { return OFF_SIG + MH; }
-    static_assert(CT * RBW / 4 % kThreads == 0, "whole x units per thread");
-};
-
-// Grid: n_seqs x n_segs x (H P / 128) workgroups (a.n_row_blocks = H P / 128),
-// XCD-contiguous order.  Requires the vector path, N = 16 NT, P % 32 == 0 and
-// heads_per_group * P % 128 == 0.
-template <int NT>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-ssd_scan_wide_kernel(ScanArgs a) {
-    using S = SsdWideShape<NT>;
-    constexpr int N = S::N, CT = S::CT, LDN = S::LDN, TW = 2;
-    extern __shared__ float4 lds_raw[];
-    float *const lds = reinterpret_cast<float *>(lds_raw);
-
-    const int bid = blockIdx.x;
-    const int nb = a.n_blocks;
-    const int per = nb / kXcds, rem = nb % kXcds;
-    const int xcd = bid % kXcds, kx = bid / kXcds;
-    const int L = (xcd < rem) ? xcd * (per + 1) + kx : rem * (per + 1) + (xcd - rem) * per + kx;
-    const int slabs = a.n_row_blocks;
-    const int blk = L % slabs;
-    const int seg = (L / slabs) % a.n_segs;
-    const int s = L / (slabs * a.n_segs);
-
-    const int H = a.H, P = a.P, G = a.G;
-    const SegRange sr = segment_range(a, s, seg);
-    const int last = sr.n_real - 1;
-    if (seg > last) return;                          // past the sequence's segments
-    const int t_begin = sr.t_begin, t_end = sr.t_end;
-    const int n_tok = t_end - t_begin;
-    const bool from_slot = seg == 0 && a.fresh[s] == 0;
-    const bool from_carry = seg > 0;
-    if (from_slot && n_tok <= 0) return;             // empty resume: slot unchanged
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int tl = lane & 15, kq = lane >> 4;        // lane % 16, lane / 16
-    const int fr_wg = blk * S::RBW;                  // first flattened row h P + p of the workgroup
-    const int h_wg = fr_wg / P;                      // its first head
-    const int n_heads_wg = (fr_wg + S::RBW - 1) / P - h_wg + 1;   // heads it touches (<= MH: 32-row blocks)
-    const int fr0 = fr_wg + 32 * w;                  // first row of this wave
-    const int hw = fr0 / P - h_wg;                   // this wave's head, relative to h_wg
-    const int g = h_wg / a.heads_per_group;
-    const int64_t HPN = int64_t(H) * P * N;
-    float *const st_w = a.state + int64_t(a.slot[s]) * HPN + int64_t(fr0) * N;
-    float *const ws_w = a.ws_state + int64_t(s) * a.n_segs * HPN + int64_t(fr0) * N;
-    // wave 0, DPP row j = lane / 16: the scalars of head h_wg + j
-    const bool hrow_ok = kq < n_heads_wg;
-    const float A_j = (tid < 64 && hrow_ok) ? a.A[h_wg + kq] : 0.f;
-    const float bias_j = (tid < 64 && hrow_ok && a.dt_bias) ? a.dt_bias[h_wg + kq] : 0.f;
-
-    // ---- state h^T in accumulators: hacc[i][nt] register v of lane l holds
-    // h[row fr0 + 16 i + l%16][16 nt + 4 (l/16) + v]
-    f4m hacc[TW][NT];
-#pragma unroll
-    for (int i = 0; i < TW; ++i)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) hacc[i][nt] = f4m{0.f, 0.f, 0.f, 0.f};
-    if (from_slot || from_carry) {
-        const float *src = from_slot ? st_w : ws_w + int64_t(seg - 1) * HPN;
-#pragma unroll
-        for (int i = 0; i < TW; ++i)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const f4 v = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(
-                    src + int64_t(16 * i + tl) * N + 16 * nt + 4 * kq));
-                hacc[i][nt] = f4m{v.x, v.y, v.z, v.w};
-            }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-
-    // ---- chunk staging (as the narrow scan pass, one chunk ahead: two waves
-    // per SIMD leave no registers for a second set): chunk k committed to LDS
-    // buffer k & 1
-    constexpr int kNone = 0x7ffffff0;
-    const int x_tok = H * P * int(sizeof(float));
-    int vo_bc[S::U_BC], lo_bc[S::U_BC], vo_x[S::U_X];
-#pragma unroll
-    for (int u = 0; u < S::U_BC; ++u) {
-        const int q = u * kThreads + tid;            // unit = (token, 4-group)
-        const int tt = q / (N / 4), n0 = 4 * (q - tt * (N / 4));
-        vo_bc[u] = q < CT * N / 4 ? ((tt * G + g) * N + n0) * int(sizeof(float)) : kNone;
-        lo_bc[u] = q < CT * N / 4 ? tt * LDN + n0 : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < S::U_X; ++u) {
-        const int q = u * kThreads + tid;            // unit = (token, 4 rows)
-        const int tt = q / (S::RBW / 4), pi = 4 * (q - tt * (S::RBW / 4));
-        vo_x[u] = (tt * H * P + fr_wg + pi) * int(sizeof(float));
-    }
-    // dt: lane 16 j + t of wave 0 takes token t of head h_wg + j
-    const int vo_dt = (tid < 64 && hrow_ok) ? (tl * H + h_wg + kq) * int(sizeof(float)) : kNone;
-    struct Stage {
-        f4 pb[S::U_BC], pc[S::U_BC], px[S::U_X];
-        float pdt;
-    };
-    Stage stg;
-    auto issue_loads = [&](Stage &sg, int t0, int nt_) {
-        const __amdgpu_buffer_rsrc_t rb = buffer_of(a.B + int64_t(t0) * G * N, nt_ * G * N * int(sizeof(float)));
-        const __amdgpu_buffer_rsrc_t rc = buffer_of(a.C + int64_t(t0) * G * N, nt_ * G * N * int(sizeof(float)));
-        const __amdgpu_buffer_rsrc_t rx = buffer_of(a.x + int64_t(t0) * H * P, nt_ * x_tok);
-        const __amdgpu_buffer_rsrc_t rd = buffer_of(a.dt + int64_t(t0) * H, nt_ * H * int(sizeof(float)));
-#pragma unroll
-        for (int u = 0; u < S::U_BC; ++u) {
-            sg.pb[u] = buffer_load<4>(rb, vo_bc[u], 0);
-            sg.pc[u] = buffer_load<4>(rc, vo_bc[u], 0);
-        }
-#pragma unroll
-        for (int u = 0; u < S::U_X; ++u) sg.px[u] = buffer_load<4>(rx, vo_x[u], 0);
-        sg.pdt = buffer_load<1>(rd, vo_dt, 0);      // raw dt: transformed at the commit
-    };
-    // Deferred decay per head, as in the narrow scan pass; wave 0's lanes of
-    // DPP row j hold head j's sigma.
+    // Per head: wave 0's lanes of DPP row j hold head j's sigma.
     float sigma = 1.f;
     auto commit = [&](auto bufc, int nt_) {
         constexpr int buf = decltype(bufc)::value;
         float *base = lds + buf * S::BUF;
-        const Stage &sg = stg;
+        const Stage &sg = stg[buf % S::PF];
 #pragma unroll
         for (int u = 0; u < S::U_BC; ++u) {
             if (lo_bc[u] >= 0) {
@@ -851,7 +509,10 @@ ssd_scan_wide_kernel(ScanArgs a) {
         }
     };
 
-    // y of a chunk is finished during the next one (as the narrow scan pass)
+    // y of a chunk is finished during the next one: the G^T parts (written to
+    // LDS slot c & 1) are summed after the barrier that ends chunk c, scaled by
+    // the coefficients kept here and multiplied into the operand kept here,
+    // then added to the carried-in term:  y = (ysave + G' X) * yscale.
     f4m ysave[TW];
     float gopnd[TW][4], gcoef[4], yscale[4];
 #pragma unroll
@@ -913,7 +574,7 @@ ssd_scan_wide_kernel(ScanArgs a) {
 #pragma unroll
         for (int i = 0; i < TW; ++i)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) xr[i][v] = base[S::OFF_X + (4 * kq + v) * S::RBW + 32 * w + 16 * i + tl];
+            for (int v = 0; v < 4; ++v) xr[i][v] = base[S::OFF_X + (4 * kq + v) * S::RBW + 16 * TW * w + 16 * i + tl];
         float bup[4][NT];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -931,6 +592,7 @@ ssd_scan_wide_kernel(ScanArgs a) {
         for (int i = 0; i < NT; ++i) gpart = mfma16(gb[i], gc[i], gpart);
         reinterpret_cast<f4m *>(lds + S::OFF_GX + buf * S::GX)[w * 64 + lane] = gpart;
         __builtin_amdgcn_sched_barrier(0);
+        if (!wave_ok) return;                        // past the group: staging and G^T only
         if (c > 0) finish_y(buf ^ 1, c - 1);         // the previous chunk's parts are all in
         if (pre != 1.f) {                            // renormalise the deferred state
 #pragma unroll
@@ -1006,14 +668,15 @@ ssd_scan_wide_kernel(ScanArgs a) {
         issue_loads(sg, t0, min(CT, t_end - t0));
     };
     if (n_chunks > 0) {
-        issue_chunk(stg, 0);
+#pragma unroll
+        for (int k = 0; k < S::PF; ++k) issue_chunk(stg[k], k);
         commit(B0{}, min(CT, n_tok));
     }
     __syncthreads();
     auto step = [&](int c, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
         const int t1 = t_begin + (c + 1) * CT;
-        issue_chunk(stg, c + 1);
+        issue_chunk(stg[(buf + S::PF) % S::PF], c + S::PF);   // into the set chunk c just left
         __builtin_amdgcn_sched_barrier(0);
         compute(bufc, c);
         if (c + 1 < n_chunks) commit(std::integral_constant<int, buf ^ 1>{}, min(CT, t_end - t1));
@@ -1023,7 +686,7 @@ ssd_scan_wide_kernel(ScanArgs a) {
         step(c, B0{});
         if (c + 1 < n_chunks) step(c + 1, B1{});
     }
-    if (n_chunks > 0) finish_y((n_chunks - 1) & 1, n_chunks - 1);
+    if (n_chunks > 0 && wave_ok) finish_y((n_chunks - 1) & 1, n_chunks - 1);
 
     // ---- the sequence's end state after its last segment: h = sigma * accumulators
     if (seg == last) {
@@ -1031,6 +694,7 @@ ssd_scan_wide_kernel(ScanArgs a) {
         if (tid < 64 && tl == 0) sig_lds[kq] = sigma;
         __syncthreads();
         const float sg = sig_lds[hw];
+        if (wave_ok)
 #pragma unroll
         for (int i = 0; i < TW; ++i)
 #pragma unroll

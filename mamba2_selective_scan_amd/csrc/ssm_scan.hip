@@ -229,11 +229,32 @@ bool ssd_shape(const ssm_scan_dims *d) {
            int64_t(d->n_groups) * N * span < INT32_MAX;
 }
 bool ssd_eligible(const ssm_scan_dims *d, bool vec) { return vec && ssd_shape(d); }
-// The wide scan pass (two 16-row tiles per wave, 128 rows per workgroup) needs
-// each wave's 32 rows in one head and each group's rows in whole 128-row blocks.
-bool ssd_wide(const ssm_scan_dims *d) {
+// The scan pass takes two 16-row tiles per wave (128-row windows) when a
+// wave's 32 rows stay in one head, else one (64-row windows).
+int ssd_tiles(const ssm_scan_dims *d) { return d->head_dim % 32 == 0 ? 2 : 1; }
+// Scan-pass windows per B/C group (the last one may be cut short).
+int64_t ssd_windows(const ssm_scan_dims *d) {
     const int64_t group_rows = int64_t(d->n_heads / d->n_groups) * d->head_dim;
-    return d->head_dim % 32 == 0 && group_rows % ssm::SsdWideShape<8>::RBW == 0;
+    const int64_t rbw = 64 * ssd_tiles(d);
+    return (group_rows + rbw - 1) / rbw;
+}
+// Scan-pass kernel and its LDS floats for state tiles NT and tiles per wave TW.
+template <int NT, int TW>
+void ssd_scan_pick(const void **kern, int *lds) {
+    *kern = reinterpret_cast<const void *>(&ssm::ssd_scan_kernel<NT, TW>);
+    *lds = ssm::SsdScanShape<NT, TW>::lds_floats();
+}
+void ssd_scan_for(const ssm_scan_dims *d, const void **kern, int *lds) {
+    const int nt = d->d_state / 16;
+    if (ssd_tiles(d) == 2) {
+        if (nt == 2) ssd_scan_pick<2, 2>(kern, lds);
+        else if (nt == 4) ssd_scan_pick<4, 2>(kern, lds);
+        else ssd_scan_pick<8, 2>(kern, lds);
+    } else {
+        if (nt == 2) ssd_scan_pick<2, 1>(kern, lds);
+        else if (nt == 4) ssd_scan_pick<4, 1>(kern, lds);
+        else ssd_scan_pick<8, 1>(kern, lds);
+    }
 }
 
 SegPlan plan_segments(const ssm_scan_dims *d, const ShapeRow &row, int32_t n_seqs,
@@ -244,14 +265,11 @@ SegPlan plan_segments(const ssm_scan_dims *d, const ShapeRow &row, int32_t n_seq
     if (requested > 1) {
         K = requested;
     } else if (ssd_shape(d)) {
-        // matrix-core segments: a scan-pass workgroup of four waves per 128 rows
-        // (wide) or per 64 rows of a head; aim at two waves per SIMD (measured
-        // at 1 x 4096, H64 P64 N128 with the wide scan pass: 16 segments 0.169
-        // ms, 12: 0.194, 8: 0.176)
-        const int64_t rows = int64_t(d->n_heads) * d->head_dim;
-        const int64_t waves = int64_t(n_seqs) * ssm::kWaves *
-                              (ssd_wide(d) ? rows / ssm::SsdWideShape<8>::RBW
-                                           : d->n_heads * ((d->head_dim + 63) / 64));
+        // matrix-core segments: a scan-pass workgroup of four waves per window
+        // of a group's rows; aim at two waves per SIMD (measured at 1 x 4096,
+        // H64 P64 N128, two tiles per wave: 16 segments 0.169 ms, 12: 0.194,
+        // 8: 0.176)
+        const int64_t waves = int64_t(n_seqs) * ssm::kWaves * d->n_groups * ssd_windows(d);
         if (waves >= kSsdTargetWaves) return SegPlan{1, 0};
         K = (kSsdTargetWaves + waves - 1) / waves;
         K = std::min<int64_t>(K, max_seqlen / kMinSegTokens);
@@ -378,7 +396,7 @@ int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_
             const void *kern;
             int lds;
             int64_t blocks = per_seg * plan.n_segs;
-            int64_t slabs = sa.n_row_blocks;     // row blocks per head, or 128-row slabs
+            int64_t slabs = sa.n_row_blocks;     // row blocks per head, or windows per group
             if (states) {
                 blocks = per_seg * (plan.n_segs - 1);
                 lds = 0;                         // static LDS only
@@ -392,22 +410,10 @@ int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_
                 } else {
                     kern = reinterpret_cast<const void *>(&ssm::ssd_state_kernel<2, 1, kSsdStateGroup>);
                 }
-            } else if (ssd_wide(d)) {
-                kern = nt == 2 ? reinterpret_cast<const void *>(&ssm::ssd_scan_wide_kernel<2>)
-                     : nt == 4 ? reinterpret_cast<const void *>(&ssm::ssd_scan_wide_kernel<4>)
-                               : reinterpret_cast<const void *>(&ssm::ssd_scan_wide_kernel<8>);
-                lds = nt == 2 ? ssm::SsdWideShape<2>::lds_floats()
-                    : nt == 4 ? ssm::SsdWideShape<4>::lds_floats()
-                              : ssm::SsdWideShape<8>::lds_floats();
-                slabs = int64_t(d->n_heads) * d->head_dim / ssm::SsdWideShape<8>::RBW;
-                blocks = int64_t(n_seqs) * plan.n_segs * slabs;
             } else {
-                kern = nt == 2 ? reinterpret_cast<const void *>(&ssm::ssd_scan_kernel<2>)
-                     : nt == 4 ? reinterpret_cast<const void *>(&ssm::ssd_scan_kernel<4>)
-                               : reinterpret_cast<const void *>(&ssm::ssd_scan_kernel<8>);
-                lds = nt == 2 ? ssm::SsdShape<2>::lds_floats()
-                    : nt == 4 ? ssm::SsdShape<4>::lds_floats()
-                              : ssm::SsdShape<8>::lds_floats();
+                ssd_scan_for(d, &kern, &lds);
+                slabs = ssd_windows(d);
+                blocks = int64_t(n_seqs) * plan.n_segs * d->n_groups * slabs;
             }
             if (blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
             ScanArgs la = sa;
@@ -635,26 +641,18 @@ int ssm_scan_query_prefill_plan(const ssm_scan_dims *dims, int32_t n_seqs, int32
         const bool vec = out->vector_path != 0;
         if (ssd_eligible(dims, vec)) {
             // matrix-core segment scan: 4 lanes hold a row's N values (l % 16 is
-            // the row, l / 16 the quarter of each 16-wide state tile), 64 rows
-            // per workgroup, 16-token chunks
-            const int nt = dims->d_state / 16;
+            // the row, l / 16 the quarter of each 16-wide state tile), 16-token
+            // chunks
             out->lanes_per_row = 4;
             out->elems_per_lane = dims->d_state / 4;
             out->chunk_tokens = 16;
-            if (ssd_wide(dims)) {       // the scan pass: 128 rows (two tiles per wave)
-                out->rows_per_block = ssm::SsdWideShape<8>::RBW;
-                out->lds_bytes = (nt == 2 ? ssm::SsdWideShape<2>::lds_floats()
-                                : nt == 4 ? ssm::SsdWideShape<4>::lds_floats()
-                                          : ssm::SsdWideShape<8>::lds_floats()) * int(sizeof(float));
-                out->blocks = int64_t(n_seqs) * plan.n_segs * dims->n_heads * dims->head_dim /
-                              ssm::SsdWideShape<8>::RBW;
-            } else {
-                out->rows_per_block = 64;
-                out->lds_bytes = (nt == 2 ? ssm::SsdShape<2>::lds_floats()
-                                : nt == 4 ? ssm::SsdShape<4>::lds_floats()
-                                          : ssm::SsdShape<8>::lds_floats()) * int(sizeof(float));
-                out->blocks = int64_t(n_seqs) * plan.n_segs * dims->n_heads * ((dims->head_dim + 63) / 64);
-            }
+            // the scan pass: a window of 64 rows per tile per wave
+            const void *kern;
+            int lds;
+            ssd_scan_for(dims, &kern, &lds);
+            out->rows_per_block = 64 * ssd_tiles(dims);
+            out->lds_bytes = lds * int(sizeof(float));
+            out->blocks = int64_t(n_seqs) * plan.n_segs * dims->n_groups * ssd_windows(dims);
         } else {
             const Geo geo = geo_for(*row, Kind::kSegScan);
             out->chunk_tokens = geo.CT;

@@ -121,7 +121,7 @@ def test_no_kernel_uses_scratch():
     # 7 state-size classes x (vector, scalar) x (4 option sets x (prefill, decode)
     # + segment scan + correction) + 2 combine kernels + 6 matrix-core corrections
     # (3 contraction lengths, masked or not) + 3 x 3 matrix-core segment kernels
-    # (N 32, 64, 128; state pass, scan pass and the wide scan pass);
+    # (N 32, 64, 128; the state pass and the scan pass with one or two tiles per wave);
     # conv1d + SiLU: (vector, scalar) x (4 history lengths x (decode, prefill)
     # + 3 with snapshots); gated RMSNorm: (vector, scalar) x 6 row-length classes
     n_scan = 7 * 2 * (4 * 2 + 2) + 2 + 6 + 3 * 3
@@ -149,7 +149,7 @@ def test_prefill_plan_and_workspace():
     plus the decay arrays."""
     g = m.prefill_plan(64, 64, 128, 8, 1, 4096)
     assert g["segments"] == 16 and g["segment_tokens"] == 256 and g["blocks"] == 16 * 32
-    # the scan pass of this shape is the wide one: 128 rows (two heads) per workgroup
+    # the scan pass of this shape takes two tiles per wave: 128 rows (two heads) per workgroup
     assert g["chunk_tokens"] == 16 and g["rows_per_block"] == 128 and g["lds_bytes"] <= 64 * 1024
     ws = m.workspace_size(64, 64, 128, 8, 1, 4096, 4096)
     # + per-segment decay totals [1][16][64] and alignment
