@@ -32,13 +32,14 @@
 // then runs every segment from its true carried-in state, so the y it writes
 // is final and the last segment's end state is the sequence's.  No y is ever
 // read back.  The scan pass runs one workgroup per (sequence, time segment,
-// head, block of 64 rows): its four wavefronts own 16 rows each.  B, C and x of
-// a chunk are staged in LDS, double-buffered (rows padded so the strided
-// state-update reads are conflict-free), the per-token scalars are formed once
-// in wave 0, and G^T, the same for the four wavefronts, is formed a quarter
-// by each and summed through LDS.  G^T only feeds the chunk's own y (never the
-// state), so a chunk's y is finished during the next chunk, after the one
-// barrier per chunk that the staging needs anyway.
+// window of 64 TW rows of a B/C group): its four wavefronts own TW 16-row
+// tiles each.  B, C and x of a chunk are staged in LDS, double-buffered (rows
+// padded so the strided state-update reads are conflict-free), the per-token
+// scalars of each head are formed once in wave 0, and G^T, the same for the
+// four wavefronts, is formed a quarter by each and summed through LDS.  G^T
+// only feeds the chunk's own y (never the state), so a chunk's y is finished
+// during the next chunk, after the one barrier per chunk that the staging
+// needs anyway.
 #pragma once
 
 #include "scan_kernel.hpp"
