@@ -164,6 +164,10 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
     constexpr int CW = NKT / 4;                      // 16-column tiles per wave
     static_assert(NKT % 4 == 0, "Dk must be a multiple of 64");
     __shared__ f4m xch[2][2][kWaves][64];            // parity, (K S0^T, Q S0^T), wave, lane
+    // each wave's K tile of the chunk (16 tokens x its 16 CW key columns, rows
+    // padded to 16 CW + 4), written and read back transposed by the same wave
+    constexpr int LDK = 16 * CW + 4;
+    __shared__ __attribute__((aligned(16))) float k_lds[kWaves][16 * LDK];
     const GdnArgs &a = c.a;
 
     const int bid = blockIdx.x;
@@ -202,7 +206,6 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
     // one chunk's operands, loaded a chunk ahead
     struct Ops {
         f4 kr[CW], qr[CW];        // K, Q row l%16 at columns i0 + 16 cc + 4 (l/16) + v
-        float kt[CW][4];          // K[4 (l/16) + v][i0 + 16 cc + l%16]
         float vv[4];              // V[4 (l/16) + v][j0 + l%16]
         f4 trow, mrow;            // T, M row l%16 at columns 4 (l/16) + v
         f4 gam, beta, bgam, wl;   // token 4 (l/16) + v
@@ -210,7 +213,6 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
     };
     const int kq_bytes = Hk * Dk * int(sizeof(float)), v_bytes = Hv * Dv * int(sizeof(float));
     const int vo_kq = (tl * Hk * Dk + kh * Dk + i0 + 4 * kq) * int(sizeof(float));
-    const int vo_kt = (4 * kq * Hk * Dk + kh * Dk + i0 + tl) * int(sizeof(float));
     const int vo_v = (4 * kq * Hv * Dv + vh * Dv + j0 + tl) * int(sizeof(float));
     auto load = [&](Ops &o, int ch) {
         const int t0 = c0 + 16 * ch;
@@ -222,8 +224,6 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
         for (int cc = 0; cc < CW; ++cc) {
             o.kr[cc] = buffer_load<4>(rk, vo_kq + 64 * cc, 0);
             o.qr[cc] = buffer_load<4>(rq, vo_kq + 64 * cc, 0);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) o.kt[cc][v] = buffer_load<1>(rk, vo_kt + 64 * cc, v * kq_bytes);
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) o.vv[v] = buffer_load<1>(rv, vo_v, v * v_bytes);
@@ -238,6 +238,16 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
     };
     const int vo_y = (4 * kq * Hv * Dv + vh * Dv + j0 + tl) * int(sizeof(float));
     auto chunk_step = [&](const Ops &o, int ch, int par) {
+        // K transposed for the state update, through this wave's LDS tile:
+        // kt[cc][v] = K[4 (l/16) + v][i0 + 16 cc + l%16]
+        float *const kw = k_lds[w];
+#pragma unroll
+        for (int cc = 0; cc < CW; ++cc) *reinterpret_cast<f4 *>(kw + tl * LDK + 16 * cc + 4 * kq) = o.kr[cc];
+        float kt[CW][4];
+#pragma unroll
+        for (int cc = 0; cc < CW; ++cc)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) kt[cc][v] = kw[(4 * kq + v) * LDK + 16 * cc + tl];
         // this wave's parts of K S0^T and Q S0^T over its key columns
         f4m ks = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -293,7 +303,7 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
         for (int cc = 0; cc < CW; ++cc) {
             hacc[cc] *= o.glast;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) hacc[cc] = mfma16(wl[v] * o.kt[cc][v], dl[v], hacc[cc]);
+            for (int v = 0; v < 4; ++v) hacc[cc] = mfma16(wl[v] * kt[cc][v], dl[v], hacc[cc]);
         }
     };
 
