@@ -140,6 +140,46 @@ def test_single_hip_runtime():
     assert len(m.hip_runtimes_loaded()) == 1, m.hip_runtimes_loaded()
 
 
+@pytest.mark.parametrize("H,G,P", [(64, 8, 64), (16, 2, 32), (4, 1, 96), (4, 2, 96), (2, 1, 256),
+                                   (4, 2, 16), (4, 2, 48), (4, 2, 80), (6, 3, 160), (8, 1, 112),
+                                   (3, 3, 32), (12, 4, 208)])
+def test_scan_pass_windows(H, G, P):
+    """The matrix-core scan pass's geometry, modelled on the host: a workgroup
+    owns a window of 64 TW rows of a group's flattened (head, row) space, cut at
+    the group's end, and wave w the TW 16-row tiles from row 16 TW w (TW = 2
+    when P % 32 == 0).  Every row of every group is covered by exactly one wave;
+    a wave's tiles stay in one head; a window touches at most four heads (the
+    per-head scalar rows of wave 0); the library plans the same window size and
+    grid (16 segments forced, one sequence)."""
+    N, n_segs = 128, 16
+    tw = 2 if P % 32 == 0 else 1
+    rbw = 64 * tw
+    hpg = H // G
+    group_rows = hpg * P
+    wpg = -(-group_rows // rbw)
+    covered = np.zeros(H * P, np.int32)
+    for g in range(G):
+        group_end = (g + 1) * group_rows
+        for wb in range(wpg):
+            fr_wg = g * group_rows + wb * rbw
+            rows_wg = min(rbw, group_end - fr_wg)
+            assert rows_wg > 0 and rows_wg % (16 * tw) == 0
+            h_wg = fr_wg // P
+            n_heads = (fr_wg + rows_wg - 1) // P - h_wg + 1
+            assert 1 <= n_heads <= 4 and (fr_wg + rows_wg - 1) // P < (g + 1) * hpg
+            for w in range(4):
+                fr0 = fr_wg + 16 * tw * w
+                if fr0 >= fr_wg + rows_wg:
+                    continue
+                assert fr0 // P == (fr0 + 16 * tw - 1) // P          # one head
+                assert 0 <= fr0 // P - h_wg < n_heads
+                covered[fr0:fr0 + 16 * tw] += 1
+    assert np.all(covered == 1)
+    plan = m.prefill_plan(H, P, N, G, 1, 16 * 256, n_segs)
+    assert plan["rows_per_block"] == rbw
+    assert plan["blocks"] == plan["segments"] * G * wpg
+
+
 def test_prefill_plan_and_workspace():
     """The headline prefill (1 x 4096 at H64 P64 N128 G8) gives the wide
     matrix-core scan pass 128 wavefronts per segment, so automatic planning
