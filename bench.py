@@ -7,11 +7,13 @@ resuming state.  A step is one ssm_scan_decode call.  Consecutive steps use
 state comes from HBM, not from the 256 MB Infinity Cache.  The 16 steps of one
 rotation are captured once in a HIP graph and replayed, so host launch
 overhead does not pad the step time.  Also measured and reported beside it:
-the 1 x 4096-token prefill at the same geometry (fresh state), eager launches.
+the 1 x 4096-token prefill at the same geometry (fresh state, eager launches,
+the automatic time split on the matrix cores), the secondary scan workloads,
+the ops beside the scan (conv1d + SiLU, gated RMSNorm) and the gated delta rule.
 
 Prints one JSON line.  Times come from HIP events on the stream the kernels run
 on; the roofline objects use algorithmic bytes (decode, HBM-bound) and
-algorithmic flops (prefill, FP32 VALU-bound).
+algorithmic flops (prefill, bound by the FP32 matrix cores).
 """
 from __future__ import annotations
 
