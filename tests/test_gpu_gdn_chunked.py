@@ -61,6 +61,30 @@ def test_gdn_chunked_varlen(ssm, orc, Dk, Dv, Hv, Hk):
     assert_gdn_parity(case, y, st, y32, s32, label=case.name)
 
 
+def test_gdn_chunked_decay_regimes(ssm, orc):
+    """Eight value heads in four decay regimes over a long and a short sequence
+    (one resumed): almost none (g = -0.001), moderate (-0.5), steep (-20: the
+    decay from a chunk's start underflows fp32 within the chunk, so every
+    factor the chunked form uses must come from differences of running sums,
+    never a quotient of two decays) and bursts (-30 on 5% of the tokens, -0.01
+    elsewhere)."""
+    import dataclasses
+    case = ssm_inputs.make_gdn_case(8, 4, 64, 32, [300, 130], [1, 0], seed=751,
+                                    name="gdn_decay_regimes")
+    rng = np.random.Generator(np.random.PCG64(7511))
+    g = case.g.copy()
+    T = g.shape[0]
+    g[:, 0:2] = -0.001
+    g[:, 2:4] = -0.5
+    g[:, 4:6] = -20.0
+    g[:, 6:8] = np.where(rng.uniform(size=(T, 2)) < 0.05, -30.0, -0.01)
+    case = dataclasses.replace(case, g=g.astype(np.float32))
+    y, st = run_gdn_gpu(case, "prefill_ws")
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(st))
+    y32, s32 = orc.gdn_case(case)
+    assert_gdn_parity(case, y, st, y32, s32, label=case.name)
+
+
 def test_gdn_chunked_matches_per_token(ssm, orc):
     """The chunked and the per-token kernels on the same batch agree within the bar."""
     case = ssm_inputs.make_gdn_case(8, 4, 128, 64, [300, 77, 160], [1, 0, 0], seed=733,
