@@ -332,19 +332,20 @@ def test_split_prefill_shapes(ssm, orc, N, P):
 
 
 @pytest.mark.parametrize("H,P,N,G", [(4, 96, 64, 1), (8, 32, 32, 2), (2, 256, 32, 1), (4, 64, 128, 2),
-                                     (4, 128, 64, 2)])
+                                     (4, 128, 64, 2), (3, 32, 64, 3), (2, 16, 32, 2)])
 def test_split_prefill_wide_layouts(ssm, orc, H, P, N, G):
-    """Shapes whose scan pass runs 128 rows per workgroup (P % 32 == 0 and each
-    group's rows in whole blocks of 128): windows that straddle two heads
+    """Scan-pass windows over a group's rows: windows that straddle two heads
     (P 96), four heads per workgroup (P 32), two workgroups per head (P 256),
-    every state size; fresh, resumed and empty sequences."""
+    a group of one 32-row head (one wave of the window works) and of one
+    16-row head (one tile per wave, one wave works); every state size;
+    fresh, resumed and empty sequences."""
     lengths = [0, 1, 77, 200, 31]
     case = ssm_inputs.make_case(H, P, N, G, lengths, [1, 0, 0, 1, 0], seed=500 + H + P + N,
                                 slots=[6, 0, 2, 5, 3], n_slots=8, poison_fresh=True,
                                 sentinel_unused=True, name=f"wide_H{H}_P{P}_N{N}_G{G}")
     plan = ssm.prefill_plan(H, P, N, G, len(lengths), 200, 4)
     say(f"wide layout H={H} P={P} N={N} G={G}: {plan}")
-    assert plan["rows_per_block"] == 128
+    assert plan["rows_per_block"] == (128 if P % 32 == 0 else 64)
     y, st = run_gpu(case, "prefill_ws", segments=4)
     y32, st32 = orc.scan_case(case, precision="f32")
     assert_parity(case, y, st, y32, st32)
