@@ -103,7 +103,11 @@ int dispatch(const GdnArgs &a, int64_t units, bool vec, bool decode, hipStream_t
 // nothing from chunks of 16), no snapshots, 16-byte aligned arrays.
 constexpr int kGdnChunkMinLen = 32;
 bool chunk_shape(const ssm_gdn_dims *d) {
-    return (d->d_k == 64 || d->d_k == 128) && d->d_v % 16 == 0;
+    // a chunk's rows of q, k and v (16 tokens) must fit 32-bit buffer offsets
+    const int64_t chunk_bytes = 16 * int64_t(sizeof(float));
+    return (d->d_k == 64 || d->d_k == 128) && d->d_v % 16 == 0 &&
+           int64_t(d->n_k_heads) * d->d_k * chunk_bytes < INT32_MAX &&
+           int64_t(d->n_v_heads) * d->d_v * chunk_bytes < INT32_MAX;
 }
 size_t chunk_ws_bytes(const ssm_gdn_dims *d, int32_t n_seqs, int32_t max_seqlen) {
     const size_t chunks = (size_t(max_seqlen) + 15) / 16;

@@ -317,6 +317,10 @@ def test_gdn_workspace_size():
     assert size(4, 2, 128, 64, 3, 31) == 0       # short sequences: per-token kernel
     assert size(4, 2, 100, 64, 3, 500) == 0      # key width without a chunked form
     assert size(4, 2, 128, 24, 3, 500) == 0      # value rows not in 16-row tiles
+    # a chunk's rows of v (or of q, k) past 32-bit buffer offsets: per-token kernel
+    assert size(1024, 1024, 128, 16384, 1, 64) == 4 * 1024 * 592 * 4
+    assert size(2048, 2048, 128, 16384, 1, 64) == 0
+    assert size(262144, 262144, 128, 16, 1, 64) == 0
     b = ctypes.c_size_t()
     lib = m.lib()
     assert lib.ssm_gdn_prefill_workspace_size(None, 1, 64, ctypes.byref(b)) == m.SSM_ERR_NULL
