@@ -15,9 +15,13 @@
  *     delta = (v[j] - pred) * beta
  *     row   = row + k * delta
  *     y[j]  = scale * (row . q)
- * q and k are used as given (the page L2-normalises them before the
- * recurrence); g is the log decay and beta the write strength, both per
- * (token, value head).  The kernel forms y as scale * (row_decayed . q +
+ * q and k are used as given, at any length (the page L2-normalises them in
+ * a kernel of its own before the recurrence); no kernel here assumes unit
+ * rows.  The update row <- row (I - beta k k^T) + beta v k^T is a contraction
+ * while 0 <= beta |k|^2 <= 2, which unit keys with beta in [0, 1] satisfy;
+ * beyond that the state can grow without bound, in the recurrence itself.
+ * g is the log decay and beta the write strength, both per (token, value
+ * head).  The kernel forms y as scale * (row_decayed . q +
  * delta * (k . q)), which equals the above in exact arithmetic.
  *
  * Conventions are those of ssm_scan.h: DEVICE arrays owned by the caller,

@@ -21,9 +21,10 @@
  *    layouts written beside each argument, owned by the caller.  float arrays
  *    are fp32 and must be 4-byte aligned; 16-byte alignment together with
  *    d_state % 4 == 0 and head_dim % 4 == 0 selects the vector (float4) path.
- *  - The library allocates nothing and never synchronizes.  Work is enqueued
- *    on `stream` (a hipStream_t; NULL = the null stream) and the call returns
- *    as soon as it is enqueued.
+ *  - The library allocates nothing and never synchronizes (the one exception
+ *    is the debugging aid ssm_scan_check_metadata, which waits for its
+ *    copies).  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and the call returns as soon as it is enqueued.
  *  - Return value: SSM_OK (0) or a negative SSM_ERR_* code.  Argument errors
  *    are detected on the host before anything is enqueued; then nothing on the
  *    device has been touched.  No C++ exception crosses the ABI.
@@ -50,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 1
+#define SSM_SCAN_ABI_VERSION 2
 #define SSM_SCAN_MAX_D_STATE 1024
 
 enum ssm_scan_status {
@@ -199,14 +200,28 @@ int ssm_scan_last_hip_error(void);
 const char *ssm_scan_last_hip_error_string(void);
 
 /*
- * Debug / test helper on HOST arrays (copy them from the device first):
- * checks cu_seqlens[0] == 0, non-decreasing, cu_seqlens[n_seqs] == n_tokens,
- * every slot in [0, n_slots) and no slot named twice.  Returns SSM_OK,
- * SSM_ERR_NULL, SSM_ERR_DIMS or SSM_ERR_METADATA.  cu_seqlens may be NULL to
- * check the slots of a decode batch only.  Touches no device.
+ * Debug / test helper on the DEVICE metadata a prefill or decode call would
+ * take: copies cu_seqlens (n_seqs + 1 entries; NULL to check the slots of a
+ * decode batch only) and slot (n_seqs entries) to the host on `stream`, waits
+ * for the stream, then checks what ssm_scan_check_metadata_host checks.  It
+ * synchronizes, so it is for tests and debugging, never for the hot path
+ * (the scans themselves do not check array contents).  Returns SSM_OK,
+ * SSM_ERR_NULL (slot NULL with n_seqs > 0), SSM_ERR_DIMS (a negative count),
+ * SSM_ERR_METADATA, or SSM_ERR_LAUNCH if a copy failed (then
+ * ssm_scan_last_hip_error() tells why).  n_seqs == 0 returns SSM_OK at once.
  */
 int ssm_scan_check_metadata(int32_t n_seqs, int32_t n_tokens, const int32_t *cu_seqlens,
-                            const int32_t *slot, int32_t n_slots);
+                            const int32_t *slot, int32_t n_slots, void *stream);
+
+/*
+ * The same checks on HOST arrays: cu_seqlens[0] == 0, non-decreasing,
+ * cu_seqlens[n_seqs] == n_tokens, every slot in [0, n_slots) and no slot
+ * named twice.  Returns SSM_OK, SSM_ERR_NULL, SSM_ERR_DIMS or
+ * SSM_ERR_METADATA.  cu_seqlens may be NULL to check the slots of a decode
+ * batch only.  Touches no device.
+ */
+int ssm_scan_check_metadata_host(int32_t n_seqs, int32_t n_tokens, const int32_t *cu_seqlens,
+                                 const int32_t *slot, int32_t n_slots);
 
 /* The launch shape the library picks for a call (for logs and tests). */
 typedef struct ssm_scan_geometry {

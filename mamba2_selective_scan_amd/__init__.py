@@ -92,8 +92,10 @@ _lib.ssm_scan_last_hip_error.argtypes = []
 _lib.ssm_scan_last_hip_error.restype = ctypes.c_int
 _lib.ssm_scan_last_hip_error_string.argtypes = []
 _lib.ssm_scan_last_hip_error_string.restype = ctypes.c_char_p
-_lib.ssm_scan_check_metadata.argtypes = [_i32, _i32, _vp, _vp, _i32]
+_lib.ssm_scan_check_metadata.argtypes = [_i32, _i32, _vp, _vp, _i32, _vp]
 _lib.ssm_scan_check_metadata.restype = ctypes.c_int
+_lib.ssm_scan_check_metadata_host.argtypes = [_i32, _i32, _vp, _vp, _i32]
+_lib.ssm_scan_check_metadata_host.restype = ctypes.c_int
 _lib.ssm_scan_query_geometry.argtypes = [ctypes.POINTER(Dims), _i32, _i32, _i32,
                                          ctypes.POINTER(Geometry)]
 _lib.ssm_scan_query_geometry.restype = ctypes.c_int
@@ -216,14 +218,27 @@ def workspace_size(H, P, N, G, n_seqs, n_tokens, max_seqlen, segments=0) -> int:
     return int(b.value)
 
 
-def check_metadata(cu_seqlens, slot, n_tokens: int, n_slots: int) -> int:
-    """Check metadata given as host arrays (numpy/torch CPU int32) or None for
-    cu_seqlens; returns the status code (SSM_OK or SSM_ERR_*)."""
+def check_metadata(cu_seqlens, slot, n_tokens: int, n_slots: int, stream=None) -> int:
+    """Check a batch's metadata; returns the status code (SSM_OK or SSM_ERR_*).
+
+    ``slot`` as a CUDA int32 tensor (and ``cu_seqlens`` as one, or None for a
+    decode batch): ``ssm_scan_check_metadata`` copies them to the host on
+    ``stream`` (default: the current stream) and waits.  Host arrays (numpy
+    or CPU tensors): ``ssm_scan_check_metadata_host``."""
     import numpy as np
+    if hasattr(slot, "is_cuda") and slot.is_cuda:
+        import torch
+        dev = slot.device
+        slot_p = _dev_ptr(slot, torch.int32, "slot", dev)
+        cu_p = None if cu_seqlens is None else _dev_ptr(cu_seqlens, torch.int32, "cu_seqlens", dev)
+        if cu_seqlens is not None and tuple(cu_seqlens.shape) != (int(slot.shape[0]) + 1,):
+            raise ValueError("cu_seqlens must have n_seqs + 1 entries")
+        return int(_lib.ssm_scan_check_metadata(int(slot.shape[0]), int(n_tokens), cu_p, slot_p,
+                                                int(n_slots), _stream_handle(stream, dev)))
     slot_h = np.ascontiguousarray(_to_host(slot), dtype=np.int32)
     cu_h = None if cu_seqlens is None else np.ascontiguousarray(_to_host(cu_seqlens),
                                                                  dtype=np.int32)
-    return int(_lib.ssm_scan_check_metadata(
+    return int(_lib.ssm_scan_check_metadata_host(
         int(slot_h.shape[0]), int(n_tokens),
         None if cu_h is None else cu_h.ctypes.data, slot_h.ctypes.data, int(n_slots)))
 

@@ -11,6 +11,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "correct_mfma.hpp"
 #include "scan_kernel.hpp"
@@ -572,8 +573,8 @@ const char *ssm_scan_last_hip_error_string(void) {
     return t_last_hip_error == hipSuccess ? "no error" : hipGetErrorString(t_last_hip_error);
 }
 
-int ssm_scan_check_metadata(int32_t n_seqs, int32_t n_tokens, const int32_t *cu_seqlens,
-                            const int32_t *slot, int32_t n_slots) {
+int ssm_scan_check_metadata_host(int32_t n_seqs, int32_t n_tokens, const int32_t *cu_seqlens,
+                                 const int32_t *slot, int32_t n_slots) {
     if (n_seqs < 0 || n_tokens < 0 || n_slots < 0) return SSM_ERR_DIMS;
     if (n_seqs == 0) return SSM_OK;
     if (!slot) return SSM_ERR_NULL;
@@ -604,6 +605,26 @@ int ssm_scan_check_metadata(int32_t n_seqs, int32_t n_tokens, const int32_t *cu_
     }
     delete[] heap;
     return rc;
+}
+
+int ssm_scan_check_metadata(int32_t n_seqs, int32_t n_tokens, const int32_t *cu_seqlens,
+                            const int32_t *slot, int32_t n_slots, void *stream_ptr) {
+    if (n_seqs < 0 || n_tokens < 0 || n_slots < 0) return SSM_ERR_DIMS;
+    if (n_seqs == 0) return SSM_OK;
+    if (!slot) return SSM_ERR_NULL;
+    // Host copies (a debugging aid: this call synchronizes by design).
+    std::vector<int32_t> cu_h(cu_seqlens ? size_t(n_seqs) + 1 : 0);
+    std::vector<int32_t> slot_h(static_cast<size_t>(n_seqs));
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    hipError_t err = hipMemcpyAsync(slot_h.data(), slot, slot_h.size() * sizeof(int32_t),
+                                    hipMemcpyDeviceToHost, stream);
+    if (err == hipSuccess && cu_seqlens)
+        err = hipMemcpyAsync(cu_h.data(), cu_seqlens, cu_h.size() * sizeof(int32_t),
+                             hipMemcpyDeviceToHost, stream);
+    if (err == hipSuccess) err = hipStreamSynchronize(stream);
+    if (err != hipSuccess) return hip_fail(err, SSM_ERR_LAUNCH);
+    return ssm_scan_check_metadata_host(n_seqs, n_tokens, cu_seqlens ? cu_h.data() : nullptr,
+                                        slot_h.data(), n_slots);
 }
 
 int ssm_scan_query_geometry(const ssm_scan_dims *dims, int32_t n_seqs, int32_t decode,

@@ -27,6 +27,20 @@ _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
 
 
+def default_threads() -> int:
+    """Host threads the oracle uses when not told: the CPUs this process may
+    run on, capped by OMP_NUM_THREADS when that is set (a shared host's share
+    can be far below what os.cpu_count() reports)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
 def _ptr(a: np.ndarray, t):
     return a.ctypes.data_as(t)
 
@@ -99,7 +113,7 @@ class Oracle:
             bias = np.ascontiguousarray(dt_bias, dtype=np.float32)
             assert bias.shape == (H,)
         if threads is None:
-            threads = os.cpu_count() or 1
+            threads = default_threads()
         if precision == "f32":
             dtype, fn, fp = np.float32, self.lib.ssm_oracle_scan_opt_f32, _f32p
         elif precision == "f64":
@@ -143,7 +157,7 @@ class Oracle:
         assert cu.shape[0] == n_seqs + 1 and w.shape == (D, K) and x.shape == (T, D)
         assert conv_state.ndim == 3 and conv_state.shape[1:] == (D, K - 1)
         if threads is None:
-            threads = os.cpu_count() or 1
+            threads = default_threads()
         if precision == "f32":
             dtype, fn, fp = np.float32, self.lib.ssm_oracle_conv1d_silu_f32, _f32p
         elif precision == "f64":
@@ -175,7 +189,7 @@ class Oracle:
         assert y.shape == z.shape and y.shape[-1] == L
         n_rows = y.size // L
         if threads is None:
-            threads = os.cpu_count() or 1
+            threads = default_threads()
         if precision == "f32":
             out = np.zeros(y.shape, dtype=np.float32)
             rc = self.lib.ssm_oracle_gated_rmsnorm_f32(n_rows, L, _ptr(y, _f32p), _ptr(z, _f32p),
@@ -214,7 +228,7 @@ class Oracle:
         assert g.shape == (T, Hv) and beta.shape == (T, Hv)
         assert state.ndim == 4 and state.shape[1:] == (Hv, Dv, Dk)
         if threads is None:
-            threads = os.cpu_count() or 1
+            threads = default_threads()
         if precision == "f32":
             dtype, fn, fp = np.float32, self.lib.ssm_oracle_gdn_f32, _f32p
         elif precision == "f64":

@@ -315,8 +315,8 @@ class GdnCase:
     cu_seqlens: np.ndarray
     slot: np.ndarray
     fresh: np.ndarray
-    q: np.ndarray                # f32 [T, Hk, Dk], unit rows
-    k: np.ndarray                # f32 [T, Hk, Dk], unit rows
+    q: np.ndarray                # f32 [T, Hk, Dk], unit rows unless drawn otherwise
+    k: np.ndarray                # f32 [T, Hk, Dk], unit rows unless drawn otherwise
     v: np.ndarray                # f32 [T, Hv, Dv]
     g: np.ndarray                # f32 [T, Hv], log decay
     beta: np.ndarray             # f32 [T, Hv]
@@ -344,7 +344,13 @@ def _unit_rows(a):
 
 
 def make_gdn_case(Hv, Hk, Dk, Dv, lengths, fresh, seed, *, slots=None, n_slots=None,
-                  state_std=0.5, poison_fresh=False, sentinel_unused=False, name="") -> GdnCase:
+                  state_std=0.5, poison_fresh=False, sentinel_unused=False, qk_norm=None,
+                  beta=None, name="") -> GdnCase:
+    """Draw one packed delta-rule batch.  By default q and k rows have unit
+    length.  ``qk_norm=(lo, hi)`` rescales every q and k row to a length
+    drawn from U[lo, hi]; ``beta`` (a float) replaces the drawn write
+    strengths with that constant.  Both are drawn or applied after every
+    default draw, so cases without them keep their bits."""
     lengths = np.asarray(lengths, dtype=np.int32)
     fresh = np.asarray(fresh, dtype=np.uint8)
     n_seqs = lengths.shape[0]
@@ -362,9 +368,14 @@ def make_gdn_case(Hv, Hk, Dk, Dv, lengths, fresh, seed, *, slots=None, n_slots=N
     q = _unit_rows(rng.standard_normal((T, Hk, Dk), dtype=np.float32))
     k = _unit_rows(rng.standard_normal((T, Hk, Dk), dtype=np.float32))
     v = rng.standard_normal((T, Hv, Dv), dtype=np.float32)
-    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((T, Hv))))).astype(np.float32)
+    beta_drawn = (1.0 / (1.0 + np.exp(-rng.standard_normal((T, Hv))))).astype(np.float32)
     state = rng.standard_normal((n_slots, Hv, Dv, Dk), dtype=np.float32)
     state *= np.float32(state_std)
+    if qk_norm is not None:
+        lo, hi = qk_norm
+        q = (q * rng.uniform(lo, hi, size=(T, Hk, 1))).astype(np.float32)
+        k = (k * rng.uniform(lo, hi, size=(T, Hk, 1))).astype(np.float32)
+    beta_arr = beta_drawn if beta is None else np.full((T, Hv), beta, dtype=np.float32)
     if sentinel_unused:
         used = np.zeros(n_slots, dtype=bool)
         used[slots] = True
@@ -375,7 +386,7 @@ def make_gdn_case(Hv, Hk, Dk, Dv, lengths, fresh, seed, *, slots=None, n_slots=N
             if fresh[s]:
                 state[slots[s]] = np.nan
     return GdnCase(Hv=Hv, Hk=Hk, Dk=Dk, Dv=Dv, lengths=lengths, cu_seqlens=cu, slot=slots,
-                   fresh=fresh, q=q, k=k, v=v, g=g, beta=beta, state=state,
+                   fresh=fresh, q=q, k=k, v=v, g=g, beta=beta_arr, state=state,
                    scale=float(np.float32(1.0 / math.sqrt(Dk))), seed=seed, name=name)
 
 

@@ -65,6 +65,46 @@ def pin_gdn_matrix_form(orc):
         assert rel_err(y32, y_ref) <= 1e-5 and rel_err(st32[used], st_ref[used]) <= 1e-5, seed
 
 
+def pin_gdn_matrix_form_general_keys(orc):
+    """Keys and queries of any length (rows rescaled to norms in [0.25, 1.4])
+    and write strengths 0, 1/2, 1 and drawn: the oracle still follows the
+    matrix form.  The recurrence takes q and k as given, so nothing in it may
+    assume unit rows (a kernel that dropped k.k or normalised would fail)."""
+    for seed, beta in ((21, None), (22, 0.0), (23, 0.5), (24, 1.0)):
+        n = 5
+        slots = np.random.Generator(np.random.PCG64(seed + 9)).permutation(n + 2)[:n]
+        case = ssm_inputs.make_gdn_case(4, 2, 6, 3, [5, 1, 0, 8, 3], [1, 0, 1, 0, 0], seed,
+                                        slots=slots.astype(np.int32), n_slots=n + 2,
+                                        sentinel_unused=True, qk_norm=(0.25, 1.4), beta=beta)
+        norms = np.linalg.norm(case.k.astype(np.float64), axis=-1)
+        assert norms.min() < 0.6 and norms.max() > 1.1, "rows must not be unit length"
+        y_ref, st_ref = matrix_form(case)
+        used = np.unique(case.slot)
+        y64, st64 = orc.gdn_case(case, precision="f64", threads=2)
+        assert rel_err(y64, y_ref) <= 1e-12 and rel_err(st64[used], st_ref[used]) <= 1e-12, seed
+        y32, st32 = orc.gdn_case(case, precision="f32", threads=2)
+        assert rel_err(y32, y_ref) <= 1e-5 and rel_err(st32[used], st_ref[used]) <= 1e-5, seed
+
+
+def pin_gdn_key_length_overwrite(orc):
+    """beta = 1 and a key of length c along e_m: the write leaves the stored
+    column at (1 - c^2) times its old value plus c times v (the matrix form
+    with k k^T = c^2 e_m e_m^T), exactly for c = 2 and small integers."""
+    Dk, Dv, m, c = 4, 3, 2, 2.0
+    state0 = np.arange(1, Dv * Dk + 1, dtype=np.float32).reshape(1, 1, Dv, Dk)
+    k = np.zeros((1, 1, Dk), np.float32)
+    k[0, 0, m] = c
+    q = np.zeros((1, 1, Dk), np.float32)
+    q[0, 0, m] = 1.0
+    v = np.array([[[3.0, -1.0, 5.0]]], np.float32)
+    y, st = orc.gdn(1, 1, Dk, Dv, [0, 1], [0], [0], q, k, v, np.zeros((1, 1), np.float32),
+                    np.ones((1, 1), np.float32), 1.0, state0, precision="f32", threads=1)
+    want = state0[0, 0].copy()
+    want[:, m] = (1.0 - c * c) * state0[0, 0, :, m] + c * v[0, 0]
+    assert np.array_equal(st[0, 0], want)
+    assert np.array_equal(y[0, 0], want[:, m])
+
+
 def pin_gdn_tiny_workload_matrix_form(orc):
     case = ssm_inputs.gdn_workload("tiny")
     y_ref, st_ref = matrix_form(case)
@@ -226,7 +266,8 @@ def pin_gdn_thread_count(orc):
     assert np.array_equal(y1, y3) and np.array_equal(s1, s3, equal_nan=True)
 
 
-GDN_PINS = [pin_gdn_matrix_form, pin_gdn_tiny_workload_matrix_form, pin_gdn_overwrite,
+GDN_PINS = [pin_gdn_matrix_form, pin_gdn_matrix_form_general_keys, pin_gdn_key_length_overwrite,
+            pin_gdn_tiny_workload_matrix_form, pin_gdn_overwrite,
             pin_gdn_pure_decay, pin_gdn_single_token, pin_gdn_split_resume,
             pin_gdn_batch_independence, pin_gdn_gqa_interleaved, pin_gdn_slot_hygiene,
             pin_gdn_snapshots, pin_gdn_thread_count]

@@ -18,6 +18,7 @@ def test_exports_every_declared_symbol():
     names = m.header_symbols()
     assert set(names) == {"ssm_scan_prefill", "ssm_scan_decode", "ssm_scan_strerror",
                           "ssm_scan_version", "ssm_scan_check_metadata",
+                          "ssm_scan_check_metadata_host",
                           "ssm_scan_query_geometry", "ssm_scan_last_hip_error",
                           "ssm_scan_last_hip_error_string", "ssm_scan_prefill_ws",
                           "ssm_scan_prefill_workspace_size", "ssm_scan_query_prefill_plan",
@@ -30,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert m.version() == 1
+    assert m.version() == 2
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert m.strerror(code) and "unknown" not in m.strerror(code)
     assert "unknown" in m.strerror(-99)
@@ -94,7 +95,11 @@ def test_check_metadata():
     assert m.check_metadata(np.array([0, 3, 2, 5]), np.array([2, 0, 1]), 5, 3) == m.SSM_ERR_METADATA
     assert m.check_metadata(None, np.arange(300)[::-1], 0, 300) == m.SSM_OK       # decode, big
     assert m.check_metadata(None, np.r_[np.arange(200), 7], 0, 300) == m.SSM_ERR_METADATA
-    assert m.lib().ssm_scan_check_metadata(2, 0, None, None, 4) == m.SSM_ERR_NULL
+    assert m.lib().ssm_scan_check_metadata_host(2, 0, None, None, 4) == m.SSM_ERR_NULL
+    # the device form rejects sizes and a missing slot array before any copy
+    assert m.lib().ssm_scan_check_metadata(2, 0, None, None, 4, None) == m.SSM_ERR_NULL
+    assert m.lib().ssm_scan_check_metadata(-1, 0, None, None, 4, None) == m.SSM_ERR_DIMS
+    assert m.lib().ssm_scan_check_metadata(0, 0, None, None, 4, None) == m.SSM_OK
 
 
 @pytest.mark.parametrize("N", [1, 15, 16, 17, 64, 100, 128, 129, 256, 300, 512, 513, 1024])

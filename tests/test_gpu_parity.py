@@ -200,6 +200,32 @@ def test_empty_and_degenerate(ssm):
     assert not np.any(st[1]) and np.array_equal(st[0], case.state[0])
 
 
+def test_check_metadata_device(ssm):
+    """ssm_scan_check_metadata on device arrays: copies on the given stream,
+    waits, and reports the same codes as the host form."""
+    import torch
+    case = ssm_inputs.workload("mixed")
+    dev = "cuda:0"
+    cu = torch.from_numpy(case.cu_seqlens).to(dev)
+    slot = torch.from_numpy(case.slot).to(dev)
+    T, ns = case.n_tokens, case.n_slots
+    s = torch.cuda.Stream()
+    assert ssm.check_metadata(cu, slot, T, ns) == ssm.SSM_OK
+    assert ssm.check_metadata(cu, slot, T, ns, stream=s) == ssm.SSM_OK
+    assert ssm.check_metadata(None, slot, 0, ns) == ssm.SSM_OK
+    bad = slot.clone()
+    bad[3] = bad[5]
+    assert ssm.check_metadata(cu, bad, T, ns) == ssm.SSM_ERR_METADATA          # repeated slot
+    bad[3] = ns
+    assert ssm.check_metadata(None, bad, 0, ns) == ssm.SSM_ERR_METADATA        # out of range
+    assert ssm.check_metadata(cu, slot, T + 1, ns) == ssm.SSM_ERR_METADATA     # total
+    cu_bad = cu.clone()
+    cu_bad[2], cu_bad[3] = cu[3], cu[2]
+    assert ssm.check_metadata(cu_bad, slot, T, ns) == ssm.SSM_ERR_METADATA     # not monotone
+    # the host form on the same values agrees
+    assert ssm.check_metadata(case.cu_seqlens, case.slot, T, ns) == ssm.SSM_OK
+
+
 def test_side_stream(ssm, orc):
     import torch
     case = ssm_inputs.workload("tiny")
@@ -368,6 +394,62 @@ def test_split_prefill_wide_many_segments(ssm, orc, segments):
     y32, st32 = orc.scan_case(case, precision="f32")
     assert_parity(case, y, st, y32, st32)
     assert not np.any(st[5])                 # the fresh empty sequence's slot is zeroed
+
+
+@pytest.mark.parametrize("lengths,fresh", [([1500, 1200], [1, 0]), ([1300, 700, 0], [0, 1, 0]),
+                                           ([3000, 40], [0, 1])])
+def test_split_prefill_multi_window_state_pass(ssm, orc, lengths, fresh):
+    """Two segments per sequence, so a segment runs 650-1504 tokens and the
+    state pass walks it in two or three 512-token windows, carrying the state
+    across them (h <- e^{S_window} h); fresh and resumed segment 0, a short
+    sequence with one segment, an empty resumed one."""
+    n = len(lengths)
+    case = ssm_inputs.make_case(4, 64, 128, 2, lengths, fresh, seed=800 + lengths[0],
+                                slots=list(range(1, n + 1)), n_slots=n + 2, poison_fresh=True,
+                                sentinel_unused=True, name=f"multi_window_{lengths}")
+    plan = ssm.prefill_plan(4, 64, 128, 2, n, max(lengths), 2)
+    say(f"multi-window state pass {lengths}: {plan}")
+    assert plan["segments"] == 2 and plan["segment_tokens"] > 512
+    y, st = run_gpu(case, "prefill_ws", segments=2)
+    y32, st32 = orc.scan_case(case, precision="f32")
+    assert_parity(case, y, st, y32, st32, label=f"{case.name} vs fp32")
+    y64, st64 = orc.scan_case(case, precision="f64")
+    assert_parity(case, y, st, y64, st64, label=f"{case.name} vs fp64")
+
+
+@pytest.mark.parametrize("max_seqlen,segments", [(300, 3), (600, 2), (200, 0)])
+def test_split_prefill_ssd_understated_max_seqlen(ssm, orc, max_seqlen, segments):
+    """Matrix-core split with max_seqlen below the longest sequence (1300):
+    the plan cuts segments for max_seqlen and a longer sequence's last segment
+    runs on to its end (here up to 1076 tokens in one scan-pass segment)."""
+    lengths = [1300, 700, 90, 0]
+    case = ssm_inputs.make_case(4, 64, 128, 2, lengths, [1, 0, 0, 1], seed=850 + max_seqlen,
+                                slots=[4, 0, 2, 1], n_slots=6, poison_fresh=True,
+                                sentinel_unused=True, name=f"ssd_understated_{max_seqlen}")
+    plan = ssm.prefill_plan(4, 64, 128, 2, len(lengths), max_seqlen, segments)
+    say(f"understated max_seqlen={max_seqlen} segments={segments}: {plan}")
+    if segments:
+        assert plan["segments"] == segments and plan["rows_per_block"] == 128
+    y, st = run_gpu(case, "prefill_ws", max_seqlen=max_seqlen, segments=segments)
+    y32, st32 = orc.scan_case(case, precision="f32")
+    assert_parity(case, y, st, y32, st32)
+    assert not np.any(st[1])                  # the fresh empty sequence's slot is zeroed
+
+
+def test_split_prefill_1x16384_auto(ssm, orc):
+    """1 x 16384 at the headline geometry: the automatic plan takes 16
+    segments of 1024 tokens, so every state-pass segment spans two windows."""
+    case = ssm_inputs.make_case(64, 64, 128, 8, [16384], [0], seed=16384,
+                                name="prefill_1x16384")
+    plan = ssm.prefill_plan(64, 64, 128, 8, 1, 16384)
+    say(f"split prefill 1x16384 (resumed): plan {plan}")
+    assert plan["segments"] == 16 and plan["segment_tokens"] == 1024
+    y, st = run_gpu(case, "prefill_ws")
+    y64, st64 = orc.scan_case(case, precision="f64")
+    assert_parity(case, y, st, y64, st64, label="split 1x16384 vs fp64")
+    del y64, st64
+    y32, st32 = orc.scan_case(case, precision="f32")
+    assert_parity(case, y, st, y32, st32, label="split 1x16384 vs fp32")
 
 
 def test_split_prefill_scalar_path(ssm, orc):
