@@ -63,7 +63,8 @@ enum ssm_scan_status {
                                  exceed the launch limits                           */
     SSM_ERR_ALIGN = -4,       /* a float or int array is not 4-byte aligned         */
     SSM_ERR_LAUNCH = -5,      /* the HIP runtime refused the launch                 */
-    SSM_ERR_METADATA = -6     /* ssm_scan_check_metadata found a violation          */
+    SSM_ERR_METADATA = -6,    /* ssm_scan_check_metadata found a violation          */
+    SSM_ERR_SCRATCH = -7      /* the call needs more than the static scratch holds  */
 };
 
 /* H, P, N, G: heads, head-dim rows per head, state size, B/C groups. */
@@ -125,6 +126,35 @@ int ssm_scan_prefill_ws(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tok
                         const float *dt, const float *A, const float *B, const float *C,
                         float *state, int32_t n_slots, float *y, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * ssm_scan_prefill_ws with the library's own scratch in place of the caller's
+ * workspace.  Same arguments, meaning and results (bit for bit the same
+ * kernels and plan), minus workspace and workspace_bytes.
+ *   - The scratch is one static device array of SSM_SCAN_STATIC_SCRATCH_BYTES
+ *     on each GPU the library runs on, held until the process ends.  The
+ *     first call on a GPU looks up its address there (a runtime query, no
+ *     allocation); make that first call outside graph capture.
+ *   - A call whose split needs more than SSM_SCAN_STATIC_SCRATCH_BYTES
+ *     (ssm_scan_prefill_workspace_size tells) returns SSM_ERR_SCRATCH before
+ *     anything is enqueued; ask for fewer segments or use ssm_scan_prefill_ws.
+ *     The 1 x 4096-token prefill at H 64, P 64, N 128 (16 segments) needs 33 MB.
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents (nothing in it needs clearing).  Calls that overlap on
+ *     one GPU (on concurrent streams, or from several host threads) race on it
+ *     and give wrong results: the caller serialises them.
+ * Never calls hipMalloc, hipFree or any allocating library routine.  Errors as
+ * for ssm_scan_prefill_ws, plus SSM_ERR_SCRATCH, and SSM_ERR_LAUNCH if the
+ * scratch's address cannot be found (ssm_scan_last_hip_error tells why).
+ */
+#define SSM_SCAN_STATIC_SCRATCH_BYTES ((size_t)48 << 20)
+int ssm_scan_prefill_static(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens,
+                            int32_t max_seqlen, int32_t n_segments, const int32_t *cu_seqlens,
+                            const int32_t *slot, const uint8_t *fresh, const float *x,
+                            const float *dt, const float *A, const float *B, const float *C,
+                            float *state, int32_t n_slots, float *y, void *stream);
 
 /* Workspace bytes ssm_scan_prefill_ws needs for these sizes (0 if it would not
  * split).  Touches no device.  The same size serves ssm_scan_prefill_opt, which

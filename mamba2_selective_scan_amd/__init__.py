@@ -54,7 +54,9 @@ SSM_ERR_UNSUPPORTED = -3
 SSM_ERR_ALIGN = -4
 SSM_ERR_LAUNCH = -5
 SSM_ERR_METADATA = -6
+SSM_ERR_SCRATCH = -7
 MAX_D_STATE = 1024
+STATIC_SCRATCH_BYTES = 48 << 20     # SSM_SCAN_STATIC_SCRATCH_BYTES
 
 
 class Dims(ctypes.Structure):
@@ -108,6 +110,9 @@ _lib.ssm_scan_prefill_workspace_size.restype = ctypes.c_int
 _lib.ssm_scan_prefill_ws.argtypes = ([ctypes.POINTER(Dims), _i32, _i32, _i32, _i32] + [_vp] * 9
                                      + [_i32, _vp, _vp, ctypes.c_size_t, _vp])
 _lib.ssm_scan_prefill_ws.restype = ctypes.c_int
+_lib.ssm_scan_prefill_static.argtypes = ([ctypes.POINTER(Dims), _i32, _i32, _i32, _i32] + [_vp] * 9
+                                         + [_i32, _vp, _vp])
+_lib.ssm_scan_prefill_static.restype = ctypes.c_int
 _lib.ssm_scan_prefill_opt.argtypes = ([ctypes.POINTER(Dims), ctypes.POINTER(Options), _i32, _i32,
                                        _i32, _i32] + [_vp] * 9
                                       + [_i32, _vp, _vp, ctypes.c_size_t, _vp])
@@ -362,6 +367,40 @@ def prefill_ws(x, dt, A, B, C, state, cu_seqlens, slot, fresh, max_seqlen, segme
     return _prefill_any(x, dt, A, B, C, state, cu_seqlens, slot, fresh, max(int(max_seqlen), 0),
                         segments, workspace, y, stream, dt_bias, dt_softplus, A_per_state,
                         snapshots)
+
+
+def prefill_static(x, dt, A, B, C, state, cu_seqlens, slot, fresh, max_seqlen, segments=0,
+                   y=None, stream=None):
+    """``ssm_scan_prefill_static``: ``prefill_ws`` with the library's own
+    static device scratch (no workspace, nothing allocated in the call; only
+    ``y`` is allocated here when not given).  Raises ``ScanError`` with
+    ``SSM_ERR_SCRATCH`` when the split would need more than the scratch holds."""
+    import torch
+    n_slots, H, P, N = (int(v) for v in state.shape)
+    T = int(x.shape[0])
+    G = int(B.shape[1])
+    n_seqs = int(slot.shape[0])
+    if tuple(x.shape) != (T, H, P) or tuple(dt.shape) != (T, H) or tuple(A.shape) != (H,):
+        raise ValueError("x, dt or A has the wrong shape")
+    if tuple(B.shape) != (T, G, N) or tuple(C.shape) != (T, G, N):
+        raise ValueError("B or C has the wrong shape")
+    if tuple(cu_seqlens.shape) != (n_seqs + 1,) or tuple(fresh.shape) != (n_seqs,):
+        raise ValueError("cu_seqlens or fresh has the wrong shape")
+    dev = state.device
+    if y is None:
+        y = torch.empty((T, H, P), dtype=torch.float32, device=dev)
+    elif tuple(y.shape) != (T, H, P):
+        raise ValueError("y has the wrong shape")
+    f32, i32 = torch.float32, torch.int32
+    rc = _lib.ssm_scan_prefill_static(
+        ctypes.byref(Dims(H, P, N, G)), n_seqs, T, max(int(max_seqlen), 0), int(segments),
+        _dev_ptr(cu_seqlens, i32, "cu_seqlens", dev), _dev_ptr(slot, i32, "slot", dev),
+        _dev_ptr(fresh, torch.uint8, "fresh", dev), _dev_ptr(x, f32, "x", dev),
+        _dev_ptr(dt, f32, "dt", dev), _dev_ptr(A, f32, "A", dev), _dev_ptr(B, f32, "B", dev),
+        _dev_ptr(C, f32, "C", dev), _dev_ptr(state, f32, "state", dev), n_slots,
+        _dev_ptr(y, f32, "y", dev), _stream_handle(stream, dev))
+    _check(rc, "ssm_scan_prefill_static")
+    return y
 
 
 def decode(x, dt, A, B, C, state, slot, fresh, y=None, stream=None, dt_bias=None,

@@ -71,6 +71,36 @@ const ShapeRow *shape_for(int N) {
 
 constexpr int kMaxDevices = 64;
 
+}  // namespace
+
+// Scratch of ssm_scan_prefill_static: one copy on each GPU, for the life of
+// the process.  In host code its name is only a handle; kernels get the
+// device address that static_scratch() looks up.
+static __device__ __align__(256) char scratch[SSM_SCAN_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+std::atomic<char *> g_scratch_addr[kMaxDevices];
+
+// The current GPU's copy of `scratch`, looked up on the first call there.
+int static_scratch(char **out) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return hip_fail(err, SSM_ERR_LAUNCH);
+    if (dev < 0 || dev >= kMaxDevices) return SSM_ERR_UNSUPPORTED;
+    char *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void *addr = nullptr;
+        err = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return hip_fail(err, SSM_ERR_LAUNCH);
+        if (!addr || reinterpret_cast<uintptr_t>(addr) % 256 != 0) return SSM_ERR_LAUNCH;
+        p = static_cast<char *>(addr);
+        g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return SSM_OK;
+}
+
 template <class S, bool VEC, Mode MODE, int OPT = 0>
 int launch(const ScanArgs &a, hipStream_t stream) {
     const void *kern = reinterpret_cast<const void *>(&ssm::scan_kernel<S, VEC, MODE, OPT>);
@@ -530,6 +560,32 @@ int ssm_scan_prefill_ws(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tok
                                 workspace, workspace_bytes, stream);
 }
 
+int ssm_scan_prefill_static(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens,
+                            int32_t max_seqlen, int32_t n_segments, const int32_t *cu_seqlens,
+                            const int32_t *slot, const uint8_t *fresh, const float *x,
+                            const float *dt, const float *A, const float *B, const float *C,
+                            float *state, int32_t n_slots, float *y, void *stream) {
+    const int rc = check_dims(dims);
+    if (rc != SSM_OK) return rc;
+    if (n_seqs < 0 || n_tokens < 0 || n_slots < 0 || max_seqlen < 0 || n_segments < 0)
+        return SSM_ERR_DIMS;
+    if (n_seqs == 0) return SSM_OK;
+    if (n_slots == 0) return SSM_ERR_DIMS;
+    if (!cu_seqlens || !slot || !fresh || !A || !state) return SSM_ERR_NULL;
+    if (n_tokens > 0 && (!x || !dt || !B || !C || !y)) return SSM_ERR_NULL;
+    const ShapeRow *row = shape_for(dims->d_state);
+    const SegPlan plan = plan_segments(dims, *row, n_seqs, max_seqlen, n_segments);
+    char *ws = nullptr;
+    if (plan.n_segs > 1) {
+        if (ws_layout(dims, n_seqs, n_tokens, plan.n_segs).total > SSM_SCAN_STATIC_SCRATCH_BYTES)
+            return SSM_ERR_SCRATCH;
+        const int src = static_scratch(&ws);
+        if (src != SSM_OK) return src;
+    }
+    return scan_common(dims, nullptr, n_seqs, n_tokens, cu_seqlens, slot, fresh, x, dt, A, B, C,
+                       state, y, /*decode=*/false, plan, ws, stream);
+}
+
 int ssm_scan_decode_opt(const ssm_scan_dims *dims, const ssm_scan_options *opts, int32_t n_seqs,
                         const int32_t *slot, const uint8_t *fresh, const float *x,
                         const float *dt, const float *A, const float *B, const float *C,
@@ -561,6 +617,7 @@ const char *ssm_scan_strerror(int code) {
     case SSM_ERR_ALIGN: return "an array is not 4-byte aligned";
     case SSM_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
     case SSM_ERR_METADATA: return "invalid metadata (cu_seqlens not monotone from 0 to n_tokens, or a slot out of range or repeated)";
+    case SSM_ERR_SCRATCH: return "the split needs more scratch than the library's static buffer (SSM_SCAN_STATIC_SCRATCH_BYTES) holds";
     default: return "unknown status code";
     }
 }

@@ -22,7 +22,7 @@ def test_exports_every_declared_symbol():
                           "ssm_scan_query_geometry", "ssm_scan_last_hip_error",
                           "ssm_scan_last_hip_error_string", "ssm_scan_prefill_ws",
                           "ssm_scan_prefill_workspace_size", "ssm_scan_query_prefill_plan",
-                          "ssm_scan_prefill_opt", "ssm_scan_decode_opt",
+                          "ssm_scan_prefill_opt", "ssm_scan_decode_opt", "ssm_scan_prefill_static",
                           "ssm_conv1d_silu_prefill", "ssm_conv1d_silu_decode",
                           "ssm_gated_rmsnorm", "ssm_gdn_prefill", "ssm_gdn_decode",
                           "ssm_gdn_prefill_ws", "ssm_gdn_prefill_workspace_size"}
@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     assert m.version() == 2
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert m.strerror(code) and "unknown" not in m.strerror(code)
     assert "unknown" in m.strerror(-99)
     assert m.lib().ssm_scan_last_hip_error() == 0
