@@ -4,16 +4,27 @@
 Headline: decode, 16 sequences x 1 token at H=64, P=64, N=128, G=8, fp32,
 resuming state.  A step is one ssm_scan_decode call.  Consecutive steps use
 16 disjoint slot sets of a 256-slot state (537 MB), so each step's 33.5 MB of
-state comes from HBM, not from the 256 MB Infinity Cache.  The 16 steps of one
-rotation are captured once in a HIP graph and replayed, so host launch
-overhead does not pad the step time.  Also measured and reported beside it:
-the 1 x 4096-token prefill at the same geometry (fresh state, eager launches,
-the automatic time split on the matrix cores), the secondary scan workloads,
-the ops beside the scan (conv1d + SiLU, gated RMSNorm) and the gated delta rule.
+state comes from HBM, not from the 256 MB Infinity Cache.  After --warmup
+untimed steps, exactly --steps launches are timed between HIP events; a spin
+kernel enqueued ahead of the start event keeps the GPU busy while the host
+enqueues them, so they run back to back and the timed region holds the
+steps' kernels and the gaps between them only.  The same is done for a
+hand-written read-modify-write stream over the same slot sets (the
+achievable ceiling for a kernel that reads and writes each state value once).
+
+Also measured and reported beside it: the 1 x 4096-token prefill at the same
+geometry, both on the matrix cores (the automatic time split) and on the
+VALU (the one-pass register kernel), the secondary scan workloads, the ops
+beside the scan (conv1d + SiLU, gated RMSNorm), the gated delta rule, and the
+fp32 CPU oracle on all five workloads at one thread and at every thread the
+process may use.
 
 Prints one JSON line.  Times come from HIP events on the stream the kernels run
 on; the roofline objects use algorithmic bytes (decode, HBM-bound) and
-algorithmic flops (prefill, bound by the FP32 matrix cores).
+algorithmic flops (prefill).  Figures from counter and kernel-trace runs
+(HBM traffic, VALU and matrix-core busy, LDS bank conflicts, kernel-trace
+medians) are read from committed summaries under profiles/ and only when they
+were taken on the current kernel sources (a hash of them); else null.
 """
 from __future__ import annotations
 
@@ -65,6 +76,8 @@ def kernel_source_hash():
     for rel in ("mamba2_selective_scan_amd/csrc/scan_kernel.hpp",
                 "mamba2_selective_scan_amd/csrc/correct_mfma.hpp",
                 "mamba2_selective_scan_amd/csrc/ssd_kernel.hpp",
+                "mamba2_selective_scan_amd/csrc/decode_kernel.hpp",
+                "mamba2_selective_scan_amd/csrc/buffer_io.hpp",
                 "mamba2_selective_scan_amd/csrc/status.hpp",
                 "mamba2_selective_scan_amd/csrc/ssm_scan.hip", "include/ssm_scan.h"):
         with open(os.path.join(ROOT, rel)) as f:
@@ -78,18 +91,23 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(name):
-    """Measured HBM bytes per launch from a committed counter run, if it was
-    taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+def load_profile(name):
+    """A committed summary under profiles/ (``<name>.json``) if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{name}.json")
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_hash") != kernel_source_hash():
-        return None
-    return t.get("bytes_per_launch")
+    return t if t.get("kernel_hash") == kernel_source_hash() else None
+
+
+def load_traffic(name):
+    """Measured HBM bytes per launch from a committed counter run, if it was
+    taken on the current kernel source; else None."""
+    t = load_profile(f"{name}_traffic")
+    return None if t is None else t.get("bytes_per_launch")
 
 
 def host_cpu_model():
@@ -110,29 +128,55 @@ def host_cores():
         return os.cpu_count() or 1
 
 
-def cpu_baseline_decode(case, seconds):
-    """The fp32 oracle on the same decode step, repeated for ~``seconds`` on
-    all host threads (up to 16) and for ~seconds/3 on one thread."""
-    import oracle
-    threads = min(16, host_cores())
-    orc = oracle.default()
+CPU_CONFIGS = (("decode16", "decode 16 x 1, resuming, H64 P64 N128 G8"),
+               ("tiny", "tiny scan T64 H4 P16 N16 G1"),
+               ("mixed", "mixed edge batch, 8 seqs / 523 tokens, H16 P96 N100 G4"),
+               ("decode256", "decode 256 x 1, resuming, H64 P64 N128 G8"),
+               ("prefill4096", "prefill 1 x 4096, fresh, H64 P64 N128 G8"))
 
-    def rate(th, budget):
-        orc.scan_case(case, threads=th)                # page in
-        n, t0 = 0, time.perf_counter()
+
+def cpu_baseline(seconds):
+    """The fp32 oracle (plain sequential C, OpenMP over (sequence, head)) on
+    each of the five workloads, at one thread and at every thread the process
+    may use; each timing repeats the whole workload until ``seconds`` have
+    passed (at least once) and keeps the fastest run.  The fp64 oracle on all
+    threads is informational.  Rank 0, one GPU only."""
+    import oracle
+    import ssm_inputs
+    orc = oracle.default()
+    threads = oracle.default_threads()
+
+    def best(case, th, precision="f32"):
+        runs, t_all = [], time.perf_counter()
         while True:
-            orc.scan_case(case, threads=th)
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= budget:
-                return n, el
-    n, el = rate(threads, seconds)
-    n1, el1 = rate(1, max(1.0, seconds / 3))
-    return {"value": round(el / n * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle",
-            "value_1_thread": round(el1 / n1 * 1e6, 1), "cpu_model": host_cpu_model(),
-            "sample": f"{n} repetitions of the full decode 16x1 step (16 seqs x 64 heads x 64 "
-                      f"rows x 128 state, fp32, resuming) on {threads} threads, {el:.1f} s; "
-                      f"{n1} on 1 thread, {el1:.1f} s"}
+            t0 = time.perf_counter()
+            orc.scan_case(case, precision=precision, threads=th)
+            runs.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_all >= seconds:
+                return min(runs), len(runs)
+    per, total_s = {}, time.perf_counter()
+    for name, desc in CPU_CONFIGS:
+        case = ssm_inputs.workload(name)
+        orc.scan_case(case, threads=threads)             # page in
+        t1, n1 = best(case, 1)
+        tn, nn = best(case, threads)
+        t64, n64 = best(case, threads, "f64")
+        per[name] = {"workload": desc, "ms_1_thread": round(t1 * 1e3, 3),
+                     f"ms_{threads}_threads": round(tn * 1e3, 3),
+                     f"ms_f64_{threads}_threads": round(t64 * 1e3, 3),
+                     "runs": [n1, nn, n64]}
+    head = per["decode16"]
+    return {"value": round(head[f"ms_{threads}_threads"] * 1e3, 1), "unit": "us",
+            "cores": threads, "kind": "oracle",
+            "value_1_thread": round(head["ms_1_thread"] * 1e3, 1),
+            "cores_available": {"affinity": host_cores(), "os_cpu_count": os.cpu_count(),
+                                "omp_num_threads": os.environ.get("OMP_NUM_THREADS")},
+            "cpu_model": host_cpu_model(),
+            "sample": f"each of the five workloads run whole, repeated for {seconds:g} s per "
+                      f"setting (fastest run kept): fp32 on 1 and on {threads} threads, fp64 on "
+                      f"{threads}; value = the decode 16x1 step on {threads} threads; "
+                      f"{time.perf_counter() - total_s:.1f} s in all",
+            "per_config": per}
 
 
 def _timed(fn, n, stream):
@@ -146,9 +190,84 @@ def _timed(fn, n, stream):
     return a.elapsed_time(b) / n
 
 
+def sleep_cycles_per_ms(stream):
+    """Clock rate of torch's spin kernel (cycles per ms), measured once."""
+    import torch
+    torch.cuda._sleep(1000)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    torch.cuda._sleep(2_000_000)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return 2_000_000 / max(a.elapsed_time(b), 1e-3)
+
+
+def queued_steps_ms(calls, warmup, stream, cycles_per_ms):
+    """``warmup`` untimed calls (calls[i % len]), then exactly len(calls)
+    calls timed between two HIP events.  A spin kernel enqueued ahead of the
+    start event keeps the GPU busy while the host enqueues the timed calls, so
+    they run back to back from the queue: the timed region holds their
+    kernels and the gaps between them, not the host's launch cost.  Returns
+    (total milliseconds, host enqueue milliseconds, spin milliseconds); the
+    host time below the spin time shows that the queue never ran dry."""
+    import torch
+    if warmup:
+        calls[0]()                                   # first launch: loading, set-up
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(1, warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    per_call = (time.perf_counter() - t0) / (warmup - 1) if warmup > 1 else 50e-6
+    spin_ms = min(200.0, max(2.0, 3e3 * per_call * len(calls)))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(cycles_per_ms * spin_ms))
+    a.record(stream)
+    t1 = time.perf_counter()
+    for f in calls:
+        f()
+    host_ms = (time.perf_counter() - t1) * 1e3
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b), host_ms, spin_ms
+
+
+def calib_lib():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "mamba2_selective_scan_amd", "libssmcalib.so"))
+    lib.ssm_calib_stream_rw.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                        ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+    lib.ssm_calib_stream_rw.restype = ctypes.c_int
+    return lib
+
+
+def stream_ceiling(state, n_sets, steps, warmup, stream, cycles_per_ms):
+    """The hand-written read-modify-write stream over the same rotated slot
+    sets as the decode step (each set: DECODE_SEQS slots, 33.5 MB read and
+    written), for 1, 2, 4 and 8 float4 per lane, timed like the decode steps;
+    returns the best lane count and the microseconds per launch of each."""
+    import ctypes
+    lib = calib_lib()
+    per_set = DECODE_SEQS * H * P * N            # floats per slot set
+    h = ctypes.c_void_p(stream.cuda_stream)
+    out = {}
+    for pl in (1, 2, 4, 8):
+        def call(k, pl=pl):
+            rc = lib.ssm_calib_stream_rw(ctypes.c_void_p(state.data_ptr() + 4 * k * per_set),
+                                         per_set // 4, pl, 1.0, 0.0, h)
+            if rc != 0:
+                raise RuntimeError(f"ssm_calib_stream_rw: {rc}")
+        calls = [(lambda i=i: call(i % n_sets)) for i in range(steps)]
+        out[pl] = 1e3 * queued_steps_ms(calls, warmup, stream, cycles_per_ms)[0] / steps
+    pl_best = min(out, key=out.get)
+    return pl_best, out
+
+
 def profile_mode(args, dev, stream):
-    """One kernel kind, eager launches, for counter runs: every dispatch of the
-    named kernel is the workload of the headline (decode) or of the prefill."""
+    """One kernel kind, eager launches, for counter and trace runs: every
+    dispatch of the named kernel is the workload of the headline (decode), of
+    the prefill (split on the matrix cores, or one pass on the VALU), or a
+    plain copy / stream for calibrating counters."""
     import torch
 
     import mamba2_selective_scan_amd as ssm
@@ -163,24 +282,13 @@ def profile_mode(args, dev, stream):
         ms = _timed(lambda i: dst.copy_(src), args.steps, stream)
         out.update(bytes_read=4 * n, bytes_written=4 * n, ms=ms,
                    GBs=2 * 4 * n / (ms * 1e-3) / 1e9)
-    elif args.mode == "copy16":
-        n = DECODE_SEQS * H * P * N
-        src = [torch.randn(n, device=dev) for _ in range(SLOT_SETS)]
-        dst = [torch.empty_like(src[0]) for _ in range(SLOT_SETS)]
-
-        def rot():
-            for k in range(SLOT_SETS):
-                dst[k].copy_(src[k])
-        rot()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            rot()
-        for _ in range(2):
-            graph.replay()
-        ms = _timed(lambda i: graph.replay(), max(1, args.steps // SLOT_SETS), stream) / SLOT_SETS
-        out.update(bytes_per_copy=2 * 4 * n, us_per_copy=ms * 1e3,
-                   GBs=2 * 4 * n / (ms * 1e-3) / 1e9)
+    elif args.mode == "stream16":
+        state = torch.zeros((DECODE_SEQS * SLOT_SETS, H, P, N), dtype=torch.float32, device=dev)
+        cpm = sleep_cycles_per_ms(stream)
+        pl, us = stream_ceiling(state, SLOT_SETS, args.steps, args.warmup, stream, cpm)
+        nbytes = 2 * 4 * DECODE_SEQS * H * P * N
+        out.update(bytes_per_launch=nbytes, us_per_launch=us, best_per_lane=pl,
+                   GBs=nbytes / (us[pl] * 1e-6) / 1e9)
     elif args.mode == "decode":
         case = ssm_inputs.workload("decode16", sets=SLOT_SETS)
         d = ssm.to_device(case, dev)
@@ -217,6 +325,30 @@ def profile_mode(args, dev, stream):
                    ms_per_launch=ms)
     out["kernel_hash"] = kernel_source_hash()
     print(json.dumps(out), flush=True)
+
+
+def summarize_trace(path):
+    """Per (kernel, grid size) dispatch statistics from a rocprofv3 kernel
+    trace (``*_kernel_trace.csv``): count, median, mean, min and max duration
+    in microseconds.  Prints one JSON object (the input of the committed
+    kernel-trace summaries under profiles/)."""
+    import csv
+    import statistics
+    rows = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name") or r.get("KernelName") or "?"
+            grid = r.get("Grid_Size") or r.get("Grid_Size_X") or r.get("Grid_Sizes") or "?"
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            rows.setdefault((name, grid), []).append(dur)
+    out = []
+    for (name, grid), d in sorted(rows.items(), key=lambda kv: -sum(kv[1])):
+        out.append({"kernel": name, "grid": grid, "count": len(d),
+                    "median_us": round(statistics.median(d), 3),
+                    "mean_us": round(statistics.fmean(d), 3), "min_us": round(min(d), 3),
+                    "max_us": round(max(d), 3)})
+    print(json.dumps({"kernel_hash": kernel_source_hash(), "trace": os.path.basename(path),
+                      "kernels": out}, indent=1))
 
 
 def _event_ms(fn, n, warm, stream):
@@ -446,32 +578,39 @@ def gated_delta(args, dev, stream):
 
 
 def main():
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=320, help="timed decode steps")
     ap.add_argument("--warmup", type=int, default=32, help="untimed decode steps")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-warmup", type=int, default=3)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=1.0,
+                    help="oracle timing budget per workload and setting")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the secondary workloads (decode 256x1, mixed batch, options)")
-    ap.add_argument("--mode", choices=("all", "decode", "prefill", "prefill1", "copy", "copy16"),
+    ap.add_argument("--mode", choices=("all", "decode", "prefill", "prefill1", "copy", "stream16"),
                     default="all",
                     help="decode/prefill: launch only that path (prefill: the time-split path; "
                          "prefill1: the unsplit single kernel), eagerly, and print its "
                          "timing (for counter runs); copy: a plain 256 MiB device copy, the "
-                         "reference for scaling HBM byte counters; copy16: device copies of "
-                         "one decode step's state size over 16 rotating buffers, replayed "
-                         "from a HIP graph like the decode bench (achievable-bandwidth "
-                         "reference)")
+                         "reference for scaling HBM byte counters; stream16: the read-modify-"
+                         "write stream over the decode step's 16 rotating slot sets")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="print per-kernel statistics of a rocprofv3 kernel trace and exit")
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the scan needs no collective and this build runs "
               "on a single MI355X (see the sharding notes); run it with --gpus 1.",
               file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -487,6 +626,7 @@ def main():
     if args.mode != "all":
         profile_mode(args, dev, stream)
         return
+    cpm = sleep_cycles_per_ms(stream)
 
     # ---------------- decode 16x1, 16 rotating slot sets
     case = ssm_inputs.workload("decode16", sets=SLOT_SETS)
@@ -499,39 +639,24 @@ def main():
         ssm.decode(d["x"], d["dt"], d["A"], d["B"], d["C"], d["state"], slot_sets[k],
                    d["fresh"], y=y)
 
-    for k in range(SLOT_SETS):                          # eager warm-up, sets the kernels up
-        decode_step(k)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for k in range(SLOT_SETS):
-            decode_step(k)
-    torch.cuda.synchronize()
-    replays_w = max(1, -(-args.warmup // SLOT_SETS))
-    replays = max(1, -(-args.steps // SLOT_SETS))
-    steps = replays * SLOT_SETS
-    for _ in range(replays_w):
-        graph.replay()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    calls = [(lambda i=i: decode_step(i % SLOT_SETS)) for i in range(args.steps)]
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(replays):
-        graph.replay()
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    dec_ms, host_ms, spin_ms = queued_steps_ms(calls, args.warmup, stream, cpm)
     wall = time.perf_counter() - t0
-    dec_us = ev0.elapsed_time(ev1) * 1e3 / steps        # average step (= launch) duration
+    dec_us = dec_ms * 1e3 / args.steps                   # average step (= launch) duration
     dec_gbs = decode_bytes() / (dec_us * 1e-6) / 1e9
-    traffic = load_traffic("decode16")
+    # the ceiling: a plain read-modify-write stream over the same slot sets
+    pl, st_us = stream_ceiling(d["state"], SLOT_SETS, args.steps, args.warmup, stream, cpm)
+    st_gbs = 2 * 4 * DECODE_SEQS * H * P * N / (st_us[pl] * 1e-6) / 1e9
+    trace = load_profile("decode16_kernel_trace")
 
     result = {
         "metric": "scan time per layer (ms prefill 1x4096, us decode 16x1); % HBM/VALU roofline",
         "value": round(dec_us, 3),
         "unit": "us",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": replays_w * SLOT_SETS,
+        "steps": args.steps,
+        "warmup": args.warmup,
         "ms_per_step": round(dec_us / 1e3, 6),
         "higher_is_better": False,
         "scaling": "weak",
@@ -542,18 +667,30 @@ def main():
         "config": {"workload": "decode 16 seqs x 1 token, resuming", "H": H, "P": P, "N": N,
                    "G": G, "slot_sets_rotated": SLOT_SETS,
                    "state_bytes_rotated": int(case.state.nbytes),
-                   "launch": "HIP graph of 16 steps, replayed",
+                   "launch": f"{args.warmup} untimed steps, then {args.steps} steps queued "
+                             "behind a spin kernel and timed between HIP events",
+                   "host_enqueue_ms": round(host_ms, 3), "spin_ms": round(spin_ms, 3),
                    "geometry": ssm.geometry(H, P, N, G, DECODE_SEQS, decode=True)},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "algorithmic_bytes_per_launch": decode_bytes()},
+                     "traffic": load_traffic("decode16"),
+                     "algorithmic_bytes_per_launch": decode_bytes(),
+                     "achievable": {"kernel": "read-modify-write stream over the same slot "
+                                              f"sets ({pl} float4 per lane, best of 1/2/4/8)",
+                                    "us": round(st_us[pl], 3), "GBs": round(st_gbs, 1),
+                                    "us_per_lane_count": {str(k): round(v, 3)
+                                                          for k, v in st_us.items()},
+                                    "frac_of_achievable": round(st_us[pl] / dec_us, 4)},
+                     "kernel_trace": None if trace is None else {
+                         "median_us": trace.get("median_us"), "mean_us": trace.get("mean_us"),
+                         "source": trace.get("source")}},
         "wall_s_timed": round(wall, 4),
+        "timed_steps_ms": round(dec_ms, 4),
     }
 
-    # ---------------- prefill 1x4096, fresh.  One sequence fills only a quarter
-    # of the SIMDs, so the library splits it over time (ssm_scan_prefill_ws,
-    # automatic plan); the unsplit single-pass time is reported beside it.
+    # ---------------- prefill 1x4096, fresh.  On the matrix cores: the library
+    # splits the one sequence over time (ssm_scan_prefill_ws, automatic plan).
+    # On the VALU: the one-pass register kernel (ssm_scan_prefill).
     if not args.no_prefill:
         pc = ssm_inputs.workload("prefill4096")
         pd = ssm.to_device(pc, dev)
@@ -584,33 +721,49 @@ def main():
             torch.cuda.synchronize()
             return [a.elapsed_time(b) for a, b in pairs]
 
+        def stats(ms):
+            return {"ms": round(float(np.mean(ms)), 4), "ms_median": round(float(np.median(ms)), 4),
+                    "ms_min": round(min(ms), 4), "ms_max": round(max(ms), 4),
+                    "iterations": args.prefill_steps, "warmup": args.prefill_warmup}
+
         ms = event_times(prefill_split)
-        ms_unsplit = event_times(prefill_unsplit)
-        pf_ms = float(np.mean(ms))
+        ms1 = event_times(prefill_unsplit)
+        pf_ms, pf1_ms = float(np.mean(ms)), float(np.mean(ms1))
         tflops = prefill_flops() / (pf_ms * 1e-3) / 1e12
-        result["prefill"] = {
-            "workload": "prefill 1 seq x 4096 tokens, fresh", "ms": round(pf_ms, 4),
-            "ms_min": round(min(ms), 4), "ms_max": round(max(ms), 4),
-            "iterations": args.prefill_steps,
+        tflops1 = prefill_flops() / (pf1_ms * 1e-3) / 1e12
+        counters = load_profile("prefill4096_counters") or {}
+        result["prefill"] = dict(stats(ms), **{
+            "workload": "prefill 1 seq x 4096 tokens, fresh",
             "path": "ssm_scan_prefill_ws, automatic time split: matrix-core state pass (end "
                     "states of segments 0..n-2), carry combine, matrix-core chunked scans of every "
-                    "segment from its carried-in state, two 16-row tiles per wave (3 kernels)",
+                    "segment from its carried-in state (3 kernels)",
             "plan": ssm.prefill_plan(H, P, N, G, 1, PREFILL_T),
-            "ms_unsplit": round(float(np.mean(ms_unsplit)), 4),
-            "geometry_unsplit": ssm.geometry(H, P, N, G, 1),
-            # both dominant kernels are fp32 matrix-core contractions now; MI355X's
+            # the dominant kernels are fp32 matrix-core contractions; MI355X's
             # dense fp32 MFMA peak is the same 157.3 TFLOP/s as its packed vector
             # peak.  `achieved` counts the recurrence's own 5 flop per state
             # element per token (the chunked form does more arithmetic).
             "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
                          "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4),
-                         "frac_of_unpacked_fp32": round(tflops / FP32_VALU_UNPACKED_TFLOPS, 4),
                          "traffic": load_traffic("prefill4096"),
                          "algorithmic_flops_per_launch": prefill_flops(),
                          "algorithmic_bytes_per_launch": prefill_bytes(),
                          "achieved_GBs": round(prefill_bytes() / (pf_ms * 1e-3) / 1e9, 1)},
-        }
+            "counters": counters.get("split"),
+        })
+        result["prefill_valu"] = dict(stats(ms1), **{
+            "workload": "prefill 1 seq x 4096 tokens, fresh",
+            "path": "ssm_scan_prefill: one pass per (head, 16-row block), state in registers, "
+                    "y by DPP reduce-scatter, chunks of 32 tokens staged in LDS (the VALU path)",
+            "geometry": ssm.geometry(H, P, N, G, 1),
+            "roofline": {"bound": "alu", "achieved": round(tflops1, 3),
+                         "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops1 / FP32_VALU_PEAK_TFLOPS, 4),
+                         "frac_of_unpacked_fp32": round(tflops1 / FP32_VALU_UNPACKED_TFLOPS, 4),
+                         "traffic": None,
+                         "algorithmic_flops_per_launch": prefill_flops()},
+            "counters": counters.get("valu"),
+        })
 
     if not args.no_secondary:
         result["secondary"] = secondary(args, dev, stream)
@@ -618,8 +771,7 @@ def main():
         result["gated_delta_rule"] = gated_delta(args, dev, stream)
 
     if not args.no_cpu_baseline:
-        one_set = ssm_inputs.workload("decode16")
-        result["cpu_baseline"] = cpu_baseline_decode(one_set, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     result["device"] = torch.cuda.get_device_name(dev)
     print(json.dumps(result), flush=True)
 

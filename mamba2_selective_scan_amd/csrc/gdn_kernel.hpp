@@ -57,13 +57,16 @@ struct GdnShape {
     static constexpr int NP = 4 * R * J;            // staged (zero-padded) key width
     static constexpr int ROWS_PER_WAVE = 64 / R;
     static constexpr int RB = kWaves * ROWS_PER_WAVE;   // rows per workgroup
-    // One staging buffer, in floats: k[CT][NP] q[CT][NP] v[CT][RB] y[CT][RB]
+    // One staging buffer, in floats: k[CT][NP] q[CT][NP] v[CT][RB] y[CT][YR]
     // decay[CT] beta[CT] qk[CT]
     static constexpr int OFF_K = 0;
     static constexpr int OFF_Q = OFF_K + CT * NP;
     static constexpr int OFF_V = OFF_Q + CT * NP;
+    // y tile rows padded as in the scan's Shape: lane r of a row stores token
+    // r's y, so a row stride of RB would put lanes r and r + 64/RB in one bank
+    static constexpr int YR = R == 4 ? 80 : R == 8 ? 40 : R == 16 ? 20 : 12;
     static constexpr int OFF_Y = OFF_V + CT * RB;
-    static constexpr int OFF_DECAY = OFF_Y + CT * RB;
+    static constexpr int OFF_DECAY = OFF_Y + CT * YR;
     static constexpr int OFF_BETA = OFF_DECAY + CT;
     static constexpr int OFF_QK = OFF_BETA + CT;
     static constexpr int BUF = ((OFF_QK + CT) + 3) / 4 * 4;
@@ -317,14 +320,14 @@ __global__ void __launch_bounds__(kThreads) gdn_kernel(GdnArgs a) {
                     const float yv = token_y(base, t0 + kk);
                     y_keep = (rk == kk) ? yv : y_keep;
                 }
-                Ys[(t0 + rk) * RB] = y_keep;
+                Ys[(t0 + rk) * S::YR] = y_keep;
             }
             if (t0 < nt) {
                 for (int tt = t0; tt < nt; ++tt) {
                     const float yv = token_y(base, tt);
                     y_keep = (rk == tt - t0) ? yv : y_keep;
                 }
-                if (rk < nt - t0) Ys[(t0 + rk) * RB] = y_keep;
+                if (rk < nt - t0) Ys[(t0 + rk) * S::YR] = y_keep;
             }
         };
         auto flush_y = [&](int buf, int t0, int nt) {
@@ -335,13 +338,13 @@ __global__ void __launch_bounds__(kThreads) gdn_kernel(GdnArgs a) {
                     const int pi = 4 * (q - tt * (RB / 4));
                     if (pi < rows_valid)
                         *reinterpret_cast<f4 *>(a.y + (int64_t(t0 + tt) * Hv + vh) * Dv + p0 + pi) =
-                            *reinterpret_cast<const f4 *>(Ys + tt * RB + pi);
+                            *reinterpret_cast<const f4 *>(Ys + tt * S::YR + pi);
                 }
             } else {
                 for (int q = tid; q < nt * RB; q += kThreads) {
                     const int tt = q / RB;
                     const int pi = q - tt * RB;
-                    if (pi < rows_valid) a.y[(int64_t(t0 + tt) * Hv + vh) * Dv + p0 + pi] = Ys[tt * RB + pi];
+                    if (pi < rows_valid) a.y[(int64_t(t0 + tt) * Hv + vh) * Dv + p0 + pi] = Ys[tt * S::YR + pi];
                 }
             }
         };

@@ -107,12 +107,17 @@ struct Shape {
     static constexpr int ROWS_PER_WAVE = 64 / R;
     static constexpr int RB = kWaves * ROWS_PER_WAVE;   // rows per workgroup
     static constexpr int NPT = NP + 4;              // LDS state-tile row stride
-    // One staging buffer, in floats: B[CT][NP] C[CT][NP] x[CT][RB] y[CT][RB] dt[CT] dA[CT]
+    // One staging buffer, in floats: B[CT][NP] C[CT][NP] x[CT][RB] y[CT][YR] dt[CT] dA[CT]
     static constexpr int OFF_B = 0;
     static constexpr int OFF_C = OFF_B + CT * NP;
     static constexpr int OFF_X = OFF_C + CT * NP;
+    // y tile rows padded: lane r of a row stores token r's y at row r, so with
+    // a row stride of RB lanes r and r + 64/RB hit one bank; YR spreads the
+    // 64 lanes of a store over distinct banks (64 banks; at most 2-way at 32)
+    // and keeps rows 16-byte aligned for the float4 flush
+    static constexpr int YR = R == 4 ? 80 : R == 8 ? 40 : R == 16 ? 20 : 12;
     static constexpr int OFF_Y = OFF_X + CT * RB;
-    static constexpr int OFF_DT = OFF_Y + CT * RB;
+    static constexpr int OFF_DT = OFF_Y + CT * YR;
     static constexpr int OFF_DA = OFF_DT + CT;
     static constexpr int OFF_LAZY = OFF_DA + CT;    // 1: the chunk runs with the decay deferred
     static constexpr int BUF = ((OFF_LAZY + 1) + 3) / 4 * 4;
@@ -690,7 +695,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                     float yv = row_reduce_scatter<KY>(part);
                     if constexpr (R >= 32) yv += __shfl_xor(yv, 16, 64);
                     if constexpr (R >= 64) yv += __shfl_xor(yv, 32, 64);
-                    Ys[(t0 + rk) * RB] = y_scale(base, t0 + rk, lazy_tag) * yv;
+                    Ys[(t0 + rk) * S::YR] = y_scale(base, t0 + rk, lazy_tag) * yv;
                 }
             } else {
                 for (; t0 + KY <= nt; t0 += KY) {
@@ -699,7 +704,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                         const float yv = token_y(base, t0 + kk, lazy_tag);
                         y_keep = (rk == kk) ? yv : y_keep;
                     }
-                    Ys[(t0 + rk) * RB] = y_keep;
+                    Ys[(t0 + rk) * S::YR] = y_keep;
                 }
             }
             if (t0 < nt) {
@@ -707,7 +712,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                     const float yv = token_y(base, tt, lazy_tag);
                     y_keep = (rk == tt - t0) ? yv : y_keep;
                 }
-                if (rk < nt - t0) Ys[(t0 + rk) * RB] = y_keep;
+                if (rk < nt - t0) Ys[(t0 + rk) * S::YR] = y_keep;
             }
         };
         auto compute = [&](int buf, int nt) {
@@ -736,13 +741,13 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                     const int pi = 4 * (q - tt * (RB / 4));
                     if (pi < rows_valid)
                         *reinterpret_cast<f4 *>(a.y + (int64_t(t0 + tt) * H + hd) * P + p0 + pi) =
-                            *reinterpret_cast<const f4 *>(Ys + tt * RB + pi);
+                            *reinterpret_cast<const f4 *>(Ys + tt * S::YR + pi);
                 }
             } else {
                 for (int q = tid; q < nt * RB; q += kThreads) {
                     const int tt = q / RB;
                     const int pi = q - tt * RB;
-                    if (pi < rows_valid) a.y[(int64_t(t0 + tt) * H + hd) * P + p0 + pi] = Ys[tt * RB + pi];
+                    if (pi < rows_valid) a.y[(int64_t(t0 + tt) * H + hd) * P + p0 + pi] = Ys[tt * S::YR + pi];
                 }
             }
         };

@@ -34,7 +34,7 @@
 // read back.  The scan pass runs one workgroup per (sequence, time segment,
 // window of 64 TW rows of a B/C group): its four wavefronts own TW 16-row
 // tiles each.  B, C and x of a chunk are staged in LDS, double-buffered (rows
-// padded so the strided state-update reads are conflict-free), the per-token
+// of B, C and x padded so the strided reads are conflict-free), the per-token
 // scalars of each head are formed once in wave 0, and G^T, the same for the
 // four wavefronts, is formed a quarter by each and summed through LDS.  G^T
 // only feeds the chunk's own y (never the state), so a chunk's y is finished
@@ -42,6 +42,7 @@
 // needs anyway.
 #pragma once
 
+#include "buffer_io.hpp"
 #include "scan_kernel.hpp"
 
 namespace ssm {
@@ -57,10 +58,15 @@ struct SsdScanShape {
     static constexpr int RBW = 64 * TW;             // rows per workgroup (4 waves x 16 TW)
     static constexpr int MH = 4;                    // heads per workgroup at most (16 TW | P)
     static constexpr int LDN = N + 4;               // padded LDS row of B / C
+    // x rows padded by 4 floats: a lane reads row 4 (l/16) + v, column l % 16
+    // (+ a wave offset), so with RBW a multiple of the bank count the four
+    // l/16 groups would share banks; 4 more floats per row put them 16 banks
+    // apart (conflict-free for 32 and for 64 banks)
+    static constexpr int XR = RBW + 4;
     static constexpr int OFF_C = 0;
     static constexpr int OFF_B = OFF_C + CT * LDN;
-    static constexpr int OFF_X = OFF_B + CT * LDN;  // x[CT][RBW]
-    static constexpr int OFF_S = OFF_X + CT * RBW;  // [MH][CT] S_t
+    static constexpr int OFF_X = OFF_B + CT * LDN;  // x[CT][XR]
+    static constexpr int OFF_S = OFF_X + CT * XR;   // [MH][CT] S_t
     static constexpr int OFF_DT = OFF_S + MH * CT;  // [MH][CT] dt_t (0 past the segment)
     static constexpr int OFF_ES = OFF_DT + MH * CT; // [MH][CT] e^{S_t} (times sigma when deferred)
     static constexpr int OFF_W = OFF_ES + MH * CT;  // [MH][CT] the update's weights
@@ -103,41 +109,6 @@ __device__ __forceinline__ float wave_prefix_sum(float v, int lane) {
         if ((lane >> 4) == r) v += before;
     }
     return v;
-}
-
-// E consecutive floats as one load: a vector for E > 1, a float for E = 1.
-template <int E> struct VecT { using type = float __attribute__((ext_vector_type(E))); };
-template <> struct VecT<1> { using type = float; };
-template <int E> __device__ __forceinline__ float vget(const typename VecT<E>::type &v, int e) {
-    if constexpr (E == 1) return v; else return v[e];
-}
-
-// Raw buffer loads.  A descriptor covers [base, base + bytes); a load at byte
-// offset voffset + soffset past that range returns zeros without touching
-// memory, so a window's operands need no clamping, and the per-step advance
-// goes in the scalar offset: no vector address arithmetic per load.
-constexpr int kBufferFlags = 0x00020000;   // raw (stride 0) 32-bit elements, gfx9 descriptor word 3
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const float *base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, bytes, kBufferFlags);
-}
-template <int E>
-__device__ __forceinline__ typename VecT<E>::type buffer_load(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
-    using T = typename VecT<E>::type;
-    if constexpr (E == 1) {
-        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voffset, soffset, 0));
-    } else if constexpr (E == 2) {
-        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, voffset, soffset, 0));
-    } else if constexpr (E == 4) {
-        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0));
-    } else {
-        static_assert(E == 8, "1, 2, 4 or 8 floats");
-        const auto lo = __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0);
-        const auto hi = __builtin_amdgcn_raw_buffer_load_b128(r, voffset + 16, soffset, 0);
-        T v;
-        v.lo = __builtin_bit_cast(typename VecT<4>::type, lo);
-        v.hi = __builtin_bit_cast(typename VecT<4>::type, hi);
-        return v;
-    }
 }
 
 // The state pass: the end state of every segment but a sequence's last, and
@@ -416,7 +387,7 @@ ssd_scan_kernel(ScanArgs a) {
     // and chunk k is committed to LDS buffer k & 1.
     constexpr int kNone = 0x7ffffff0;
     const int x_tok = H * P * int(sizeof(float));
-    int vo_bc[S::U_BC], lo_bc[S::U_BC], vo_x[S::U_X];
+    int vo_bc[S::U_BC], lo_bc[S::U_BC], vo_x[S::U_X], lo_x[S::U_X];
 #pragma unroll
     for (int u = 0; u < S::U_BC; ++u) {
         const int q = u * kThreads + tid;            // unit = (token, 4-group)
@@ -429,6 +400,7 @@ ssd_scan_kernel(ScanArgs a) {
         const int q = u * kThreads + tid;            // unit = (token, 4 rows)
         const int tt = q / (S::RBW / 4), pi = 4 * (q - tt * (S::RBW / 4));
         vo_x[u] = pi < rows_wg ? (tt * H * P + fr_wg + pi) * int(sizeof(float)) : kNone;
+        lo_x[u] = tt * S::XR + pi;
     }
     // dt: lane 16 j + t of wave 0 takes token t of head h_wg + j
     const int vo_dt = (tid < 64 && hrow_ok) ? (tl * H + h_wg + kq) * int(sizeof(float)) : kNone;
@@ -474,7 +446,7 @@ ssd_scan_kernel(ScanArgs a) {
             }
         }
 #pragma unroll
-        for (int u = 0; u < S::U_X; ++u) reinterpret_cast<f4 *>(base + S::OFF_X)[u * kThreads + tid] = sg.px[u];
+        for (int u = 0; u < S::U_X; ++u) *reinterpret_cast<f4 *>(base + S::OFF_X + lo_x[u]) = sg.px[u];
         if (tid < 64) {                                  // wave 0: row j = head h_wg + j, lane t = token t
             const float dtv = (tl < nt_ && hrow_ok) ? dt_transform(sg.pdt, bias_j, a.dt_softplus) : 0.f;
             const float Sv = row_prefix_sum(dtv * A_j);
@@ -575,7 +547,7 @@ ssd_scan_kernel(ScanArgs a) {
 #pragma unroll
         for (int i = 0; i < TW; ++i)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) xr[i][v] = base[S::OFF_X + (4 * kq + v) * S::RBW + 16 * TW * w + 16 * i + tl];
+            for (int v = 0; v < 4; ++v) xr[i][v] = base[S::OFF_X + (4 * kq + v) * S::XR + 16 * TW * w + 16 * i + tl];
         float bup[4][NT];
 #pragma unroll
         for (int q = 0; q < 4; ++q)

@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "correct_mfma.hpp"
+#include "decode_kernel.hpp"
 #include "scan_kernel.hpp"
 #include "ssd_kernel.hpp"
 #include "status.hpp"
@@ -126,6 +127,16 @@ int launch(const ScanArgs &a, hipStream_t stream) {
     return err == hipSuccess ? SSM_OK : hip_fail(err, SSM_ERR_LAUNCH);
 }
 
+// The decode step on the vector path with no option bits (decode_kernel.hpp).
+template <class S>
+int launch_decode(const ScanArgs &a, hipStream_t stream) {
+    ScanArgs args = a;
+    void *params[] = {&args};
+    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&ssm::decode_kernel<S>),
+                                           dim3(unsigned(a.n_blocks)), dim3(kThreads), params, 0, stream);
+    return err == hipSuccess ? SSM_OK : hip_fail(err, SSM_ERR_LAUNCH);
+}
+
 // Calls f.template run<R, J, CT, DR, DJ>() for the table row: the compile-time
 // shapes are read from kShapes itself, so the kernels and the host geometry
 // (geo_for) cannot disagree.
@@ -180,7 +191,9 @@ struct Launch {
     int run() const {
         constexpr int SCT = seg_chunk(CT);
         switch (kind) {
-        case Kind::kDecode: return launch_opt<Shape<DR, DJ, 1>, Mode::kDecode>(a, vec, opt, stream);
+        case Kind::kDecode:
+            if (vec && opt == 0) return launch_decode<Shape<DR, DJ, 1>>(a, stream);
+            return launch_opt<Shape<DR, DJ, 1>, Mode::kDecode>(a, vec, opt, stream);
         case Kind::kPrefill: return launch_opt<Shape<R, J, CT>, Mode::kPrefill>(a, vec, opt, stream);
         case Kind::kSegScan:
             return vec ? launch<Shape<R, J, SCT>, true, Mode::kSegScan>(a, stream)

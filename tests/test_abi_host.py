@@ -30,6 +30,26 @@ def test_exports_every_declared_symbol():
         assert hasattr(m.lib(), n), n
 
 
+def test_calib_library_exports_its_declared_symbol():
+    """The benchmark's stream-ceiling aid (include/ssm_calib.h) is a library
+    of its own; it loads and exports what its header declares, and rejects
+    bad arguments before any launch."""
+    path = os.path.join(os.path.dirname(m.LIB_PATH), "libssmcalib.so")
+    lib = ctypes.CDLL(path)
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(m.LIB_PATH)), "include",
+                            "ssm_calib.h")).read()
+    names = set(re.findall(r"^\s*int\s+(ssm_\w+)\s*\(", hdr, re.M))
+    assert names == {"ssm_calib_stream_rw"}
+    f = lib.ssm_calib_stream_rw
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+                  ctypes.c_void_p]
+    assert f(None, 1024, 1, 1.0, 0.0, None) == -2
+    assert f(FAKE + 4, 1024, 1, 1.0, 0.0, None) == -4
+    assert f(FAKE, 0, 1, 1.0, 0.0, None) == -2
+    assert f(FAKE, 100, 1, 1.0, 0.0, None) == -2          # not a multiple of 256 * per_lane
+    assert f(FAKE, 1024, 3, 1.0, 0.0, None) == -2
+
+
 def test_version_and_strerror():
     assert m.version() == 2
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
@@ -126,10 +146,11 @@ def test_no_kernel_uses_scratch():
     # 7 state-size classes x (vector, scalar) x (4 option sets x (prefill, decode)
     # + segment scan + correction) + 2 combine kernels + 6 matrix-core corrections
     # (3 contraction lengths, masked or not) + 3 x 3 matrix-core segment kernels
-    # (N 32, 64, 128; the state pass and the scan pass with one or two tiles per wave);
+    # (N 32, 64, 128; the state pass and the scan pass with one or two tiles per wave)
+    # + 7 branch-free decode kernels (one per state-size class, vector path);
     # conv1d + SiLU: (vector, scalar) x (4 history lengths x (decode, prefill)
     # + 3 with snapshots); gated RMSNorm: (vector, scalar) x 6 row-length classes
-    n_scan = 7 * 2 * (4 * 2 + 2) + 2 + 6 + 3 * 3
+    n_scan = 7 * 2 * (4 * 2 + 2) + 2 + 6 + 3 * 3 + 7
     n_conv = 2 * (4 * 2 + 3)
     n_norm = 2 * 6
     # gated delta rule: 5 key-width classes x (vector, scalar) x (prefill, decode)
