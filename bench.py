@@ -351,18 +351,17 @@ def summarize_trace(path):
                       "kernels": out}, indent=1))
 
 
+_CPM = None
+
+
 def _event_ms(fn, n, warm, stream):
-    import torch
-    for _ in range(warm):
-        fn()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(n):
-        fn()
-    b.record(stream)
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / n
+    """Milliseconds per call of ``fn``: ``warm`` untimed calls, then ``n``
+    calls queued behind a spin kernel and timed between HIP events (so short
+    kernels are not padded by the host's launch cost)."""
+    global _CPM
+    if _CPM is None:
+        _CPM = sleep_cycles_per_ms(stream)
+    return queued_steps_ms([fn] * n, warm, stream, _CPM)[0] / n
 
 
 def secondary(args, dev, stream):

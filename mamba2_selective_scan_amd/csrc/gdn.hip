@@ -12,6 +12,7 @@
 #include <cstdint>
 
 #include "gdn_chunk.hpp"
+#include "gdn_decode.hpp"
 #include "gdn_kernel.hpp"
 #include "status.hpp"
 
@@ -70,10 +71,26 @@ int launch(GdnArgs a, int64_t n_blocks, hipStream_t stream) {
     return err == hipSuccess ? SSM_OK : ssm::hip_fail(err, SSM_ERR_LAUNCH);
 }
 
+// The decode step on the vector path without snapshots (gdn_decode.hpp).
+template <class S>
+int launch_decode(GdnArgs a, int64_t n_blocks, hipStream_t stream) {
+    a.n_row_blocks = (a.Dv + S::RB - 1) / S::RB;
+    const int64_t blocks = n_blocks * a.n_row_blocks;
+    if (blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+    a.n_blocks = int32_t(blocks);
+    void *params[] = {&a};
+    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&ssm::gdn_decode_kernel<S>),
+                                           dim3(unsigned(blocks)), dim3(kThreads), params, 0, stream);
+    return err == hipSuccess ? SSM_OK : ssm::hip_fail(err, SSM_ERR_LAUNCH);
+}
+
 template <int R, int J, int CT, bool DECODE>
 int launch_vs(const GdnArgs &a, int64_t units, bool vec, hipStream_t stream) {
     using S = GdnShape<R, J, CT>;
     const bool snap = a.snapshots != nullptr;
+    if constexpr (DECODE) {
+        if (vec && !snap) return launch_decode<S>(a, units, stream);
+    }
     if (vec)
         return snap ? launch<S, true, DECODE, true>(a, units, stream)
                     : launch<S, true, DECODE, false>(a, units, stream);

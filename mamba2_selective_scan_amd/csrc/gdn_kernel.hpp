@@ -80,6 +80,41 @@ struct GdnShape {
     static constexpr int lds_floats(bool decode) { return decode ? 0 : 2 * BUF; }
 };
 
+// One token of the delta rule on a lane's E = 4J state values, given its J
+// groups of k and q: decay, the row's dots with k and q (DPP over the row's R
+// lanes), the rank-1 write; returns y, identical in every lane of the row.
+// The per-token prefill and both decode kernels go through here.
+template <int R, int J>
+__device__ __forceinline__ float gdn_token(float (&h)[4 * J], const f4 (&kv)[J], const f4 (&qv)[J],
+                                           float decay, float beta, float qk, float vr, float scale) {
+    float pk0 = 0.f, pk1 = 0.f, pq0 = 0.f, pq1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        float *hj = h + 4 * j;
+        hj[0] *= decay; hj[1] *= decay; hj[2] *= decay; hj[3] *= decay;
+        pk0 = __builtin_fmaf(hj[0], kv[j].x, pk0);
+        pk1 = __builtin_fmaf(hj[1], kv[j].y, pk1);
+        pk0 = __builtin_fmaf(hj[2], kv[j].z, pk0);
+        pk1 = __builtin_fmaf(hj[3], kv[j].w, pk1);
+        pq0 = __builtin_fmaf(hj[0], qv[j].x, pq0);
+        pq1 = __builtin_fmaf(hj[1], qv[j].y, pq1);
+        pq0 = __builtin_fmaf(hj[2], qv[j].z, pq0);
+        pq1 = __builtin_fmaf(hj[3], qv[j].w, pq1);
+    }
+    const float pred = row_allreduce<R>(pk0 + pk1);
+    const float oq = row_allreduce<R>(pq0 + pq1);
+    const float delta = (vr - pred) * beta;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        float *hj = h + 4 * j;
+        hj[0] = __builtin_fmaf(kv[j].x, delta, hj[0]);
+        hj[1] = __builtin_fmaf(kv[j].y, delta, hj[1]);
+        hj[2] = __builtin_fmaf(kv[j].z, delta, hj[2]);
+        hj[3] = __builtin_fmaf(kv[j].w, delta, hj[3]);
+    }
+    return scale * __builtin_fmaf(qk, delta, oq);
+}
+
 template <class S, bool VEC, bool DECODE, bool SNAP>
 __global__ void __launch_bounds__(kThreads) gdn_kernel(GdnArgs a) {
     extern __shared__ float4 lds_raw[];
@@ -170,36 +205,11 @@ __global__ void __launch_bounds__(kThreads) gdn_kernel(GdnArgs a) {
         }
     }
 
-    // One token on the lane's E values given its J groups of k and q; returns
-    // y (identical in every lane of the row).  Decode and prefill share it.
+    // One token on the lane's E values (gdn_token): y, identical in every
+    // lane of the row.  Decode and prefill share it.
     auto token = [&](const f4 (&kv)[J], const f4 (&qv)[J], float decay, float beta, float qk,
                      float vr) -> float {
-        float pk0 = 0.f, pk1 = 0.f, pq0 = 0.f, pq1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            float *hj = h + 4 * j;
-            hj[0] *= decay; hj[1] *= decay; hj[2] *= decay; hj[3] *= decay;
-            pk0 = __builtin_fmaf(hj[0], kv[j].x, pk0);
-            pk1 = __builtin_fmaf(hj[1], kv[j].y, pk1);
-            pk0 = __builtin_fmaf(hj[2], kv[j].z, pk0);
-            pk1 = __builtin_fmaf(hj[3], kv[j].w, pk1);
-            pq0 = __builtin_fmaf(hj[0], qv[j].x, pq0);
-            pq1 = __builtin_fmaf(hj[1], qv[j].y, pq1);
-            pq0 = __builtin_fmaf(hj[2], qv[j].z, pq0);
-            pq1 = __builtin_fmaf(hj[3], qv[j].w, pq1);
-        }
-        const float pred = row_allreduce<R>(pk0 + pk1);
-        const float oq = row_allreduce<R>(pq0 + pq1);
-        const float delta = (vr - pred) * beta;
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            float *hj = h + 4 * j;
-            hj[0] = __builtin_fmaf(kv[j].x, delta, hj[0]);
-            hj[1] = __builtin_fmaf(kv[j].y, delta, hj[1]);
-            hj[2] = __builtin_fmaf(kv[j].z, delta, hj[2]);
-            hj[3] = __builtin_fmaf(kv[j].w, delta, hj[3]);
-        }
-        return a.scale * __builtin_fmaf(qk, delta, oq);
+        return gdn_token<R, J>(h, kv, qv, decay, beta, qk, vr, a.scale);
     };
 
     if constexpr (DECODE) {

@@ -119,8 +119,13 @@ struct Shape {
     static constexpr int OFF_Y = OFF_X + CT * RB;
     static constexpr int OFF_DT = OFF_Y + CT * YR;
     static constexpr int OFF_DA = OFF_DT + CT;
-    static constexpr int OFF_LAZY = OFF_DA + CT;    // 1: the chunk runs with the decay deferred
-    static constexpr int BUF = ((OFF_LAZY + 1) + 3) / 4 * 4;
+    // the decay is deferred over sub-chunks of SUB tokens (one 16-lane DPP row
+    // of prefix products each), whatever the staging chunk, so a chunk of 32
+    // and two of 16 give the same bits
+    static constexpr int SUB = CT < 16 ? CT : 16;
+    static constexpr int NSUB = CT / SUB;
+    static constexpr int OFF_LAZY = OFF_DA + CT;    // [NSUB] 1: the sub-chunk runs with the decay deferred
+    static constexpr int BUF = ((OFF_LAZY + NSUB) + 3) / 4 * 4;
     static constexpr int TILE = RB * NPT;           // state tile (scalar path), floats
     // register prefetch units per thread
     static constexpr int U_BC = (CT * NP / 4 + kThreads - 1) / kThreads;    // float4 of B (and of C)
@@ -210,37 +215,17 @@ __device__ __forceinline__ float row_prefix_product(float v) {
     return v;
 }
 
-// Inclusive running product over lanes 0..CT-1 of the wavefront (CT <= 64,
-// all 64 lanes active): a DPP product inside each 16-lane row, then each row
-// times the totals of the rows before it.
-template <int CT>
-__device__ __forceinline__ float chunk_prefix_product(float v) {
-    static_assert(CT <= 64, "one wavefront");
-    v = row_prefix_product(v);
-    if constexpr (CT > 16) {
-        const int lane = threadIdx.x & 63;
-        const float t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
-        float m = lane >= 16 ? t0 : 1.f;
-        if constexpr (CT > 32) {
-            const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
-            m = lane >= 32 ? m * t1 : m;
-            if constexpr (CT > 48) {
-                const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
-                m = lane >= 48 ? m * t2 : m;
-            }
-        }
-        v *= m;
-    }
-    return v;
-}
-
-// Deferred decay.  Within a chunk the row is kept as h / sigma_t, with
-// sigma_t the product of dA from the chunk start through token t; then
+// Deferred decay.  Within a sub-chunk of at most 16 tokens (Shape::SUB) the
+// row is kept as h / sigma_t, with sigma_t the product of dA from the
+// sub-chunk start through token t; then
 //     h / sigma_t = h / sigma_{t-1} + b * (x * dt / sigma_t)
 // is one fused multiply-add per element instead of a multiply and an FMA, y is
-// sigma_t times the row's dot with C, and the chunk ends by multiplying the
-// row by its sigma.  A chunk whose sigma would fall below this floor (so that
-// 1/sigma could overflow the stored row) runs the direct update instead.
+// sigma_t times the row's dot with C, and the sub-chunk ends by multiplying
+// the row by its sigma.  A sub-chunk whose sigma would fall below this floor
+// (so that 1/sigma could overflow the stored row) runs the direct update
+// instead.  Sub-chunks start every 16 tokens of a sequence (every chunk for
+// chunks of fewer tokens), so the rounding does not depend on the staging
+// chunk.
 constexpr float kLazyFloor = 0x1p-40f;
 
 // Load 4 consecutive floats, the ones at index >= n_valid read as 0.
@@ -588,8 +573,10 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                 if (tid < 64) {                              // wave 0, all lanes active
                     const float dtv = dt_eff();
                     const float dA = (tid < nt) ? expf(dtv * A_h) : 1.f;
-                    const float loc = chunk_prefix_product<CT>(dA);     // from the chunk start
-                    const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(loc), CT - 1));
+                    // from the start of the token's sub-chunk (its DPP row; for
+                    // chunks of at most 16 tokens, the chunk)
+                    const float loc = row_prefix_product(dA);
+                    const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(loc), S::SUB - 1));
                     if constexpr (SEGMENTED) {
                         const float cum = run * loc;                     // from the segment start
                         if constexpr (CORRECT) {
@@ -605,14 +592,23 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                         run *= total;
                     }
                     if constexpr (LAZY) {
-                        // one-token chunks keep the direct update, so a lone token
-                        // gives the same bits as decode
-                        const bool lazy = nt > 1 && total >= kLazyFloor;
+                        // per sub-chunk; one-token sub-chunks keep the direct
+                        // update, so a lone token gives the same bits as decode
+                        bool lazy_k[S::NSUB];
+#pragma unroll
+                        for (int k = 0; k < S::NSUB; ++k) {
+                            const float tot = __int_as_float(
+                                __builtin_amdgcn_readlane(__float_as_int(loc), S::SUB * k + S::SUB - 1));
+                            lazy_k[k] = nt - S::SUB * k > 1 && tot >= kLazyFloor;
+                        }
+                        bool lazy = lazy_k[0];
+#pragma unroll
+                        for (int k = 1; k < S::NSUB; ++k) lazy = (tid / S::SUB == k) ? lazy_k[k] : lazy;
                         if (tid < CT) {
                             base[S::OFF_DT + tid] = lazy ? dtv / loc : dtv;
                             base[S::OFF_DA + tid] = lazy ? loc : dA;
                         }
-                        if (tid == 0) base[S::OFF_LAZY] = lazy ? 1.f : 0.f;
+                        if (tid < S::NSUB) base[S::OFF_LAZY + tid] = lazy ? 1.f : 0.f;
                     }
                 }
             } else {
@@ -680,8 +676,10 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                 return y_scale(base, tt, lazy_tag) * row_allreduce<R>(token_part(base, tt, lazy_tag));
             }
         };
-        auto run_tokens = [&](const float *base, float *Ys, int nt, auto lazy_tag) {
-            int t0 = 0;
+        // tokens tb .. tb + nt - 1 of the staged chunk
+        auto run_tokens = [&](const float *base, float *Ys, int tb, int nt, auto lazy_tag) {
+            int t0 = tb;
+            nt += tb;
             float y_keep = 0.f;
             if constexpr (!CORRECT && !SNAPSHOTS) {
                 // KY tokens at a time: their partials reduce-scattered over the
@@ -719,17 +717,23 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
             const float *base = lds + buf * S::BUF;
             float *Ys = lds + buf * S::BUF + S::OFF_Y + i;
             if constexpr (LAZY) {
-                if (base[S::OFF_LAZY] != 0.f) {                 // chunk-uniform
-                    run_tokens(base, Ys, nt, std::true_type{});
-                    const float sigma = base[S::OFF_DA + nt - 1];
+#pragma unroll 1
+                for (int k = 0; k < S::NSUB; ++k) {
+                    const int tb = S::SUB * k;
+                    const int n = min(S::SUB, nt - tb);
+                    if (n <= 0) break;
+                    if (base[S::OFF_LAZY + k] != 0.f) {         // sub-chunk-uniform
+                        run_tokens(base, Ys, tb, n, std::true_type{});
+                        const float sigma = base[S::OFF_DA + tb + n - 1];
 #pragma unroll
-                    for (int e = 0; e < E; ++e) h[e] *= sigma;
-                    return;
+                        for (int e = 0; e < E; ++e) h[e] *= sigma;
+                    } else {
+                        // a direct sub-chunk (one token, or a decay below the floor)
+                        run_tokens(base, Ys, tb, n, std::false_type{});
+                    }
                 }
-                // a direct chunk (one token, or a decay product below the floor)
-                run_tokens(base, Ys, nt, std::false_type{});
             } else {
-                run_tokens(base, Ys, nt, std::false_type{});
+                run_tokens(base, Ys, 0, nt, std::false_type{});
             }
         };
 

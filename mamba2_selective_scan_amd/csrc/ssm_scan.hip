@@ -162,9 +162,10 @@ int with_row(const ShapeRow &row, F &&f) {
     }
 }
 
-// What a launch computes: a whole-sequence prefill, a decode step, or one of
-// the two kernel halves of a time-split prefill (segment scans, corrections).
-enum class Kind { kPrefill, kDecode, kSegScan, kCorrect };
+// What a launch computes: a whole-sequence prefill (with the table's chunk, or
+// half of it), a decode step, or one of the two kernel halves of a time-split
+// prefill (segment scans, corrections).
+enum class Kind { kPrefill, kPrefillHalf, kDecode, kSegScan, kCorrect };
 
 constexpr int seg_chunk(int CT) { return CT / 2 > 2 ? CT / 2 : 2; }
 
@@ -195,6 +196,9 @@ struct Launch {
             if (vec && opt == 0) return launch_decode<Shape<DR, DJ, 1>>(a, stream);
             return launch_opt<Shape<DR, DJ, 1>, Mode::kDecode>(a, vec, opt, stream);
         case Kind::kPrefill: return launch_opt<Shape<R, J, CT>, Mode::kPrefill>(a, vec, opt, stream);
+        case Kind::kPrefillHalf:
+            return vec ? launch<Shape<R, J, SCT>, true, Mode::kPrefill>(a, stream)
+                       : launch<Shape<R, J, SCT>, false, Mode::kPrefill>(a, stream);
         case Kind::kSegScan:
             return vec ? launch<Shape<R, J, SCT>, true, Mode::kSegScan>(a, stream)
                        : launch<Shape<R, J, SCT>, false, Mode::kSegScan>(a, stream);
@@ -216,6 +220,7 @@ struct LdsBytes {
         switch (kind) {
         case Kind::kDecode: floats = Shape<DR, DJ, 1>::lds_floats(Mode::kDecode, vec); break;
         case Kind::kPrefill: floats = Shape<R, J, CT>::lds_floats(Mode::kPrefill, vec); break;
+        case Kind::kPrefillHalf: floats = Shape<R, J, SCT>::lds_floats(Mode::kPrefill, vec); break;
         case Kind::kSegScan: floats = Shape<R, J, SCT>::lds_floats(Mode::kSegScan, vec); break;
         case Kind::kCorrect: floats = Shape<R, J, SCT>::lds_floats(Mode::kCorrect, vec); break;
         }
@@ -231,6 +236,7 @@ Geo geo_for(const ShapeRow &row, Kind kind) {
     const bool decode = kind == Kind::kDecode;
     const int R = decode ? row.DR : row.R;
     const int J = decode ? row.DJ : row.J;
+    // half-chunk prefills and segment scans take seg_chunk(CT)
     const int CT = decode ? 1 : (kind == Kind::kPrefill ? row.CT : seg_chunk(row.CT));
     return Geo{R, 4 * J, ssm::kWaves * (64 / R), CT};
 }
@@ -244,6 +250,30 @@ int check_dims(const ssm_scan_dims *d) {
     if (d->n_heads % d->n_groups != 0) return SSM_ERR_DIMS;
     if (d->d_state > SSM_SCAN_MAX_D_STATE) return SSM_ERR_UNSUPPORTED;
     return SSM_OK;
+}
+
+// Whole-sequence prefill: the table's chunk, unless the grid would not fit on
+// the GPU at once with it but would with half the chunk (half the LDS per
+// workgroup).  A grid that runs in two rounds makes its last workgroups --
+// often a batch's longest sequences, at the end of the grid -- wait for the
+// first round, so their token chains run back to back (measured on the mixed
+// batch, 8 sequences up to 150 tokens at H 16, P 96, N 100: 768 workgroups,
+// 512 resident at 74 KB of LDS each).  Counted from LDS alone (at most four
+// workgroups of four wavefronts per CU; every gfx950 part has 256 CUs), so
+// the choice needs no device query.
+constexpr int64_t kCus = 256;
+constexpr int kLdsPerCu = 160 * 1024;
+int64_t resident_per_cu(int lds_bytes) {
+    const int64_t by_lds = lds_bytes > 0 ? kLdsPerCu / lds_bytes : 4;
+    return std::min<int64_t>(4, by_lds);
+}
+Kind prefill_kind(const ShapeRow &row, bool vec, int opt, int64_t n_blocks) {
+    if (opt != 0) return Kind::kPrefill;
+    const int lds_full = with_row(row, LdsBytes{vec, Kind::kPrefill});
+    const int lds_half = with_row(row, LdsBytes{vec, Kind::kPrefillHalf});
+    const bool two_rounds = n_blocks > kCus * resident_per_cu(lds_full);
+    const bool one_round_half = n_blocks <= kCus * resident_per_cu(lds_half);
+    return two_rounds && one_round_half ? Kind::kPrefillHalf : Kind::kPrefill;
 }
 
 // How a prefill is cut over time.  A single long sequence exposes only
@@ -368,8 +398,8 @@ int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_
     const ShapeRow *row = shape_for(d->d_state);
     if (!row) return SSM_ERR_UNSUPPORTED;
     const bool split = !decode && plan.n_segs > 1;
-    const Kind kind = decode ? Kind::kDecode : (split ? Kind::kSegScan : Kind::kPrefill);
-    const int RB = geo_for(*row, kind).RB;
+    Kind kind = decode ? Kind::kDecode : (split ? Kind::kSegScan : Kind::kPrefill);
+    const int RB = geo_for(*row, kind).RB;       // the same for every prefill chunk
     const int64_t n_row_blocks = (int64_t(d->head_dim) + RB - 1) / RB;
     const int64_t n_blocks = int64_t(n_seqs) * (split ? plan.n_segs : 1) * d->n_heads * n_row_blocks;
     if (n_blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
@@ -381,6 +411,7 @@ int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_
         if (p && !aligned(p, 16)) vec = false;
     }
     if (!aligned(slot, 4) || (cu_seqlens && !aligned(cu_seqlens, 4))) return SSM_ERR_ALIGN;
+    if (kind == Kind::kPrefill) kind = prefill_kind(*row, vec, opt, n_blocks);
 
     ScanArgs a{};
     a.cu_seqlens = cu_seqlens;
@@ -706,7 +737,11 @@ int ssm_scan_query_geometry(const ssm_scan_dims *dims, int32_t n_seqs, int32_t d
     const ShapeRow *row = shape_for(dims->d_state);
     if (!row) return SSM_ERR_UNSUPPORTED;
     const bool vec = aligned16 && dims->d_state % 4 == 0 && dims->head_dim % 4 == 0;
-    const Kind kind = decode ? Kind::kDecode : Kind::kPrefill;
+    Kind kind = decode ? Kind::kDecode : Kind::kPrefill;
+    if (!decode) {
+        const int64_t rb = geo_for(*row, kind).RB;
+        kind = prefill_kind(*row, vec, 0, int64_t(n_seqs) * dims->n_heads * ((dims->head_dim + rb - 1) / rb));
+    }
     const Geo geo = geo_for(*row, kind);
     out->lanes_per_row = geo.R;
     out->elems_per_lane = geo.E;

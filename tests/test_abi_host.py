@@ -147,18 +147,35 @@ def test_no_kernel_uses_scratch():
     # + segment scan + correction) + 2 combine kernels + 6 matrix-core corrections
     # (3 contraction lengths, masked or not) + 3 x 3 matrix-core segment kernels
     # (N 32, 64, 128; the state pass and the scan pass with one or two tiles per wave)
-    # + 7 branch-free decode kernels (one per state-size class, vector path);
+    # + 7 branch-free decode kernels (one per state-size class, vector path)
+    # + 7 x 2 whole-sequence prefills at half the chunk (vector, scalar);
     # conv1d + SiLU: (vector, scalar) x (4 history lengths x (decode, prefill)
     # + 3 with snapshots); gated RMSNorm: (vector, scalar) x 6 row-length classes
-    n_scan = 7 * 2 * (4 * 2 + 2) + 2 + 6 + 3 * 3 + 7
+    n_scan = 7 * 2 * (4 * 2 + 2) + 2 + 6 + 3 * 3 + 7 + 7 * 2
     n_conv = 2 * (4 * 2 + 3)
     n_norm = 2 * 6
     # gated delta rule: 5 key-width classes x (vector, scalar) x (prefill, decode)
     # x (snapshots or not)
     # + the chunked prefill: (prep, scan) x key widths 64 and 128
-    n_gdn = 5 * 2 * 2 * 2 + 2 * 2
+    # + 5 branch-free decode kernels (one per key-width class, vector path)
+    n_gdn = 5 * 2 * 2 * 2 + 2 * 2 + 5
     assert len(names) == n_scan + n_conv + n_norm + n_gdn and len(scratch) == len(names)
     assert all(v == 0 for v in scratch), dict(zip(names, scratch))
+
+
+@pytest.mark.parametrize("n_seqs", [1, 2, 3, 4, 5, 8])
+def test_prefill_chunk_by_grid_size(n_seqs):
+    """Whole-sequence prefill takes half the table's chunk when its grid would
+    not be resident at once with the full chunk (two workgroups of 74 KB of
+    LDS per CU, 256 CUs) but would be with half (four per CU)."""
+    g = m.geometry(64, 96, 128, 8, n_seqs)          # 6 row blocks per head: 384 per sequence
+    assert g["blocks"] == 384 * n_seqs
+    half = 512 < g["blocks"] <= 1024
+    assert g["chunk_tokens"] == (16 if half else 32)
+    assert g["lds_bytes"] * (4 if half else 2) <= 160 * 1024
+    mixed = m.geometry(16, 96, 100, 4, 8)            # the mixed edge batch: 768 workgroups
+    assert mixed["blocks"] == 768 and mixed["chunk_tokens"] == 16
+    assert m.geometry(64, 64, 128, 8, 16, decode=True)["chunk_tokens"] == 1
 
 
 def test_single_hip_runtime():

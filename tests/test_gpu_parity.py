@@ -100,6 +100,27 @@ def test_shapes_and_chunk_edges(ssm, orc, N, P):
     assert np.array_equal(st[7], case.state[7])    # zero-length resume: unchanged
 
 
+@pytest.mark.parametrize("offset", [0, 1])
+def test_prefill_half_chunk_grid(ssm, orc, offset):
+    """Batches whose grid needs half the chunk to be resident at once (2 x 384
+    workgroups at H 64, P 96): lengths around the 16-token chunk, fresh and
+    resumed, poisoned fresh slots, an empty fresh sequence, unused slots;
+    vector and scalar paths."""
+    for k, (lengths, fresh, slots) in enumerate((([15, 40], [1, 0], [2, 0]),
+                                                 ([16, 33], [0, 1], [1, 3]),
+                                                 ([17, 0], [0, 1], [0, 4]))):
+        case = ssm_inputs.make_case(64, 96, 128, 8, lengths, fresh, seed=70 + 2 * k + offset,
+                                    slots=slots, n_slots=5, poison_fresh=True,
+                                    sentinel_unused=True, name=f"half_chunk_grid_{lengths}")
+        g = ssm.geometry(64, 96, 128, 8, 2, aligned=offset == 0)
+        say(f"half-chunk grid {lengths}, offset {offset}: {g}")
+        assert g["chunk_tokens"] == 16 and g["blocks"] == 768
+        y, st = run_gpu(case, "prefill", offset_floats=offset)
+        y32, st32 = orc.scan_case(case, precision="f32")
+        assert_parity(case, y, st, y32, st32)
+    assert not np.any(st[4])                       # the fresh empty sequence's slot is zeroed
+
+
 @pytest.mark.parametrize("name", ["mixed", "tiny"])
 def test_scalar_path_unaligned_pointers(ssm, orc, name):
     """Arrays placed one float past a 16-byte boundary take the scalar path
