@@ -576,6 +576,23 @@ def gated_delta(args, dev, stream):
     return out
 
 
+def summarize_counters(path):
+    """Per-kernel means of each counter in a rocprofv3 counter collection
+    (``*_counter_collection.csv``), over that kernel's dispatches.  Prints one
+    JSON object (the input of the committed counter summaries)."""
+    import csv
+    import statistics
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            k = r["Kernel_Name"]
+            acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = {k: {c: {"mean": statistics.fmean(v), "dispatches": len(v)} for c, v in cs.items()}
+           for k, cs in acc.items()}
+    print(json.dumps({"kernel_hash": kernel_source_hash(), "counters": os.path.basename(path),
+                      "kernels": out}, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -598,10 +615,15 @@ def main():
                          "write stream over the decode step's 16 rotating slot sets")
     ap.add_argument("--summarize-trace", metavar="CSV",
                     help="print per-kernel statistics of a rocprofv3 kernel trace and exit")
+    ap.add_argument("--summarize-counters", metavar="CSV",
+                    help="print per-kernel counter means of a rocprofv3 counter collection and exit")
     args = ap.parse_args()
 
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the scan needs no collective and this build runs "
