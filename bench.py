@@ -266,8 +266,9 @@ def stream_ceiling(state, n_sets, steps, warmup, stream, cycles_per_ms):
 def profile_mode(args, dev, stream):
     """One kernel kind, eager launches, for counter and trace runs: every
     dispatch of the named kernel is the workload of the headline (decode), of
-    the prefill (split on the matrix cores, or one pass on the VALU), or a
-    plain copy / stream for calibrating counters."""
+    the prefill (split on the matrix cores, or one pass on the VALU), of the
+    chunked gated delta rule, or a plain copy / stream for calibrating
+    counters."""
     import torch
 
     import mamba2_selective_scan_amd as ssm
@@ -303,6 +304,24 @@ def profile_mode(args, dev, stream):
             step(i)
         ms = _timed(step, args.steps, stream)
         out.update(algorithmic_bytes=decode_bytes(), ms_per_launch_eager=ms)
+    elif args.mode == "gdn_prefill":
+        c = ssm_inputs.gdn_workload("prefill4096")
+        t = {f: torch.from_numpy(getattr(c, f)).to(dev)
+             for f in ("q", "k", "v", "g", "beta", "state", "cu_seqlens", "slot", "fresh")}
+        Hv, D = t["v"].shape[1], t["v"].shape[2]
+        y = torch.empty((c.n_tokens, Hv, D), device=dev)
+        max_len = int((c.cu_seqlens[1:] - c.cu_seqlens[:-1]).max())
+        ws = torch.empty(max(ssm.gdn_workspace_size(Hv, t["k"].shape[1], t["k"].shape[2], D,
+                                                    int(c.slot.shape[0]), max_len), 1),
+                         dtype=torch.uint8, device=dev)
+
+        def once(i):
+            ssm.gdn_prefill_ws(t["q"], t["k"], t["v"], t["g"], t["beta"], t["state"],
+                               t["cu_seqlens"], t["slot"], t["fresh"], max_len, y=y, workspace=ws)
+        for i in range(args.warmup):
+            once(i)
+        ms = _timed(once, args.steps, stream)
+        out.update(algorithmic_flops=7 * c.n_tokens * Hv * D * D, ms_per_launch=ms)
     else:
         pc = ssm_inputs.workload("prefill4096")
         pd = ssm.to_device(pc, dev)
@@ -545,7 +564,7 @@ def gated_delta(args, dev, stream):
     tf_c = flops / (ms_c * 1e-3) / 1e12
     tf = flops / (ms * 1e-3) / 1e12
     out["gdn_prefill_1x4096_Hv32_Hk16_D128"] = {
-        "ms": round(ms_c, 4), "entry": "ssm_gdn_prefill_ws (chunks of 16 tokens, matrix cores)",
+        "ms": round(ms_c, 4), "entry": "ssm_gdn_prefill_ws (chunks of 32 tokens, matrix cores)",
         "TFLOPs": round(tf_c, 2), "frac_fp32_mfma": round(tf_c / FP32_MFMA_PEAK_TFLOPS, 4),
         "workspace_bytes": int(ws.numel()), "algorithmic_flops": flops,
         "per_token_kernel": {
@@ -606,10 +625,12 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the secondary workloads (decode 256x1, mixed batch, options)")
-    ap.add_argument("--mode", choices=("all", "decode", "prefill", "prefill1", "copy", "stream16"),
+    ap.add_argument("--mode", choices=("all", "decode", "prefill", "prefill1", "gdn_prefill", "copy",
+                                       "stream16"),
                     default="all",
                     help="decode/prefill: launch only that path (prefill: the time-split path; "
-                         "prefill1: the unsplit single kernel), eagerly, and print its "
+                         "prefill1: the unsplit single kernel; gdn_prefill: the chunked "
+                         "gated delta rule, 1 x 4096), eagerly, and print its "
                          "timing (for counter runs); copy: a plain 256 MiB device copy, the "
                          "reference for scaling HBM byte counters; stream16: the read-modify-"
                          "write stream over the decode step's 16 rotating slot sets")

@@ -80,18 +80,18 @@ int ssm_gdn_prefill(const ssm_gdn_dims *dims, int32_t n_seqs, int32_t n_tokens,
 
 /*
  * The same recurrence over a packed batch, with the prefill of long sequences
- * in chunked matrix form on the matrix cores.  Over a chunk of 16 tokens the
+ * in chunked matrix form on the matrix cores.  Over a chunk of 32 tokens the
  * per-token updates regroup into dense products ("ssm_gated_delta.cu" runs
  * them one token at a time; the regrouping is exact in real arithmetic, so
  * results agree with ssm_gdn_prefill to rounding):
  *     Delta = T diag(beta) (V - diag(gamma) K S0^T),  T = (I + A)^-1,
  *     A[t][s] = beta_t (gamma_t / gamma_s) (k_t . k_s) for s < t,
- *     y = scale (diag(gamma) Q S0^T + M Delta),  S' = gamma_15 S0 + Delta^T diag(gamma_15/gamma) K,
+ *     y = scale (diag(gamma) Q S0^T + M Delta),  S' = gamma_31 S0 + Delta^T diag(gamma_31/gamma) K,
  * with gamma the running product of exp(g) from the chunk start and M the
  * decayed q . k for s <= t.  Two kernels on `stream`: per (sequence, chunk, key
  * head) T, M and the weights go to the workspace; then the chunks are scanned.
  *   max_seqlen  host int >= every sequence's length (precondition: chunks past
- *               ceil(max_seqlen/16) are not run, and no memory outside the
+ *               ceil(max_seqlen/32) are not run, and no memory outside the
  *               arrays and the workspace is touched)
  *   workspace   DEVICE memory of at least ssm_gdn_prefill_workspace_size()
  *               bytes, 16-byte aligned, owned by the caller; its contents are

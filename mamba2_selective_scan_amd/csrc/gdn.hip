@@ -117,17 +117,17 @@ int dispatch(const GdnArgs &a, int64_t units, bool vec, bool decode, hipStream_t
 
 // The chunked matrix-core prefill: key widths 64 and 128, whole 16-row value
 // tiles, sequences of at least kGdnChunkMinLen tokens (shorter ones gain
-// nothing from chunks of 16), no snapshots, 16-byte aligned arrays.
+// nothing from chunks), no snapshots, 16-byte aligned arrays.
 constexpr int kGdnChunkMinLen = 32;
 bool chunk_shape(const ssm_gdn_dims *d) {
-    // a chunk's rows of q, k and v (16 tokens) must fit 32-bit buffer offsets
-    const int64_t chunk_bytes = 16 * int64_t(sizeof(float));
+    // a chunk's rows of q, k and v must fit 32-bit buffer offsets
+    const int64_t chunk_bytes = ssm::GdnUnit::CT * int64_t(sizeof(float));
     return (d->d_k == 64 || d->d_k == 128) && d->d_v % 16 == 0 &&
            int64_t(d->n_k_heads) * d->d_k * chunk_bytes < INT32_MAX &&
            int64_t(d->n_v_heads) * d->d_v * chunk_bytes < INT32_MAX;
 }
 size_t chunk_ws_bytes(const ssm_gdn_dims *d, int32_t n_seqs, int32_t max_seqlen) {
-    const size_t chunks = (size_t(max_seqlen) + 15) / 16;
+    const size_t chunks = (size_t(max_seqlen) + ssm::GdnUnit::CT - 1) / ssm::GdnUnit::CT;
     return size_t(n_seqs) * chunks * size_t(d->n_v_heads) * ssm::GdnUnit::FLOATS * sizeof(float);
 }
 
@@ -203,7 +203,7 @@ int gdn_common(const ssm_gdn_dims *d, int32_t n_seqs, int32_t n_tokens, const in
         ssm::GdnChunkArgs ca{};
         ca.a = a;
         ca.ws = static_cast<float *>(ws);
-        ca.max_chunks = int32_t((int64_t(max_seqlen) + 15) / 16);
+        ca.max_chunks = int32_t((int64_t(max_seqlen) + ssm::GdnUnit::CT - 1) / ssm::GdnUnit::CT);
         hipStream_t st = static_cast<hipStream_t>(stream);
         return d->d_k == 64 ? launch_chunked<4>(ca, n_seqs, st) : launch_chunked<8>(ca, n_seqs, st);
     }

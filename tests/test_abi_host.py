@@ -354,14 +354,15 @@ def test_gdn_argument_errors(decode):
 
 def test_gdn_workspace_size():
     size = lambda *a: m.gdn_workspace_size(*a)
-    # one unit of 592 floats per (sequence, 16-token chunk, value head)
-    assert size(32, 16, 128, 128, 1, 4096) == 256 * 32 * 592 * 4
-    assert size(4, 2, 64, 32, 3, 33) == 3 * 3 * 4 * 592 * 4
+    # one unit of 1680 floats per (sequence, 32-token chunk, value head)
+    assert size(32, 16, 128, 128, 1, 4096) == 128 * 32 * 1680 * 4
+    assert size(4, 2, 64, 32, 3, 33) == 3 * 2 * 4 * 1680 * 4
     assert size(4, 2, 128, 64, 3, 31) == 0       # short sequences: per-token kernel
     assert size(4, 2, 100, 64, 3, 500) == 0      # key width without a chunked form
     assert size(4, 2, 128, 24, 3, 500) == 0      # value rows not in 16-row tiles
     # a chunk's rows of v (or of q, k) past 32-bit buffer offsets: per-token kernel
-    assert size(1024, 1024, 128, 16384, 1, 64) == 4 * 1024 * 592 * 4
+    assert size(1024, 1024, 128, 8192, 1, 64) == 2 * 1024 * 1680 * 4
+    assert size(1024, 1024, 128, 16384, 1, 64) == 0
     assert size(2048, 2048, 128, 16384, 1, 64) == 0
     assert size(262144, 262144, 128, 16, 1, 64) == 0
     b = ctypes.c_size_t()

@@ -4,7 +4,7 @@
 Bar: max |gpu - ref| / (1 + |ref|) <= 1e-4 on y and on the final state of
 every used slot against the fp32 oracle (and the fp64 oracle on the long
 workload); unused slots bit for bit unchanged.  The chunked form regroups the
-recurrence's sums over 16-token chunks, so it agrees with the oracle and with
+recurrence's sums over 32-token chunks, so it agrees with the oracle and with
 the per-token kernel to rounding, not bit for bit.
 """
 import numpy as np
@@ -32,10 +32,11 @@ def orc():
 
 
 def test_gdn_chunked_headline(ssm, orc):
-    """1 x 4096, Hv 32 Hk 16 Dk = Dv = 128: the chunked form is taken."""
+    """1 x 4096, Hv 32 Hk 16 Dk = Dv = 128: the chunked form is taken (128
+    chunks of 32 tokens, one 1680-float workspace unit per chunk and value head)."""
     case = ssm_inputs.gdn_workload("prefill4096")
     need = ssm.gdn_workspace_size(case.Hv, case.Hk, case.Dk, case.Dv, 1, 4096)
-    assert need == 256 * 32 * 592 * 4, need
+    assert need == 128 * 32 * 1680 * 4, need
     say(f"gdn chunked prefill 1x4096: workspace {need} bytes")
     y, st = run_gdn_gpu(case, "prefill_ws")
     y32, s32 = orc.gdn_case(case)
@@ -47,12 +48,13 @@ def test_gdn_chunked_headline(ssm, orc):
 @pytest.mark.parametrize("Dk,Dv,Hv,Hk", [(128, 128, 4, 2), (64, 32, 3, 1), (128, 16, 2, 2),
                                          (64, 64, 4, 4)])
 def test_gdn_chunked_varlen(ssm, orc, Dk, Dv, Hv, Hk):
-    """Lengths around the chunk size (0, 1, 15, 16, 17, 33, 100, 250), fresh and
-    resuming sequences, NaN-poisoned fresh slots, sentinel unused slots."""
-    lengths = [0, 1, 15, 16, 17, 33, 100, 250]
-    fresh = [1, 0, 1, 0, 0, 1, 0, 1]
+    """Lengths around the chunk size and its 16-token tiles (0, 1, 15, 16, 17,
+    31, 32, 33, 100, 250), fresh and resuming sequences, NaN-poisoned fresh
+    slots, sentinel unused slots."""
+    lengths = [0, 1, 15, 16, 17, 31, 32, 33, 100, 250]
+    fresh = [1, 0, 1, 0, 0, 1, 0, 1, 0, 1]
     case = ssm_inputs.make_gdn_case(Hv, Hk, Dk, Dv, lengths, fresh, seed=700 + Dk + Dv,
-                                    slots=[3, 9, 0, 5, 7, 1, 8, 2], n_slots=11,
+                                    slots=[3, 9, 0, 5, 7, 1, 8, 2, 11, 12], n_slots=14,
                                     poison_fresh=True, sentinel_unused=True,
                                     name=f"gdn_chunked_Dk{Dk}_Dv{Dv}_Hv{Hv}_Hk{Hk}")
     assert ssm.gdn_workspace_size(Hv, Hk, Dk, Dv, len(lengths), 250) > 0
