@@ -112,10 +112,14 @@ struct Shape {
     static constexpr int OFF_C = OFF_B + CT * NP;
     static constexpr int OFF_X = OFF_C + CT * NP;
     // y tile rows padded: lane r of a row stores token r's y at row r, so with
-    // a row stride of RB lanes r and r + 64/RB hit one bank; YR spreads the
-    // 64 lanes of a store over distinct banks (64 banks; at most 2-way at 32)
-    // and keeps rows 16-byte aligned for the float4 flush
-    static constexpr int YR = R == 4 ? 80 : R == 8 ? 40 : R == 16 ? 20 : 12;
+    // a row stride of RB lanes r and r + 64/RB hit one bank.  Measured on gfx950
+    // (plain LDS probes): a 32-bit store goes 32 lanes at a time over 32 banks,
+    // and with R = 16 (16 tokens x 2 rows per half) it is conflict-free for a
+    // row stride of 2 mod 4 floats (4 mod 8 is 2-way, 0 mod 8 worse), so those
+    // rows take 18 floats and the flush reads them as float pairs (8-byte
+    // aligned); the other widths keep 16-byte aligned rows for a float4 flush.
+    static constexpr int YR = R == 4 ? 80 : R == 8 ? 40 : R == 16 ? 18 : 12;
+    static constexpr int YV = YR % 4 == 0 ? 4 : 2;   // floats per flush read
     static constexpr int OFF_Y = OFF_X + CT * RB;
     static constexpr int OFF_DT = OFF_Y + CT * YR;
     static constexpr int OFF_DA = OFF_DT + CT;
@@ -740,12 +744,14 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         auto flush_y = [&](int buf, int t0, int nt) {
             const float *Ys = lds + buf * S::BUF + S::OFF_Y;
             if constexpr (VEC) {
-                for (int q = tid; q < nt * (RB / 4); q += kThreads) {
-                    const int tt = q / (RB / 4);
-                    const int pi = 4 * (q - tt * (RB / 4));
+                constexpr int YV = S::YV;
+                using fy = float __attribute__((ext_vector_type(YV)));
+                for (int q = tid; q < nt * (RB / YV); q += kThreads) {
+                    const int tt = q / (RB / YV);
+                    const int pi = YV * (q - tt * (RB / YV));
                     if (pi < rows_valid)
-                        *reinterpret_cast<f4 *>(a.y + (int64_t(t0 + tt) * H + hd) * P + p0 + pi) =
-                            *reinterpret_cast<const f4 *>(Ys + tt * S::YR + pi);
+                        *reinterpret_cast<fy *>(a.y + (int64_t(t0 + tt) * H + hd) * P + p0 + pi) =
+                            *reinterpret_cast<const fy *>(Ys + tt * S::YR + pi);
                 }
             } else {
                 for (int q = tid; q < nt * RB; q += kThreads) {

@@ -34,7 +34,7 @@
 // read back.  The scan pass runs one workgroup per (sequence, time segment,
 // window of 64 TW rows of a B/C group): its four wavefronts own TW 16-row
 // tiles each.  B, C and x of a chunk are staged in LDS, double-buffered (rows
-// of B, C and x padded so the strided reads are conflict-free), the per-token
+// of B, C and x padded, each for the way it is read), the per-token
 // scalars of each head are formed once in wave 0, and G^T, the same for the
 // four wavefronts, is formed a quarter by each and summed through LDS.  G^T
 // only feeds the chunk's own y (never the state), so a chunk's y is finished
@@ -57,14 +57,21 @@ struct SsdScanShape {
     static constexpr int CT = 16;                   // tokens per chunk
     static constexpr int RBW = 64 * TW;             // rows per workgroup (4 waves x 16 TW)
     static constexpr int MH = 4;                    // heads per workgroup at most (16 TW | P)
-    static constexpr int LDN = N + 4;               // padded LDS row of B / C
+    // Padded LDS rows of B and C.  Measured on gfx950 (SQ_LDS_BANK_CONFLICT of
+    // plain probes): float reads at rows 4 (l/16) + v, column l%16 are free of
+    // conflicts for a row stride of 4 mod 16 floats and 2-way at 8 mod 16; float4
+    // reads at row l%16, columns 4 (l/16) .. + 3 cost 4 conflict cycles for 4 mod
+    // 16 and none for 8 mod 16.  B is read mostly the first way (the state
+    // update's B^T), C only the second (C h^T, G^T), so each has its own stride.
+    static constexpr int LDN = N + 4;               // B rows
+    static constexpr int LDC = N + 8;               // C rows
     // x rows padded by 4 floats: a lane reads row 4 (l/16) + v, column l % 16
     // (+ a wave offset), so with RBW a multiple of the bank count the four
     // l/16 groups would share banks; 4 more floats per row put them 16 banks
     // apart (conflict-free for 32 and for 64 banks)
     static constexpr int XR = RBW + 4;
     static constexpr int OFF_C = 0;
-    static constexpr int OFF_B = OFF_C + CT * LDN;
+    static constexpr int OFF_B = OFF_C + CT * LDC;
     static constexpr int OFF_X = OFF_B + CT * LDN;  // x[CT][XR]
     static constexpr int OFF_S = OFF_X + CT * XR;   // [MH][CT] S_t
     static constexpr int OFF_DT = OFF_S + MH * CT;  // [MH][CT] dt_t (0 past the segment)
@@ -315,7 +322,7 @@ template <int NT, int TW>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 ssd_scan_kernel(ScanArgs a) {
     using S = SsdScanShape<NT, TW>;
-    constexpr int N = S::N, CT = S::CT, LDN = S::LDN;
+    constexpr int N = S::N, CT = S::CT, LDN = S::LDN, LDC = S::LDC;
     extern __shared__ float4 lds_raw[];
     float *const lds = reinterpret_cast<float *>(lds_raw);
 
@@ -441,8 +448,9 @@ ssd_scan_kernel(ScanArgs a) {
 #pragma unroll
         for (int u = 0; u < S::U_BC; ++u) {
             if (lo_bc[u] >= 0) {
+                const int tt = (u * kThreads + tid) / (N / 4);   // the unit's token
                 *reinterpret_cast<f4 *>(base + S::OFF_B + lo_bc[u]) = sg.pb[u];
-                *reinterpret_cast<f4 *>(base + S::OFF_C + lo_bc[u]) = sg.pc[u];
+                *reinterpret_cast<f4 *>(base + S::OFF_C + lo_bc[u] + tt * (LDC - LDN)) = sg.pc[u];
             }
         }
 #pragma unroll
@@ -528,9 +536,9 @@ ssd_scan_kernel(ScanArgs a) {
         if constexpr (NT % 4 == 0) {
 #pragma unroll
             for (int k = 0; k < NT / 4; ++k) {
-                const int off = tl * LDN + 16 * (w * (NT / 4) + k) + 4 * kq;
-                const f4 bq = *reinterpret_cast<const f4 *>(base + S::OFF_B + off);
-                const f4 cq = *reinterpret_cast<const f4 *>(base + S::OFF_C + off);
+                const int off = 16 * (w * (NT / 4) + k) + 4 * kq;
+                const f4 bq = *reinterpret_cast<const f4 *>(base + S::OFF_B + tl * LDN + off);
+                const f4 cq = *reinterpret_cast<const f4 *>(base + S::OFF_C + tl * LDC + off);
                 gb[4 * k + 0] = bq.x; gb[4 * k + 1] = bq.y; gb[4 * k + 2] = bq.z; gb[4 * k + 3] = bq.w;
                 gc[4 * k + 0] = cq.x; gc[4 * k + 1] = cq.y; gc[4 * k + 2] = cq.z; gc[4 * k + 3] = cq.w;
             }
@@ -538,9 +546,9 @@ ssd_scan_kernel(ScanArgs a) {
 #pragma unroll
             for (int i = 0; i < NT; ++i) {
                 const int f = w * NT + i;
-                const int off = tl * LDN + 16 * (f / 4) + 4 * kq + f % 4;
-                gb[i] = base[S::OFF_B + off];
-                gc[i] = base[S::OFF_C + off];
+                const int off = 16 * (f / 4) + 4 * kq + f % 4;
+                gb[i] = base[S::OFF_B + tl * LDN + off];
+                gc[i] = base[S::OFF_C + tl * LDC + off];
             }
         }
         float xr[TW][4];
@@ -557,7 +565,7 @@ ssd_scan_kernel(ScanArgs a) {
         f4 creg[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-            creg[nt] = *reinterpret_cast<const f4 *>(base + S::OFF_C + tl * LDN + 16 * nt + 4 * kq);
+            creg[nt] = *reinterpret_cast<const f4 *>(base + S::OFF_C + tl * LDC + 16 * nt + 4 * kq);
         const float pre = base[S::OFF_PRE + hw];
         const bool fast = base[S::OFF_MODE + hw] != 0.f;
         __builtin_amdgcn_sched_barrier(0);
