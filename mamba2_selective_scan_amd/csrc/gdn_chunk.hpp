@@ -78,7 +78,8 @@ gdn_chunk_prep_kernel(GdnChunkArgs c) {
     __shared__ float t_lds[kWaves][2][16 * 16];      // T00, T11
     __shared__ float g_lds[kWaves][64];              // G_t [32], beta_t [32]
     const GdnArgs &a = c.a;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int tl = lane & 15, kq = lane >> 4;
     const int64_t unit = int64_t(blockIdx.x) * kWaves + w;   // (s, chunk, kh), kh fastest
     const int64_t n_units = int64_t(a.n_blocks);
@@ -97,18 +98,35 @@ gdn_chunk_prep_kernel(GdnChunkArgs c) {
     // t tile, column l%16 of the s tile
     f4m kk00 = {0.f, 0.f, 0.f, 0.f}, kk10 = kk00, kk11 = kk00;
     f4m qk00 = kk00, qk10 = kk00, qk11 = kk00;
+    // g and beta of the first two value heads of this key head, loaded with K
+    // and Q so that every load of the wavefront is in flight at once
+    float gpre0 = 0.f, gpre1 = 0.f, bpre0 = 0.f, bpre1 = 0.f;
     if (live) {
         const int row_bytes = a.Hk * Dk * int(sizeof(float));
         const __amdgpu_buffer_rsrc_t rk = buffer_of(a.k + int64_t(t0) * a.Hk * Dk, n * row_bytes);
         const __amdgpu_buffer_rsrc_t rq = buffer_of(a.q + int64_t(t0) * a.Hk * Dk, n * row_bytes);
         const int vo = (tl * a.Hk * Dk + kh * Dk + 4 * kq) * int(sizeof(float));
+        // lane (l%16, l/16): row l%16 of each tile at columns 16 m + 4 (l/16) .. + 3
+        f4 kr[NKT][2], qr[NKT][2];
 #pragma unroll
         for (int m = 0; m < NKT; ++m) {
-            // lane (l%16, l/16): row l%16 of each tile at columns 16 m + 4 (l/16) .. + 3
-            const f4 k0 = buffer_load<4>(rk, vo + 64 * m, 0);
-            const f4 k1 = buffer_load<4>(rk, vo + 64 * m, 16 * row_bytes);
-            const f4 q0 = buffer_load<4>(rq, vo + 64 * m, 0);
-            const f4 q1 = buffer_load<4>(rq, vo + 64 * m, 16 * row_bytes);
+            kr[m][0] = buffer_load<4>(rk, vo + 64 * m, 0);
+            kr[m][1] = buffer_load<4>(rk, vo + 64 * m, 16 * row_bytes);
+            qr[m][0] = buffer_load<4>(rq, vo + 64 * m, 0);
+            qr[m][1] = buffer_load<4>(rq, vo + 64 * m, 16 * row_bytes);
+        }
+        if (lane < n) {
+            gpre0 = a.g[int64_t(t0 + lane) * a.Hv + kh];
+            bpre0 = a.beta[int64_t(t0 + lane) * a.Hv + kh];
+            if (a.heads_per_key > 1) {
+                gpre1 = a.g[int64_t(t0 + lane) * a.Hv + kh + a.Hk];
+                bpre1 = a.beta[int64_t(t0 + lane) * a.Hv + kh + a.Hk];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NKT; ++m) {
+            const f4 k0 = kr[m][0], k1 = kr[m][1], q0 = qr[m][0], q1 = qr[m][1];
             kk00 = mfma16(k0.x, k0.x, kk00); kk10 = mfma16(k1.x, k0.x, kk10); kk11 = mfma16(k1.x, k1.x, kk11);
             qk00 = mfma16(q0.x, k0.x, qk00); qk10 = mfma16(q1.x, k0.x, qk10); qk11 = mfma16(q1.x, k1.x, qk11);
             kk00 = mfma16(k0.y, k0.y, kk00); kk10 = mfma16(k1.y, k0.y, kk10); kk11 = mfma16(k1.y, k1.y, kk11);
@@ -124,8 +142,8 @@ gdn_chunk_prep_kernel(GdnChunkArgs c) {
         float *const u = c.ws + (live ? gdn_unit(c, s, chunk, vh) : 0);
         // per-token G_t (running log decay over the chunk) and beta_t in lanes 0..31
         const bool tok = live && lane < n;
-        const float gv = tok ? a.g[int64_t(t0 + lane) * a.Hv + vh] : 0.f;
-        const float bv = tok ? a.beta[int64_t(t0 + lane) * a.Hv + vh] : 0.f;
+        const float gv = r == 0 ? gpre0 : r == 1 ? gpre1 : tok ? a.g[int64_t(t0 + lane) * a.Hv + vh] : 0.f;
+        const float bv = r == 0 ? bpre0 : r == 1 ? bpre1 : tok ? a.beta[int64_t(t0 + lane) * a.Hv + vh] : 0.f;
         float Gv = row_prefix_sum(gv);
         const float G15 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Gv), 15));
         if (kq == 1) Gv += G15;
