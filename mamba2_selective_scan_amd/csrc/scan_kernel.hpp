@@ -45,6 +45,8 @@
 
 #include <type_traits>
 
+#include "buffer_io.hpp"
+
 namespace ssm {
 
 using f4 = float __attribute__((ext_vector_type(4)));
@@ -368,12 +370,22 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     static_assert(OPT == 0 || MODE == Mode::kPrefill || MODE == Mode::kDecode,
                   "options are built for whole-sequence prefill and decode only");
 
-    // ---- workgroup -> (sequence, segment, head, row block); XCD-contiguous order
+    // ---- workgroup -> (sequence, segment, head, row block).  XCD-contiguous
+    // order (consecutive ids dealt round-robin over the XCDs take consecutive
+    // runs of the grid, so the heads of a B/C group share an L2) -- except a
+    // whole-sequence prefill of several sequences, which takes the plain order:
+    // there a sequence's workgroups are spread over every XCD, so one long
+    // sequence of a ragged batch does not pile onto a few CUs while the others
+    // idle (measured on the mixed batch, 8 sequences of 1..150 tokens at H 16,
+    // P 96, N 100: 33.7 us XCD-contiguous, 25.2 us plain; a single 1 x 4096
+    // sequence keeps the L2 sharing, 455 against 462 us).
     const int bid = blockIdx.x;
     const int nb = a.n_blocks;
     const int per = nb / kXcds, rem = nb % kXcds;
     const int xcd = bid % kXcds, kx = bid / kXcds;
-    const int L = (xcd < rem) ? xcd * (per + 1) + kx : rem * (per + 1) + (xcd - rem) * per + kx;
+    const bool plain_order = MODE == Mode::kPrefill && nb > a.n_row_blocks * a.H;
+    const int L = plain_order ? bid
+                : (xcd < rem) ? xcd * (per + 1) + kx : rem * (per + 1) + (xcd - rem) * per + kx;
     const int rb = L % a.n_row_blocks;
     const int hd = (L / a.n_row_blocks) % a.H;
     const int seg = SEGMENTED ? (L / (a.n_row_blocks * a.H)) % a.n_segs : 0;
@@ -434,7 +446,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) h[e] = 0.f;
     // the state after token t, to the snapshot buffer
-    auto snapshot = [&](int t) {
+    auto snapshot = [&](int t) __attribute__((always_inline)) {
         float *dst = a.snapshots + (int64_t(t) * H + hd) * P * int64_t(N) + int64_t(p0 + i) * N;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
@@ -522,41 +534,89 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         // segment start through each token.  Time segments keep that running
         // product in wave 0 (`run`), chunk after chunk: a 16-lane DPP prefix
         // product per chunk (chunks of a segmented launch are <= 16 tokens).
-        f4 pb[S::U_BC], pc[S::U_BC], px[S::U_X];
-        float pdt = 0.f;
+        // Chunks are loaded PF ahead: chunk k lands in register set k % PF and
+        // is committed to LDS buffer k & 1 one step before it is computed.  On
+        // the vector path the loads go through buffer descriptors that cover
+        // the chunk's tokens only (none at all for a chunk past the end): every
+        // step issues the same loads with no branch, so the wait before a
+        // commit is for that chunk's loads alone, never the newer chunk's.
+        constexpr int PF = VEC ? 2 : 1;
+        constexpr int kNone = 0x7ffffff0;                   // a byte offset past every descriptor
+        struct Stage {
+            f4 pb[S::U_BC], pc[S::U_BC], px[S::U_X];
+            float pdt;
+        };
+        Stage stg[PF];
         const float *xsrc = CORRECT ? a.y : a.x;
-
-        auto issue_loads = [&](int t0, int nt) {
+        // the vector path's fixed byte offsets into a chunk
+        int vo_bc[VEC ? S::U_BC : 1], vo_x[VEC ? S::U_X : 1];
+        int vo_dt = kNone;
+        if constexpr (VEC) {
 #pragma unroll
             for (int u = 0; u < S::U_BC; ++u) {
-                const int q = u * kThreads + tid;                 // unit = (token, 4-group)
+                const int q = u * kThreads + tid;             // unit = (token, 4-group)
                 const int tt = q / (NP / 4);
                 const int n0 = 4 * (q - tt * (NP / 4));
-                const bool ok = (q < CT * NP / 4) && (tt < nt);
-                const int64_t off = (int64_t(t0 + tt) * G + g) * N + n0;
-                const int nv = ok ? clamp4(N - n0) : 0;
-                if constexpr (!CORRECT) pb[u] = load4<VEC>(a.B + off, nv);
-                pc[u] = load4<VEC>(a.C + off, nv);
+                vo_bc[u] = q < CT * NP / 4 && n0 < N ? ((tt * G + g) * N + n0) * int(sizeof(float)) : kNone;
             }
 #pragma unroll
             for (int u = 0; u < S::U_X; ++u) {
-                const int q = u * kThreads + tid;                 // unit = (token, 4 rows)
+                const int q = u * kThreads + tid;             // unit = (token, 4 rows)
                 const int tt = q / (RB / 4);
                 const int pi = 4 * (q - tt * (RB / 4));
-                const bool ok = (q < CT * RB / 4) && (tt < nt);
-                const int nv = ok ? clamp4(rows_valid - pi) : 0;
-                px[u] = load4<VEC>(xsrc + (int64_t(t0 + tt) * H + hd) * P + p0 + pi, nv);
+                vo_x[u] = q < CT * RB / 4 && pi < rows_valid ? ((tt * H + hd) * P + p0 + pi) * int(sizeof(float)) : kNone;
             }
-            // raw dt: its transform waits until the commit, so nothing here
-            // waits for a load to arrive
-            pdt = (tid < nt) ? a.dt[int64_t(t0 + tid) * H + hd] : 0.f;
+            vo_dt = tid < CT ? (tid * H + hd) * int(sizeof(float)) : kNone;
+        }
+
+        auto issue_loads = [&](Stage &sg, int t0, int nt) __attribute__((always_inline)) {
+            if constexpr (VEC) {
+                const int nb = nt;                          // 0 past the last chunk
+                const __amdgpu_buffer_rsrc_t rbd = buffer_of(a.B + int64_t(t0) * G * N, nb * G * N * int(sizeof(float)));
+                const __amdgpu_buffer_rsrc_t rcd = buffer_of(a.C + int64_t(t0) * G * N, nb * G * N * int(sizeof(float)));
+                const __amdgpu_buffer_rsrc_t rxd = buffer_of(xsrc + int64_t(t0) * H * P, nb * H * P * int(sizeof(float)));
+                const __amdgpu_buffer_rsrc_t rdd = buffer_of(a.dt + int64_t(t0) * H, nb * H * int(sizeof(float)));
+#pragma unroll
+                for (int u = 0; u < S::U_BC; ++u) {
+                    if constexpr (!CORRECT) sg.pb[u] = buffer_load<4>(rbd, vo_bc[u], 0);
+                    sg.pc[u] = buffer_load<4>(rcd, vo_bc[u], 0);
+                }
+#pragma unroll
+                for (int u = 0; u < S::U_X; ++u) sg.px[u] = buffer_load<4>(rxd, vo_x[u], 0);
+                // raw dt: its transform waits until the commit
+                sg.pdt = buffer_load<1>(rdd, vo_dt, 0);
+            } else {
+#pragma unroll
+                for (int u = 0; u < S::U_BC; ++u) {
+                    const int q = u * kThreads + tid;             // unit = (token, 4-group)
+                    const int tt = q / (NP / 4);
+                    const int n0 = 4 * (q - tt * (NP / 4));
+                    const bool ok = (q < CT * NP / 4) && (tt < nt);
+                    const int64_t off = (int64_t(t0 + tt) * G + g) * N + n0;
+                    const int nv = ok ? clamp4(N - n0) : 0;
+                    if constexpr (!CORRECT) sg.pb[u] = load4<VEC>(a.B + off, nv);
+                    sg.pc[u] = load4<VEC>(a.C + off, nv);
+                }
+#pragma unroll
+                for (int u = 0; u < S::U_X; ++u) {
+                    const int q = u * kThreads + tid;             // unit = (token, 4 rows)
+                    const int tt = q / (RB / 4);
+                    const int pi = 4 * (q - tt * (RB / 4));
+                    const bool ok = (q < CT * RB / 4) && (tt < nt);
+                    const int nv = ok ? clamp4(rows_valid - pi) : 0;
+                    sg.px[u] = load4<VEC>(xsrc + (int64_t(t0 + tt) * H + hd) * P + p0 + pi, nv);
+                }
+                // raw dt: its transform waits until the commit, so nothing here
+                // waits for a load to arrive
+                sg.pdt = (tid < nt) ? a.dt[int64_t(t0 + tid) * H + hd] : 0.f;
+            }
         };
 
         float run = 1.f;                                    // wave 0: dA product so far
-        auto commit = [&](int buf, int t0, int nt) {
+        auto commit = [&](int buf, const Stage &sg, int t0, int nt) __attribute__((always_inline)) {
             float *base = lds + buf * S::BUF;
             // the chunk's dt after bias and softplus (0 past its tokens)
-            auto dt_eff = [&] { return (tid < nt) ? dt_transform(pdt, bias_h, a.dt_softplus) : 0.f; };
+            auto dt_eff = [&] { return (tid < nt) ? dt_transform(sg.pdt, bias_h, a.dt_softplus) : 0.f; };
             f4 *Bs4 = reinterpret_cast<f4 *>(base + S::OFF_B);
             f4 *Cs4 = reinterpret_cast<f4 *>(base + S::OFF_C);
             f4 *Xs4 = reinterpret_cast<f4 *>(base + S::OFF_X);
@@ -564,14 +624,14 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
             for (int u = 0; u < S::U_BC; ++u) {
                 const int q = u * kThreads + tid;
                 if (q < CT * NP / 4) {
-                    if constexpr (!CORRECT) Bs4[q] = pb[u];
-                    Cs4[q] = pc[u];
+                    if constexpr (!CORRECT) Bs4[q] = sg.pb[u];
+                    Cs4[q] = sg.pc[u];
                 }
             }
 #pragma unroll
             for (int u = 0; u < S::U_X; ++u) {
                 const int q = u * kThreads + tid;
-                if (q < CT * RB / 4) Xs4[q] = px[u];
+                if (q < CT * RB / 4) Xs4[q] = sg.px[u];
             }
             if constexpr (SEGMENTED || LAZY) {
                 if (tid < 64) {                              // wave 0, all lanes active
@@ -634,34 +694,50 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         int chunk_t0 = 0;                                   // first token of the chunk in compute
         // The lane's partial of token tt's y (prefill / segment scan): the row
         // sum of these, times y_scale(tt), is y.
-        auto token_part = [&](const float *base, int tt, auto lazy_tag) -> float {
-            f4 cv[J], bv[J];
-            lds_groups<R, J>(cv, base + S::OFF_C + 4 * r + tt * NP);
-            lds_groups<R, J>(bv, base + S::OFF_B + 4 * r + tt * NP);
+        // One token's operands out of LDS: the lane's B and C groups, its row's
+        // x and the token's dt and dA (deferred form: dt / sigma and sigma).
+        struct TokIn {
+            f4 b[J], c[J];
+            float x, dt, dA;
+        };
+        auto token_load = [&](const float *base, int tt) __attribute__((always_inline)) {
+            TokIn in;
+            lds_groups<R, J>(in.c, base + S::OFF_C + 4 * r + tt * NP);
+            lds_groups<R, J>(in.b, base + S::OFF_B + 4 * r + tt * NP);
+            in.x = base[S::OFF_X + tt * RB + i];
+            in.dt = base[S::OFF_DT + tt];
+            in.dA = base[S::OFF_DA + tt];
+            return in;
+        };
+        // The lane's partial of token tt's y (prefill / segment scan) from its
+        // operands: the row sum of these, times y_scale(tt), is y.
+        auto token_part_in = [&](TokIn &in, int tt, auto lazy_tag) -> float __attribute__((always_inline)) {
             if constexpr (decltype(lazy_tag)::value) {
-                const float xs = base[S::OFF_X + tt * RB + i] * base[S::OFF_DT + tt];
-                return update_token_lazy<J>(h, bv, cv, xs);
+                return update_token_lazy<J>(h, in.b, in.c, in.x * in.dt);
             } else {
-                const float dt = base[S::OFF_DT + tt];
-                const float x_dt = base[S::OFF_X + tt * RB + i] * dt;
+                const float x_dt = in.x * in.dt;
                 float part;
                 if constexpr (A_PER_STATE) {
                     float dAe[E];
 #pragma unroll
-                    for (int e = 0; e < E; ++e) dAe[e] = __expf(dt * Ae[e]);
-                    part = update_token_pe<J>(h, bv, cv, dAe, x_dt);
+                    for (int e = 0; e < E; ++e) dAe[e] = __expf(in.dt * Ae[e]);
+                    part = update_token_pe<J>(h, in.b, in.c, dAe, x_dt);
                 } else {
-                    part = update_token<J>(h, bv, cv, base[S::OFF_DA + tt], x_dt);
+                    part = update_token<J>(h, in.b, in.c, in.dA, x_dt);
                 }
                 if constexpr (SNAPSHOTS) snapshot(chunk_t0 + tt);
                 return part;
             }
         };
-        auto y_scale = [&](const float *base, int tt, auto lazy_tag) -> float {
+        auto token_part = [&](const float *base, int tt, auto lazy_tag) -> float __attribute__((always_inline)) {
+            TokIn in = token_load(base, tt);
+            return token_part_in(in, tt, lazy_tag);
+        };
+        auto y_scale = [&](const float *base, int tt, auto lazy_tag) -> float __attribute__((always_inline)) {
             if constexpr (decltype(lazy_tag)::value) return base[S::OFF_DA + tt];
             else return 1.f;
         };
-        auto token_y = [&](const float *base, int tt, auto lazy_tag) -> float {
+        auto token_y = [&](const float *base, int tt, auto lazy_tag) -> float __attribute__((always_inline)) {
             if constexpr (CORRECT) {
                 // y += dcum[t] * (C_t . carry): the carry decayed to token t
                 f4 cv[J];
@@ -681,7 +757,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
             }
         };
         // tokens tb .. tb + nt - 1 of the staged chunk
-        auto run_tokens = [&](const float *base, float *Ys, int tb, int nt, auto lazy_tag) {
+        auto run_tokens = [&](const float *base, float *Ys, int tb, int nt, auto lazy_tag) __attribute__((always_inline)) {
             int t0 = tb;
             nt += tb;
             float y_keep = 0.f;
@@ -690,10 +766,18 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                 // row, so lane r ends with token r % KY's y and stores it.
                 // (Snapshot kernels keep the per-token sums: holding KY partials
                 // beside the snapshot stores costs them occupancy.)
+                // Software-pipelined: token kk + 1's operands are read out of
+                // LDS before token kk's arithmetic, so their latency is under it.
                 for (; t0 + KY <= nt; t0 += KY) {
                     float part[KY];
+                    TokIn in[2];
+                    in[0] = token_load(base, t0);
 #pragma unroll
-                    for (int kk = 0; kk < KY; ++kk) part[kk] = token_part(base, t0 + kk, lazy_tag);
+                    for (int kk = 0; kk < KY; ++kk) {
+                        if (kk + 1 < KY) in[(kk + 1) & 1] = token_load(base, t0 + kk + 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        part[kk] = token_part_in(in[kk & 1], t0 + kk, lazy_tag);
+                    }
                     float yv = row_reduce_scatter<KY>(part);
                     if constexpr (R >= 32) yv += __shfl_xor(yv, 16, 64);
                     if constexpr (R >= 64) yv += __shfl_xor(yv, 32, 64);
@@ -717,7 +801,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                 if (rk < nt - t0) Ys[(t0 + rk) * S::YR] = y_keep;
             }
         };
-        auto compute = [&](int buf, int nt) {
+        auto compute = [&](int buf, int nt) __attribute__((always_inline)) {
             const float *base = lds + buf * S::BUF;
             float *Ys = lds + buf * S::BUF + S::OFF_Y + i;
             if constexpr (LAZY) {
@@ -741,7 +825,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
             }
         };
 
-        auto flush_y = [&](int buf, int t0, int nt) {
+        auto flush_y = [&](int buf, int t0, int nt) __attribute__((always_inline)) {
             const float *Ys = lds + buf * S::BUF + S::OFF_Y;
             if constexpr (VEC) {
                 constexpr int YV = S::YV;
@@ -768,22 +852,53 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         // the registers that carried them are free again by the time they are
         // reused (vector-memory counters on this chip count stores too).
         const int n_chunks = (n_tok + CT - 1) / CT;
+        // chunk k's loads (none past the last chunk)
+        auto issue_chunk = [&](Stage &sg, int k) __attribute__((always_inline)) {
+            const int t0 = t_begin + k * CT;
+            issue_loads(sg, k < n_chunks ? t0 : t_begin, k < n_chunks ? min(CT, t_end - t0) : 0);
+        };
+        // vector-memory instructions of one issue_loads (vector path)
+        constexpr int kLoadsPerChunk = (CORRECT ? 1 : 2) * S::U_BC + S::U_X + 1;
         if (n_chunks > 0) {
-            issue_loads(t_begin, min(CT, n_tok));
-            commit(0, t_begin, min(CT, n_tok));
+            // chunk 0's loads all before chunk 1's, so its commit waits for them alone
+#pragma unroll
+            for (int k = 0; k < PF; ++k) {
+                issue_chunk(stg[k], k);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            commit(0, stg[0], t_begin, min(CT, n_tok));
+            if constexpr (PF > 1) {
+                // chunk 0 is in LDS on every path through the commit: only
+                // chunk 1's loads may still be in flight at the loop head
+                constexpr int n = kLoadsPerChunk;
+                static_assert(n < 64, "vmcnt field");
+                __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+            }
         }
         __syncthreads();
-        for (int c = 0; c < n_chunks; ++c) {
+        // chunk c: the loads of chunk c + PF into the register set chunk c
+        // left, the previous chunk's y out, chunk c's tokens, then chunk c + 1
+        // to LDS
+        auto step = [&](int c, auto setc) __attribute__((always_inline)) {
+            constexpr int st = decltype(setc)::value;
             const int buf = c & 1;
             const int t0 = t_begin + c * CT;
             const int nt = min(CT, t_end - t0);
-            const bool has_next = c + 1 < n_chunks;
-            if (has_next) issue_loads(t0 + CT, min(CT, t_end - t0 - CT));
+            issue_chunk(stg[st], c + PF);
             if (c > 0) flush_y(buf ^ 1, t0 - CT, CT);    // previous chunk, always full
             chunk_t0 = t0;
             compute(buf, nt);
-            if (has_next) commit(buf ^ 1, t0 + CT, min(CT, t_end - t0 - CT));
+            if (c + 1 < n_chunks) commit(buf ^ 1, stg[(st + 1) % PF], t0 + CT, min(CT, t_end - t0 - CT));
             __syncthreads();
+        };
+        // (a pair cut short leaves the loop at once, so the loop head's wait
+        // counts only the loads of a whole pair)
+        for (int c = 0; c < n_chunks; c += PF) {
+            step(c, std::integral_constant<int, 0>{});
+            if constexpr (PF > 1) {
+                if (c + 1 >= n_chunks) break;
+                step(c + 1, std::integral_constant<int, 1>{});
+            }
         }
         if (n_chunks > 0) {
             const int c = n_chunks - 1;

@@ -166,6 +166,7 @@ ssd_state_kernel(ScanArgs a) {
     const int s = L / (NS * a.n_row_blocks * a.H * segs);
 
     const int H = a.H, P = a.P, G = a.G;
+    const int Nr = a.N;                              // state columns in memory (N rounds it up)
     const int g = hd / a.heads_per_group;
     const SegRange sr = segment_range(a, s, seg);
     if (seg >= sr.n_real - 1) return;                // the last segment needs no pass
@@ -178,7 +179,7 @@ ssd_state_kernel(ScanArgs a) {
     const int p0 = rbw * 64 + 32 * (w & 1);          // the wave's two row tiles: p0, p0 + 16
     const bool tile_ok[2] = {p0 < P, p0 + 16 < P};   // P % 16 == 0: whole tiles
     const int n_base = (2 * part + (w >> 1)) * NW;
-    const int64_t hpn = int64_t(H) * P * N;
+    const int64_t hpn = int64_t(H) * P * Nr;
     const float A_h = a.A[hd];
     const float bias_h = a.dt_bias ? a.dt_bias[hd] : 0.f;
 
@@ -188,7 +189,11 @@ ssd_state_kernel(ScanArgs a) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < E; ++e) hacc[t][e] = f4m{0.f, 0.f, 0.f, 0.f};
-    const int64_t head_off = int64_t(hd) * P * N;
+    // columns at Nr and past (N > Nr: padding to whole 16-column tiles) hold
+    // zeros: their B reads as zero and they are neither loaded nor stored.
+    // Nr % 4 == 0 and E <= 4 or Nr % 8 == 0, so a lane's E columns are all in
+    // or all out.
+    const int64_t head_off = int64_t(hd) * P * Nr;
     if (from_slot) {
         const float *src = a.state + int64_t(a.slot[s]) * hpn + head_off + n_base;
 #pragma unroll
@@ -196,7 +201,8 @@ ssd_state_kernel(ScanArgs a) {
             if (!tile_ok[t]) continue;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const fE h = *reinterpret_cast<const fE *>(src + int64_t(p0 + 16 * t + tl) * N + E * (4 * kq + v));
+                if (n_base + E * (4 * kq + v) >= Nr) continue;
+                const fE h = *reinterpret_cast<const fE *>(src + int64_t(p0 + 16 * t + tl) * Nr + E * (4 * kq + v));
 #pragma unroll
                 for (int e = 0; e < E; ++e) hacc[t][e][v] = vget<E>(h, e);
             }
@@ -209,9 +215,10 @@ ssd_state_kernel(ScanArgs a) {
     // past P reads rows of the next head or zeros: it is never stored.)
     float xg[2][KS][2];
     fE bg[2][KS];
-    const int x_tok = H * P * int(sizeof(float)), b_tok = G * N * int(sizeof(float));
+    constexpr int kNone = 0x7ffffff0;                // a byte offset past every descriptor
+    const int x_tok = H * P * int(sizeof(float)), b_tok = G * Nr * int(sizeof(float));
     const int vo_x = (kq * H * P + hd * P + p0 + tl) * int(sizeof(float));
-    const int vo_b = (kq * G * N + g * N + n_base + E * tl) * int(sizeof(float));
+    const int vo_b = n_base + E * tl < Nr ? (kq * G * Nr + g * Nr + n_base + E * tl) * int(sizeof(float)) : kNone;
     __amdgpu_buffer_rsrc_t rx, rb;
     auto load_group = [&](int r, int j0) {           // j0: first token of the group in the window
 #pragma unroll
@@ -238,7 +245,7 @@ ssd_state_kernel(ScanArgs a) {
     for (int tw = t_begin; tw < t_end; tw += kSsdWindow) {
         const int m = min(kSsdWindow, t_end - tw);
         rx = buffer_of(a.x + int64_t(tw) * H * P, m * x_tok);
-        rb = buffer_of(a.B + int64_t(tw) * G * N, m * b_tok);
+        rb = buffer_of(a.B + int64_t(tw) * G * Nr, m * b_tok);
         if (tile_ok[0]) load_group(0, 0);              // first operands in flight during the prologue
         // ---- prologue: w_t = e^{S_last - S_t} dt_t for the window's tokens.  The
         // exponent is summed from the window end backwards (thread 0 takes the
@@ -297,12 +304,13 @@ ssd_state_kernel(ScanArgs a) {
         if (!tile_ok[t]) continue;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
+            if (n_base + E * (4 * kq + v) >= Nr) continue;
             fE h;
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 if constexpr (E == 1) h = hacc[t][e][v]; else h[e] = hacc[t][e][v];
             }
-            *reinterpret_cast<fE *>(dst + int64_t(p0 + 16 * t + tl) * N + E * (4 * kq + v)) = h;
+            *reinterpret_cast<fE *>(dst + int64_t(p0 + 16 * t + tl) * Nr + E * (4 * kq + v)) = h;
         }
     }
 }
@@ -338,6 +346,7 @@ ssd_scan_kernel(ScanArgs a) {
     const int s = L / (wpg * a.G * a.n_segs);
 
     const int H = a.H, P = a.P, G = a.G;
+    const int Nr = a.N;                              // state columns in memory (N rounds it up)
     const SegRange sr = segment_range(a, s, seg);
     const int last = sr.n_real - 1;
     if (seg > last) return;                          // past the sequence's segments
@@ -358,16 +367,17 @@ ssd_scan_kernel(ScanArgs a) {
     const int fr0 = fr_wg + 16 * TW * w;             // first row of this wave
     const bool wave_ok = fr0 < fr_wg + rows_wg;      // whole waves: P % (16 TW) == 0
     const int hw = wave_ok ? fr0 / P - h_wg : 0;     // this wave's head, relative to h_wg
-    const int64_t HPN = int64_t(H) * P * N;
-    float *const st_w = a.state + int64_t(a.slot[s]) * HPN + int64_t(fr0) * N;
-    float *const ws_w = a.ws_state + int64_t(s) * a.n_segs * HPN + int64_t(fr0) * N;
+    const int64_t HPN = int64_t(H) * P * Nr;
+    float *const st_w = a.state + int64_t(a.slot[s]) * HPN + int64_t(fr0) * Nr;
+    float *const ws_w = a.ws_state + int64_t(s) * a.n_segs * HPN + int64_t(fr0) * Nr;
     // wave 0, DPP row j = lane / 16: the scalars of head h_wg + j
     const bool hrow_ok = kq < n_heads_wg;
     const float A_j = (tid < 64 && hrow_ok) ? a.A[h_wg + kq] : 0.f;
     const float bias_j = (tid < 64 && hrow_ok && a.dt_bias) ? a.dt_bias[h_wg + kq] : 0.f;
 
     // ---- state h^T in accumulators: hacc[i][nt] register v of lane l holds
-    // h[row fr0 + 16 i + l%16][16 nt + 4 (l/16) + v]
+    // h[row fr0 + 16 i + l%16][16 nt + 4 (l/16) + v]; columns at Nr and past
+    // (padding to whole tiles, Nr % 4 == 0) stay zero and are never stored
     f4m hacc[TW][NT];
 #pragma unroll
     for (int i = 0; i < TW; ++i)
@@ -379,8 +389,9 @@ ssd_scan_kernel(ScanArgs a) {
         for (int i = 0; i < TW; ++i)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
+                if (16 * nt + 4 * kq >= Nr) continue;
                 const f4 v = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(
-                    src + int64_t(16 * i + tl) * N + 16 * nt + 4 * kq));
+                    src + int64_t(16 * i + tl) * Nr + 16 * nt + 4 * kq));
                 hacc[i][nt] = f4m{v.x, v.y, v.z, v.w};
             }
     }
@@ -388,7 +399,8 @@ ssd_scan_kernel(ScanArgs a) {
 
     // ---- chunk staging: buffer loads -> registers -> LDS (double-buffered).
     // Each thread's byte offsets into a chunk are fixed; a chunk's descriptors
-    // cover its tokens only, so the units past the segment end read zeros.
+    // cover its tokens only, so the units past the segment end read zeros, and
+    // so do the padding columns of B and C (Nr and past).
     // Loads run PF chunks ahead (chunk k lands in register set k % PF: two with
     // one tile per wave; with two tiles, two waves per SIMD leave room for one)
     // and chunk k is committed to LDS buffer k & 1.
@@ -399,7 +411,7 @@ ssd_scan_kernel(ScanArgs a) {
     for (int u = 0; u < S::U_BC; ++u) {
         const int q = u * kThreads + tid;            // unit = (token, 4-group)
         const int tt = q / (N / 4), n0 = 4 * (q - tt * (N / 4));
-        vo_bc[u] = q < CT * N / 4 ? ((tt * G + g) * N + n0) * int(sizeof(float)) : kNone;
+        vo_bc[u] = q < CT * N / 4 && n0 < Nr ? ((tt * G + g) * Nr + n0) * int(sizeof(float)) : kNone;
         lo_bc[u] = q < CT * N / 4 ? tt * LDN + n0 : -1;
     }
 #pragma unroll
@@ -417,8 +429,8 @@ ssd_scan_kernel(ScanArgs a) {
     };
     Stage stg[S::PF];
     auto issue_loads = [&](Stage &sg, int t0, int nt_) {
-        const __amdgpu_buffer_rsrc_t rb = buffer_of(a.B + int64_t(t0) * G * N, nt_ * G * N * int(sizeof(float)));
-        const __amdgpu_buffer_rsrc_t rc = buffer_of(a.C + int64_t(t0) * G * N, nt_ * G * N * int(sizeof(float)));
+        const __amdgpu_buffer_rsrc_t rb = buffer_of(a.B + int64_t(t0) * G * Nr, nt_ * G * Nr * int(sizeof(float)));
+        const __amdgpu_buffer_rsrc_t rc = buffer_of(a.C + int64_t(t0) * G * Nr, nt_ * G * Nr * int(sizeof(float)));
         const __amdgpu_buffer_rsrc_t rx = buffer_of(a.x + int64_t(t0) * H * P, nt_ * x_tok);
         const __amdgpu_buffer_rsrc_t rd = buffer_of(a.dt + int64_t(t0) * H, nt_ * H * int(sizeof(float)));
 #pragma unroll
@@ -532,24 +544,21 @@ ssd_scan_kernel(ScanArgs a) {
         const float *base = lds + buf * S::BUF;
         // this wave's quarter of G^T = B C^T (steps f = 4 tile + j, n = 16 tile + 4 (l/16) + j)
         f4m gpart = {0.f, 0.f, 0.f, 0.f};
-        float gb[NT], gc[NT];
-        if constexpr (NT % 4 == 0) {
+        // wave w takes state tiles w, w + 4, ...: one float4 of B and of C per
+        // tile (steps f = 4 tile + j, n = 16 tile + 4 (l/16) + j)
+        constexpr int GT = (NT + kWaves - 1) / kWaves;
+        float gb[4 * GT], gc[4 * GT];
 #pragma unroll
-            for (int k = 0; k < NT / 4; ++k) {
-                const int off = 16 * (w * (NT / 4) + k) + 4 * kq;
-                const f4 bq = *reinterpret_cast<const f4 *>(base + S::OFF_B + tl * LDN + off);
-                const f4 cq = *reinterpret_cast<const f4 *>(base + S::OFF_C + tl * LDC + off);
-                gb[4 * k + 0] = bq.x; gb[4 * k + 1] = bq.y; gb[4 * k + 2] = bq.z; gb[4 * k + 3] = bq.w;
-                gc[4 * k + 0] = cq.x; gc[4 * k + 1] = cq.y; gc[4 * k + 2] = cq.z; gc[4 * k + 3] = cq.w;
+        for (int k = 0; k < GT; ++k) {
+            const int nt = w + kWaves * k;
+            const int off = 16 * nt + 4 * kq;
+            f4 bq = {0.f, 0.f, 0.f, 0.f}, cq = {0.f, 0.f, 0.f, 0.f};
+            if (NT % kWaves == 0 || nt < NT) {
+                bq = *reinterpret_cast<const f4 *>(base + S::OFF_B + tl * LDN + off);
+                cq = *reinterpret_cast<const f4 *>(base + S::OFF_C + tl * LDC + off);
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < NT; ++i) {
-                const int f = w * NT + i;
-                const int off = 16 * (f / 4) + 4 * kq + f % 4;
-                gb[i] = base[S::OFF_B + tl * LDN + off];
-                gc[i] = base[S::OFF_C + tl * LDC + off];
-            }
+            gb[4 * k + 0] = bq.x; gb[4 * k + 1] = bq.y; gb[4 * k + 2] = bq.z; gb[4 * k + 3] = bq.w;
+            gc[4 * k + 0] = cq.x; gc[4 * k + 1] = cq.y; gc[4 * k + 2] = cq.z; gc[4 * k + 3] = cq.w;
         }
         float xr[TW][4];
 #pragma unroll
@@ -570,7 +579,7 @@ ssd_scan_kernel(ScanArgs a) {
         const bool fast = base[S::OFF_MODE + hw] != 0.f;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < NT; ++i) gpart = mfma16(gb[i], gc[i], gpart);
+        for (int i = 0; i < 4 * GT; ++i) gpart = mfma16(gb[i], gc[i], gpart);
         reinterpret_cast<f4m *>(lds + S::OFF_GX + buf * S::GX)[w * 64 + lane] = gpart;
         __builtin_amdgcn_sched_barrier(0);
         if (!wave_ok) return;                        // past the group: staging and G^T only
@@ -680,9 +689,10 @@ ssd_scan_kernel(ScanArgs a) {
         for (int i = 0; i < TW; ++i)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
+                if (16 * nt + 4 * kq < Nr)
                 __builtin_nontemporal_store(
                     f4{hacc[i][nt][0] * sg, hacc[i][nt][1] * sg, hacc[i][nt][2] * sg, hacc[i][nt][3] * sg},
-                    reinterpret_cast<f4 *>(st_w + int64_t(16 * i + tl) * N + 16 * nt + 4 * kq));
+                    reinterpret_cast<f4 *>(st_w + int64_t(16 * i + tl) * Nr + 16 * nt + 4 * kq));
     }
 }
 

@@ -243,6 +243,16 @@ Geo geo_for(const ShapeRow &row, Kind kind) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// The vector (float4) path: whole float4 groups of a state row and of a row
+// block, and one chunk's B, C, x and dt within the 32-bit byte range of the
+// buffer descriptors that stage them (chunks of at most 32 tokens).
+bool vec_dims(const ssm_scan_dims *d) {
+    constexpr int64_t kChunkBytes = 32 * int64_t(sizeof(float));
+    return d->d_state % 4 == 0 && d->head_dim % 4 == 0 &&
+           int64_t(d->n_heads) * d->head_dim * kChunkBytes < INT32_MAX &&
+           int64_t(d->n_groups) * d->d_state * kChunkBytes < INT32_MAX;
+}
+
 int check_dims(const ssm_scan_dims *d) {
     if (!d) return SSM_ERR_NULL;
     if (d->n_heads <= 0 || d->head_dim <= 0 || d->d_state <= 0 || d->n_groups <= 0)
@@ -289,16 +299,24 @@ struct SegPlan {
 constexpr int64_t kTargetWaves = 4096;
 constexpr int64_t kSsdTargetWaves = 2048;  // matrix-core segment scans
 constexpr int kMinSegTokens = 256;
+// the matrix-core split costs three launches and a state pass per segment: on
+// the headline geometry one pass still wins below about 256 tokens (1 x 200:
+// 27.5 us in one pass, 36-47 us split) and 128-token segments win above it
+// (1 x 512: 53 us in 4 segments against 62 in one pass)
+constexpr int kSsdMinSegTokens = 128;
 constexpr int kSsdStateGroup = 16;         // tokens per operand group of the state pass (4 waves/SIMD)
 constexpr int kSsdStateSplit128 = 1;       // N = 128: workgroups per state-column range
 
-// The chunked matrix-core segment scan covers N in {32, 64, 128} with whole
-// 16-row tiles, on the vector path (16-byte aligned arrays).
+// The chunked matrix-core segment scan covers N <= 128 with whole 16-row
+// tiles, on the vector path (16-byte aligned arrays, N % 4 == 0).  The state
+// columns are padded with zeros to whole 16-column tiles inside the kernels
+// (N = 100 runs as 7 tiles in the scan pass, 8 in the state pass); memory
+// holds only the N real ones.
 bool ssd_shape(const ssm_scan_dims *d) {
     const int N = d->d_state;
     // a window of tokens' x and B must fit 32-bit buffer offsets
     const int64_t span = int64_t(ssm::kSsdWindow + 64) * int64_t(sizeof(float));
-    return (N == 32 || N == 64 || N == 128) && d->head_dim % 16 == 0 &&
+    return N % 4 == 0 && N <= 128 && d->head_dim % 16 == 0 &&
            int64_t(d->n_heads) * d->head_dim * span < INT32_MAX &&
            int64_t(d->n_groups) * N * span < INT32_MAX;
 }
@@ -318,17 +336,24 @@ void ssd_scan_pick(const void **kern, int *lds) {
     *kern = reinterpret_cast<const void *>(&ssm::ssd_scan_kernel<NT, TW>);
     *lds = ssm::SsdScanShape<NT, TW>::lds_floats();
 }
-void ssd_scan_for(const ssm_scan_dims *d, const void **kern, int *lds) {
-    const int nt = d->d_state / 16;
-    if (ssd_tiles(d) == 2) {
-        if (nt == 2) ssd_scan_pick<2, 2>(kern, lds);
-        else if (nt == 4) ssd_scan_pick<4, 2>(kern, lds);
-        else ssd_scan_pick<8, 2>(kern, lds);
-    } else {
-        if (nt == 2) ssd_scan_pick<2, 1>(kern, lds);
-        else if (nt == 4) ssd_scan_pick<4, 1>(kern, lds);
-        else ssd_scan_pick<8, 1>(kern, lds);
+// 16-column state tiles of the scan pass (N rounded up).
+int ssd_scan_tiles(const ssm_scan_dims *d) { return (d->d_state + 15) / 16; }
+template <int TW>
+void ssd_scan_tw(int nt, const void **kern, int *lds) {
+    switch (nt) {
+    case 1: ssd_scan_pick<1, TW>(kern, lds); break;
+    case 2: ssd_scan_pick<2, TW>(kern, lds); break;
+    case 3: ssd_scan_pick<3, TW>(kern, lds); break;
+    case 4: ssd_scan_pick<4, TW>(kern, lds); break;
+    case 5: ssd_scan_pick<5, TW>(kern, lds); break;
+    case 6: ssd_scan_pick<6, TW>(kern, lds); break;
+    case 7: ssd_scan_pick<7, TW>(kern, lds); break;
+    default: ssd_scan_pick<8, TW>(kern, lds); break;
     }
+}
+void ssd_scan_for(const ssm_scan_dims *d, const void **kern, int *lds) {
+    if (ssd_tiles(d) == 2) ssd_scan_tw<2>(ssd_scan_tiles(d), kern, lds);
+    else ssd_scan_tw<1>(ssd_scan_tiles(d), kern, lds);
 }
 
 SegPlan plan_segments(const ssm_scan_dims *d, const ShapeRow &row, int32_t n_seqs,
@@ -346,7 +371,7 @@ SegPlan plan_segments(const ssm_scan_dims *d, const ShapeRow &row, int32_t n_seq
         const int64_t waves = int64_t(n_seqs) * ssm::kWaves * d->n_groups * ssd_windows(d);
         if (waves >= kSsdTargetWaves) return SegPlan{1, 0};
         K = (kSsdTargetWaves + waves - 1) / waves;
-        K = std::min<int64_t>(K, max_seqlen / kMinSegTokens);
+        K = std::min<int64_t>(K, max_seqlen / kSsdMinSegTokens);
     } else {
         const int RB = ssm::kWaves * (64 / row.R);
         const int64_t waves = int64_t(n_seqs) * d->n_heads * ((d->head_dim + RB - 1) / RB) * ssm::kWaves;
@@ -405,7 +430,7 @@ int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_
     if (n_blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
 
     const void *fptrs[] = {x, dt, A, B, C, state, y, opts->dt_bias, opts->snapshots};
-    bool vec = (d->d_state % 4 == 0) && (d->head_dim % 4 == 0);
+    bool vec = vec_dims(d);
     for (const void *p : fptrs) {
         if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
         if (p && !aligned(p, 16)) vec = false;
@@ -466,7 +491,8 @@ int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_
         sa.n_row_blocks = (d->head_dim + 63) / 64;
         const int64_t per_seg = int64_t(n_seqs) * d->n_heads * sa.n_row_blocks;
         if (per_seg * plan.n_segs > INT32_MAX) return SSM_ERR_UNSUPPORTED;
-        const int nt = d->d_state / 16;
+        // state-pass column tiles: N rounded up to 32, 64 or 128
+        const int nt = d->d_state <= 32 ? 2 : d->d_state <= 64 ? 4 : 8;
         auto pass = [&](bool states) -> int {
             const void *kern;
             int lds;
@@ -736,7 +762,7 @@ int ssm_scan_query_geometry(const ssm_scan_dims *dims, int32_t n_seqs, int32_t d
     if (n_seqs < 0) return SSM_ERR_DIMS;
     const ShapeRow *row = shape_for(dims->d_state);
     if (!row) return SSM_ERR_UNSUPPORTED;
-    const bool vec = aligned16 && dims->d_state % 4 == 0 && dims->head_dim % 4 == 0;
+    const bool vec = aligned16 && vec_dims(dims);
     Kind kind = decode ? Kind::kDecode : Kind::kPrefill;
     if (!decode) {
         const int64_t rb = geo_for(*row, kind).RB;
@@ -770,7 +796,7 @@ int ssm_scan_query_prefill_plan(const ssm_scan_dims *dims, int32_t n_seqs, int32
             // the row, l / 16 the quarter of each 16-wide state tile), 16-token
             // chunks
             out->lanes_per_row = 4;
-            out->elems_per_lane = dims->d_state / 4;
+            out->elems_per_lane = 4 * ssd_scan_tiles(dims);
             out->chunk_tokens = 16;
             // the scan pass: a window of 64 rows per tile per wave
             const void *kern;

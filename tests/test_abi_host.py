@@ -145,13 +145,14 @@ def test_no_kernel_uses_scratch():
     scratch = [int(v) for v in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
     # 7 state-size classes x (vector, scalar) x (4 option sets x (prefill, decode)
     # + segment scan + correction) + 2 combine kernels + 6 matrix-core corrections
-    # (3 contraction lengths, masked or not) + 3 x 3 matrix-core segment kernels
-    # (N 32, 64, 128; the state pass and the scan pass with one or two tiles per wave)
+    # (3 contraction lengths, masked or not) + matrix-core segment kernels: the
+    # state pass at 32, 64 or 128 columns and the scan pass at 1..8 16-column
+    # tiles with one or two row tiles per wave
     # + 7 branch-free decode kernels (one per state-size class, vector path)
     # + 7 x 2 whole-sequence prefills at half the chunk (vector, scalar);
     # conv1d + SiLU: (vector, scalar) x (4 history lengths x (decode, prefill)
     # + 3 with snapshots); gated RMSNorm: (vector, scalar) x 6 row-length classes
-    n_scan = 7 * 2 * (4 * 2 + 2) + 2 + 6 + 3 * 3 + 7 + 7 * 2
+    n_scan = 7 * 2 * (4 * 2 + 2) + 2 + 6 + 3 + 8 * 2 + 7 + 7 * 2
     n_conv = 2 * (4 * 2 + 3)
     n_norm = 2 * 6
     # gated delta rule: 5 key-width classes x (vector, scalar) x (prefill, decode)
@@ -237,11 +238,21 @@ def test_prefill_plan_and_workspace():
     ws = m.workspace_size(64, 64, 128, 8, 1, 4096, 4096)
     # + per-segment decay totals [1][16][64] and alignment
     assert 16 * 64 * 64 * 128 * 4 + 4096 * 64 * 4 <= ws <= 16 * 64 * 64 * 128 * 4 + 4096 * 64 * 4 + 16 * 64 * 4 + 512
-    g = m.prefill_plan(64, 64, 100, 8, 1, 4096)                       # register segment scan
+    g = m.prefill_plan(64, 64, 100, 8, 1, 4096)           # N 100: the matrix-core scan, 7 padded tiles
+    assert g["segments"] == 16 and g["segment_tokens"] == 256 and g["blocks"] == 16 * 32
+    assert g["elems_per_lane"] == 28 and g["rows_per_block"] == 128
+    # the mixed edge batch (longest 150) is too short to split: one pass; forced,
+    # the matrix-core split takes it in padded 16-column tiles
+    assert m.prefill_plan(16, 96, 100, 4, 8, 150)["segments"] == 1
+    g = m.prefill_plan(16, 96, 100, 4, 8, 150, segments=4)
+    assert g["segments"] == 4 and g["segment_tokens"] == 48 and g["blocks"] == 4 * 8 * 4 * 3
+    g = m.prefill_plan(64, 64, 256, 8, 1, 4096)                       # register segment scan
     assert g["segments"] == 4 and g["segment_tokens"] == 1024 and g["blocks"] == 4 * 256
     assert m.prefill_plan(64, 64, 128, 8, 16, 4096)["segments"] == 1     # 16 seqs fill it
     assert m.workspace_size(64, 64, 128, 8, 16, 65536, 4096) == 0
-    assert m.prefill_plan(64, 64, 128, 8, 1, 200)["segments"] == 1        # too short
+    g = m.prefill_plan(64, 64, 128, 8, 1, 512)      # at least 128 tokens a segment
+    assert g["segments"] == 4 and g["segment_tokens"] == 128
+    assert m.prefill_plan(64, 64, 128, 8, 1, 255)["segments"] == 1        # too short
     f = m.prefill_plan(4, 16, 16, 1, 1, 64, segments=3)
     assert f["segments"] == 3 and f["segment_tokens"] == 22     # whole 16-token chunks would give 2
     assert m.prefill_plan(64, 64, 128, 8, 1, 4096, segments=1)["segments"] == 1
