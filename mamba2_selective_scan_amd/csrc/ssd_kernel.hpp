@@ -379,23 +379,24 @@ ssd_scan_kernel(ScanArgs a) {
     // h[row fr0 + 16 i + l%16][16 nt + 4 (l/16) + v]; columns at Nr and past
     // (padding to whole tiles, Nr % 4 == 0) stay zero and are never stored
     f4m hacc[TW][NT];
-#pragma unroll
-    for (int i = 0; i < TW; ++i)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) hacc[i][nt] = f4m{0.f, 0.f, 0.f, 0.f};
-    if ((from_slot || from_carry) && wave_ok) {
-        const float *src = from_slot ? st_w : ws_w + int64_t(seg - 1) * HPN;
+    // Loaded through a buffer descriptor that is empty for a fresh segment 0
+    // (zeros, no memory touched) and covers the wave's rows otherwise: the
+    // same loads on every path.  Issued right after the first chunk's loads,
+    // so the two latencies overlap.
+    auto load_state = [&]() {
+        const float *src = from_slot ? st_w : ws_w + int64_t(seg > 0 ? seg - 1 : 0) * HPN;
+        const int bytes = (from_slot || from_carry) && wave_ok ? 16 * TW * Nr * int(sizeof(float)) : 0;
+        const __amdgpu_buffer_rsrc_t rs = buffer_of(src, bytes);
 #pragma unroll
         for (int i = 0; i < TW; ++i)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                if (16 * nt + 4 * kq >= Nr) continue;
-                const f4 v = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(
-                    src + int64_t(16 * i + tl) * Nr + 16 * nt + 4 * kq));
+                const int n0 = 16 * nt + 4 * kq;
+                const int vo = n0 < Nr ? ((16 * i + tl) * Nr + n0) * int(sizeof(float)) : 0x7ffffff0;
+                const f4 v = buffer_load4_nt(rs, vo);
                 hacc[i][nt] = f4m{v.x, v.y, v.z, v.w};
             }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
+    };
 
     // ---- chunk staging: buffer loads -> registers -> LDS (double-buffered).
     // Each thread's byte offsets into a chunk are fixed; a chunk's descriptors
@@ -660,9 +661,15 @@ ssd_scan_kernel(ScanArgs a) {
     if (n_chunks > 0) {
 #pragma unroll
         for (int k = 0; k < S::PF; ++k) issue_chunk(stg[k], k);
-        commit(B0{}, min(CT, n_tok));
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load_state();
+    __builtin_amdgcn_sched_barrier(0);
+    if (n_chunks > 0) commit(B0{}, min(CT, n_tok));
     __syncthreads();
+    // the state is in registers before the chunk loop (whose waits then count
+    // only the chunk loads)
+    __builtin_amdgcn_s_waitcnt(0);
     auto step = [&](int c, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
         const int t1 = t_begin + (c + 1) * CT;
@@ -672,9 +679,12 @@ ssd_scan_kernel(ScanArgs a) {
         if (c + 1 < n_chunks) commit(std::integral_constant<int, buf ^ 1>{}, min(CT, t_end - t1));
         __syncthreads();
     };
+    // (a pair cut short leaves the loop at once, so the loop head's wait counts
+    // only the loads of a whole pair)
     for (int c = 0; c < n_chunks; c += 2) {
         step(c, B0{});
-        if (c + 1 < n_chunks) step(c + 1, B1{});
+        if (c + 1 >= n_chunks) break;
+        step(c + 1, B1{});
     }
     if (n_chunks > 0 && wave_ok) finish_y((n_chunks - 1) & 1, n_chunks - 1);
 
