@@ -378,6 +378,29 @@ def test_split_prefill_shapes(ssm, orc, N, P):
     assert not np.any(st[6])
 
 
+@pytest.mark.parametrize("N,P", [(4, 16), (20, 32), (48, 16), (48, 64), (80, 32), (96, 48), (112, 16),
+                                 (120, 32), (100, 16)])
+def test_split_prefill_padded_state_tiles(ssm, orc, N, P):
+    """The matrix-core split at state sizes that are not a whole number of
+    16-column tiles, or are a tile count only they use (1, 2, 3, 5, 6, 7 and a
+    padded 8 tiles in the scan pass; 32, 64 or 128 padded columns in the state
+    pass), with one (P 16, 48) and two (P 32, 64) row tiles per wave; the plan
+    must pick the matrix-core form (4 lanes per row, 4 * tiles values each)."""
+    lengths = [0, 1, 77, 200, 31]
+    case = ssm_inputs.make_case(4, P, N, 2, lengths, [1, 0, 0, 1, 0], seed=700 + N + P,
+                                slots=[6, 0, 2, 5, 3], n_slots=8, poison_fresh=True,
+                                sentinel_unused=True, name=f"padded_N{N}_P{P}")
+    plan = ssm.prefill_plan(4, P, N, 2, len(lengths), 200, 4)
+    say(f"padded state tiles N={N} P={P}: {plan}")
+    assert plan["segments"] == 4 and plan["lanes_per_row"] == 4
+    assert plan["elems_per_lane"] == 4 * -(-N // 16)
+    assert plan["rows_per_block"] == (128 if P % 32 == 0 else 64)
+    y, st = run_gpu(case, "prefill_ws", segments=4)
+    y32, st32 = orc.scan_case(case, precision="f32")
+    assert_parity(case, y, st, y32, st32)
+    assert not np.any(st[6])
+
+
 @pytest.mark.parametrize("H,P,N,G", [(4, 96, 64, 1), (8, 32, 32, 2), (2, 256, 32, 1), (4, 64, 128, 2),
                                      (4, 128, 64, 2), (3, 32, 64, 3), (2, 16, 32, 2)])
 def test_split_prefill_wide_layouts(ssm, orc, H, P, N, G):
