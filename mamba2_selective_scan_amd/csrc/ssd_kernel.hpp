@@ -61,17 +61,20 @@ struct SsdScanShape {
     // plain probes): float reads at rows 4 (l/16) + v, column l%16 are free of
     // conflicts for a row stride of 4 mod 16 floats and 2-way at 8 mod 16; float4
     // reads at row l%16, columns 4 (l/16) .. + 3 cost 4 conflict cycles for 4 mod
-    // 16 and none for 8 mod 16.  B is read mostly the first way (the state
-    // update's B^T), C only the second (C h^T, G^T), so each has its own stride.
-    static constexpr int LDN = N + 4;               // B rows
-    static constexpr int LDC = N + 8;               // C rows
+    // 16 and none for 8 mod 16.  B is read both ways (the state update's B^T
+    // the first, G^T the second), C only the second (C h^T, G^T), so B is
+    // staged twice: at N + 4 for the first way and, beside C, at N + 8 for the
+    // second.
+    static constexpr int LDN = N + 4;               // B rows, read down columns
+    static constexpr int LDC = N + 8;               // C rows and B's row-read copy
     // x rows padded by 4 floats: a lane reads row 4 (l/16) + v, column l % 16
     // (+ a wave offset), so with RBW a multiple of the bank count the four
     // l/16 groups would share banks; 4 more floats per row put them 16 banks
     // apart (conflict-free for 32 and for 64 banks)
     static constexpr int XR = RBW + 4;
     static constexpr int OFF_C = 0;
-    static constexpr int OFF_B = OFF_C + CT * LDC;
+    static constexpr int OFF_BR = OFF_C + CT * LDC;  // B rows at stride LDC (G^T)
+    static constexpr int OFF_B = OFF_BR + CT * LDC;
     static constexpr int OFF_X = OFF_B + CT * LDN;  // x[CT][XR]
     static constexpr int OFF_S = OFF_X + CT * XR;   // [MH][CT] S_t
     static constexpr int OFF_DT = OFF_S + MH * CT;  // [MH][CT] dt_t (0 past the segment)
@@ -357,7 +360,8 @@ ssd_scan_kernel(ScanArgs a) {
     if (from_slot && n_tok <= 0) return;             // empty resume: slot unchanged
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: row offsets in SGPRs
     const int tl = lane & 15, kq = lane >> 4;        // lane % 16, lane / 16
     const int group_end = (g + 1) * a.heads_per_group * P;   // one past the group's last row
     const int fr_wg = g * a.heads_per_group * P + wb * S::RBW;  // first row h P + p of the window
@@ -407,13 +411,14 @@ ssd_scan_kernel(ScanArgs a) {
     // and chunk k is committed to LDS buffer k & 1.
     constexpr int kNone = 0x7ffffff0;
     const int x_tok = H * P * int(sizeof(float));
-    int vo_bc[S::U_BC], lo_bc[S::U_BC], vo_x[S::U_X], lo_x[S::U_X];
+    int vo_bc[S::U_BC], lo_bc[S::U_BC], lo_c[S::U_BC], vo_x[S::U_X], lo_x[S::U_X];
 #pragma unroll
     for (int u = 0; u < S::U_BC; ++u) {
         const int q = u * kThreads + tid;            // unit = (token, 4-group)
         const int tt = q / (N / 4), n0 = 4 * (q - tt * (N / 4));
         vo_bc[u] = q < CT * N / 4 && n0 < Nr ? ((tt * G + g) * Nr + n0) * int(sizeof(float)) : kNone;
-        lo_bc[u] = q < CT * N / 4 ? tt * LDN + n0 : -1;
+        lo_bc[u] = q < CT * N / 4 ? tt * LDN + n0 : -1;       // B at stride LDN
+        lo_c[u] = tt * LDC + n0;                              // C and B's copy at LDC
     }
 #pragma unroll
     for (int u = 0; u < S::U_X; ++u) {
@@ -461,9 +466,9 @@ ssd_scan_kernel(ScanArgs a) {
 #pragma unroll
         for (int u = 0; u < S::U_BC; ++u) {
             if (lo_bc[u] >= 0) {
-                const int tt = (u * kThreads + tid) / (N / 4);   // the unit's token
                 *reinterpret_cast<f4 *>(base + S::OFF_B + lo_bc[u]) = sg.pb[u];
-                *reinterpret_cast<f4 *>(base + S::OFF_C + lo_bc[u] + tt * (LDC - LDN)) = sg.pc[u];
+                *reinterpret_cast<f4 *>(base + S::OFF_BR + lo_c[u]) = sg.pb[u];
+                *reinterpret_cast<f4 *>(base + S::OFF_C + lo_c[u]) = sg.pc[u];
             }
         }
 #pragma unroll
@@ -555,7 +560,7 @@ ssd_scan_kernel(ScanArgs a) {
             const int off = 16 * nt + 4 * kq;
             f4 bq = {0.f, 0.f, 0.f, 0.f}, cq = {0.f, 0.f, 0.f, 0.f};
             if (NT % kWaves == 0 || nt < NT) {
-                bq = *reinterpret_cast<const f4 *>(base + S::OFF_B + tl * LDN + off);
+                bq = *reinterpret_cast<const f4 *>(base + S::OFF_BR + tl * LDC + off);
                 cq = *reinterpret_cast<const f4 *>(base + S::OFF_C + tl * LDC + off);
             }
             gb[4 * k + 0] = bq.x; gb[4 * k + 1] = bq.y; gb[4 * k + 2] = bq.z; gb[4 * k + 3] = bq.w;

@@ -72,6 +72,26 @@ const ShapeRow *shape_for(int N) {
 
 constexpr int kMaxDevices = 64;
 
+// Opt kernel K in to more than 64 KB of dynamic LDS, once per device (the tag
+// type gives every kernel its own flags).
+template <class K>
+int opt_in_lds(const void *kern, int lds_bytes) {
+    if (lds_bytes <= 64 * 1024) return SSM_OK;
+    static std::atomic<uint8_t> opted[kMaxDevices];
+    int dev = 0;
+    const hipError_t derr = hipGetDevice(&dev);
+    if (derr != hipSuccess) return hip_fail(derr, SSM_ERR_LAUNCH);
+    if (dev < 0 || dev >= kMaxDevices) return SSM_ERR_UNSUPPORTED;
+    if (!opted[dev].load(std::memory_order_acquire)) {
+        const hipError_t aerr = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+        if (aerr != hipSuccess) return hip_fail(aerr, SSM_ERR_LAUNCH);
+        opted[dev].store(1, std::memory_order_release);
+    }
+    return SSM_OK;
+}
+
+template <class S, bool VEC, Mode MODE, int OPT> struct ScanKernelTag {};
+
 }  // namespace
 
 // Scratch of ssm_scan_prefill_static: one copy on each GPU, for the life of
@@ -106,20 +126,8 @@ template <class S, bool VEC, Mode MODE, int OPT = 0>
 int launch(const ScanArgs &a, hipStream_t stream) {
     const void *kern = reinterpret_cast<const void *>(&ssm::scan_kernel<S, VEC, MODE, OPT>);
     const int lds_bytes = S::lds_floats(MODE, VEC) * int(sizeof(float));
-    if (lds_bytes > 64 * 1024) {
-        // Opt in to more than 64 KB of dynamic LDS, once per device.
-        static std::atomic<uint8_t> opted[kMaxDevices];
-        int dev = 0;
-        const hipError_t derr = hipGetDevice(&dev);
-        if (derr != hipSuccess) return hip_fail(derr, SSM_ERR_LAUNCH);
-        if (dev < 0 || dev >= kMaxDevices) return SSM_ERR_UNSUPPORTED;
-        if (!opted[dev].load(std::memory_order_acquire)) {
-            const hipError_t aerr =
-                hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-            if (aerr != hipSuccess) return hip_fail(aerr, SSM_ERR_LAUNCH);
-            opted[dev].store(1, std::memory_order_release);
-        }
-    }
+    const int orc = opt_in_lds<ScanKernelTag<S, VEC, MODE, OPT>>(kern, lds_bytes);
+    if (orc != SSM_OK) return orc;
     ScanArgs args = a;
     void *params[] = {&args};
     const hipError_t err = hipLaunchKernel(kern, dim3(unsigned(a.n_blocks)), dim3(kThreads), params,
@@ -330,30 +338,34 @@ int64_t ssd_windows(const ssm_scan_dims *d) {
     const int64_t rbw = 64 * ssd_tiles(d);
     return (group_rows + rbw - 1) / rbw;
 }
-// Scan-pass kernel and its LDS floats for state tiles NT and tiles per wave TW.
+// Scan-pass kernel, its LDS floats and its LDS opt-in for state tiles NT and
+// tiles per wave TW.
+using OptIn = int (*)(const void *, int);
+template <int NT, int TW> struct SsdScanTag {};
 template <int NT, int TW>
-void ssd_scan_pick(const void **kern, int *lds) {
+void ssd_scan_pick(const void **kern, int *lds, OptIn *opt_in = nullptr) {
     *kern = reinterpret_cast<const void *>(&ssm::ssd_scan_kernel<NT, TW>);
     *lds = ssm::SsdScanShape<NT, TW>::lds_floats();
+    if (opt_in) *opt_in = &opt_in_lds<SsdScanTag<NT, TW>>;
 }
 // 16-column state tiles of the scan pass (N rounded up).
 int ssd_scan_tiles(const ssm_scan_dims *d) { return (d->d_state + 15) / 16; }
 template <int TW>
-void ssd_scan_tw(int nt, const void **kern, int *lds) {
+void ssd_scan_tw(int nt, const void **kern, int *lds, OptIn *opt_in) {
     switch (nt) {
-    case 1: ssd_scan_pick<1, TW>(kern, lds); break;
-    case 2: ssd_scan_pick<2, TW>(kern, lds); break;
-    case 3: ssd_scan_pick<3, TW>(kern, lds); break;
-    case 4: ssd_scan_pick<4, TW>(kern, lds); break;
-    case 5: ssd_scan_pick<5, TW>(kern, lds); break;
-    case 6: ssd_scan_pick<6, TW>(kern, lds); break;
-    case 7: ssd_scan_pick<7, TW>(kern, lds); break;
-    default: ssd_scan_pick<8, TW>(kern, lds); break;
+    case 1: ssd_scan_pick<1, TW>(kern, lds, opt_in); break;
+    case 2: ssd_scan_pick<2, TW>(kern, lds, opt_in); break;
+    case 3: ssd_scan_pick<3, TW>(kern, lds, opt_in); break;
+    case 4: ssd_scan_pick<4, TW>(kern, lds, opt_in); break;
+    case 5: ssd_scan_pick<5, TW>(kern, lds, opt_in); break;
+    case 6: ssd_scan_pick<6, TW>(kern, lds, opt_in); break;
+    case 7: ssd_scan_pick<7, TW>(kern, lds, opt_in); break;
+    default: ssd_scan_pick<8, TW>(kern, lds, opt_in); break;
     }
 }
-void ssd_scan_for(const ssm_scan_dims *d, const void **kern, int *lds) {
-    if (ssd_tiles(d) == 2) ssd_scan_tw<2>(ssd_scan_tiles(d), kern, lds);
-    else ssd_scan_tw<1>(ssd_scan_tiles(d), kern, lds);
+void ssd_scan_for(const ssm_scan_dims *d, const void **kern, int *lds, OptIn *opt_in = nullptr) {
+    if (ssd_tiles(d) == 2) ssd_scan_tw<2>(ssd_scan_tiles(d), kern, lds, opt_in);
+    else ssd_scan_tw<1>(ssd_scan_tiles(d), kern, lds, opt_in);
 }
 
 SegPlan plan_segments(const ssm_scan_dims *d, const ShapeRow &row, int32_t n_seqs,
@@ -512,7 +524,10 @@ int scan_common(const ssm_scan_dims *d, const ssm_scan_options *opts, int32_t n_
                     kern = reinterpret_cast<const void *>(&ssm::ssd_state_kernel<2, 1, kSsdStateGroup>);
                 }
             } else {
-                ssd_scan_for(d, &kern, &lds);
+                OptIn opt_in = nullptr;
+                ssd_scan_for(d, &kern, &lds, &opt_in);
+                const int orc = opt_in(kern, lds * int(sizeof(float)));
+                if (orc != SSM_OK) return orc;
                 slabs = ssd_windows(d);
                 blocks = int64_t(n_seqs) * plan.n_segs * d->n_groups * slabs;
             }

@@ -233,8 +233,9 @@ def test_prefill_plan_and_workspace():
     plus the decay arrays."""
     g = m.prefill_plan(64, 64, 128, 8, 1, 4096)
     assert g["segments"] == 16 and g["segment_tokens"] == 256 and g["blocks"] == 16 * 32
-    # the scan pass of this shape takes two tiles per wave: 128 rows (two heads) per workgroup
-    assert g["chunk_tokens"] == 16 and g["rows_per_block"] == 128 and g["lds_bytes"] <= 64 * 1024
+    # the scan pass of this shape takes two tiles per wave: 128 rows (two heads) per
+    # workgroup, two workgroups to a CU's 160 KB of LDS
+    assert g["chunk_tokens"] == 16 and g["rows_per_block"] == 128 and 2 * g["lds_bytes"] <= 160 * 1024
     ws = m.workspace_size(64, 64, 128, 8, 1, 4096, 4096)
     # + per-segment decay totals [1][16][64] and alignment
     assert 16 * 64 * 64 * 128 * 4 + 4096 * 64 * 4 <= ws <= 16 * 64 * 64 * 128 * 4 + 4096 * 64 * 4 + 16 * 64 * 4 + 512
