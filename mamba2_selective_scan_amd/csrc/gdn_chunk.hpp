@@ -244,8 +244,12 @@ gdn_chunk_prep_kernel(GdnChunkArgs c) {
 // gamma_t and beta_t gamma_t come from the prep kernel, R is formed a quarter
 // per wave, and gamma_31 / gamma_t scales Delta (8 values per lane) rather
 // than K (16).
+// Two wavefronts per SIMD at most (176 VGPRs, 66 KB of LDS at Dk 128): a
+// batch of two or more sequences runs two workgroups per CU, one wave's VALU
+// and LDS work under the other's products (2 x 4096: 22% fewer cycles than
+// one workgroup per CU; one sequence, 256 workgroups, is unchanged).
 template <int NKT>                       // Dk = 16 NKT, NKT in {4, 8}
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gdn_chunk_scan_kernel(GdnChunkArgs c) {
     constexpr int Dk = 16 * NKT;
     constexpr int CW = NKT / 4;                      // 16-column tiles per wave
@@ -260,9 +264,13 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
     constexpr int SV = 256 * UNIT_ROUNDS;            // V rows (past the unit and its padding)
     constexpr int SG = SV + CT * VS;
     __shared__ __attribute__((aligned(16))) float stg[3][SG];
-    // parity, token tile, wave, lane: each wave's part of K S0^T (xk) and of y (xy)
-    __shared__ f4m xk[2][2][kWaves][64];
-    __shared__ f4m xy[2][2][kWaves][64];
+    // token tile, wave, lane: each wave's part of K S0^T (xk) and of y (xy).
+    // One copy each: a chunk reads the K S0^T parts between its two barriers
+    // and the previous chunk's y parts there too, and writes its own y parts
+    // after the second barrier and the next chunk's K S0^T parts after that,
+    // so no wave writes either while another may still read it.
+    __shared__ f4m xk[2][kWaves][64];
+    __shared__ f4m xy[2][kWaves][64];
     // R = beta (V - gamma K S0^T), token tile, lane (register layout of K S0^T)
     __shared__ f4m rx[2][64];
     // each wave's K of the chunk (32 tokens x its 16 CW key columns, rows padded
@@ -369,13 +377,13 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
     };
     auto comp = [](const f4 &x, int v) { return v == 0 ? x.x : v == 1 ? x.y : v == 2 ? x.z : x.w; };
     auto ld4 = [](const float *p) { return *reinterpret_cast<const f4 *>(p); };
-    // y of chunk ch from the partials in xy[par] (none for ch = -1, whose
-    // partials are never written): wave w sums token tile w/2,
+    // y of chunk ch from the partials in xy (none for ch = -1, whose partials
+    // are never written): wave w sums token tile w/2,
     // registers 2 (w%2) and 2 (w%2) + 1 (tokens 16 (w/2) + 4 (l/16) + 2 (w%2) + e)
     const int yb = w >> 1, yh = w & 1;
     const int vo_y = (4 * kq * Hv * Dv + vh * Dv + j0 + tl) * int(sizeof(float));
-    auto put_y = [&](int ch, int par) {
-        const float *p = reinterpret_cast<const float *>(&xy[par][yb][0][lane]) + 2 * yh;
+    auto put_y = [&](int ch) {
+        const float *p = reinterpret_cast<const float *>(&xy[yb][0][lane]) + 2 * yh;
         float2 yv = *reinterpret_cast<const float2 *>(p);
 #pragma unroll
         for (int k = 1; k < kWaves; ++k) {
@@ -396,7 +404,7 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
     // mod 3, written at the end of the chunk before last, visible since the
     // last barrier); the K and Q of the chunk after next are loaded into on,
     // its shared data into g and, at the end, into stg[(sp + 2) mod 3]
-    auto chunk_step = [&](const KQ &o, KQ &on, Stage &g, int ch, int par, int sp) {
+    auto chunk_step = [&](const KQ &o, KQ &on, Stage &g, int ch, int sp) {
         const int last = n_chunks_of(len) - 1;
         // K to LDS, read back transposed for the state update:
         // kt[b][cc][v] = K[16 b + 4 (l/16) + v][i0 + 16 cc + l%16]
@@ -418,7 +426,7 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
 #pragma unroll
                 for (int b = 0; b < 2; ++b) ks[b] = mfma16(comp(o.kr[b][cc], v), hacc[cc][v], ks[b]);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) xk[par][b][w][lane] = ks[b];
+        for (int b = 0; b < 2; ++b) xk[b][w][lane] = ks[b];
         const float *gp = stg[sp];
         const f4 t00 = ld4(gp + GdnUnit::T00 + row), t10 = ld4(gp + GdnUnit::T10 + row),
                  t11 = ld4(gp + GdnUnit::T11 + row), mb = ld4(gp + m_off + row);
@@ -445,7 +453,7 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
         __syncthreads();
         // this wave's quarter of R from the four parts of K S0^T
         {
-            const float *pk = reinterpret_cast<const float *>(&xk[par][yb][0][lane]) + 2 * yh;
+            const float *pk = reinterpret_cast<const float *>(&xk[yb][0][lane]) + 2 * yh;
             float2 ksq = *reinterpret_cast<const float2 *>(pk);
 #pragma unroll
             for (int k = 1; k < kWaves; ++k) {
@@ -463,7 +471,7 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
         load_stage(g, min(ch + 2, last));
         __builtin_amdgcn_sched_barrier(0);
         // the previous chunk's y: its partials were left before this chunk's first barrier
-        put_y(ch - 1, par ^ 1);
+        put_y(ch - 1);
         // this wave's part of Q S0^T, covering the exchange of R
 #pragma unroll
         for (int cc = 0; cc < CW; ++cc)
@@ -506,7 +514,7 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
             for (int v = 0; v < 4; ++v) yw[1] = mfma16(comp(mb, v), dl1[v], yw[1]);
         }
 #pragma unroll
-        for (int b = 0; b < 2; ++b) xy[par][b][w][lane] = yw[b];
+        for (int b = 0; b < 2; ++b) xy[b][w][lane] = yw[b];
         // S' = gamma_31 S0 + (diag(gamma_31/gamma) Delta)^T K, this wave's columns:
         // A operand K[s][i0 + 16 cc + l%16] with s = 16 b + 4 (l/16) + v, B operand the scaled Delta
         f4m dw0, dw1;
@@ -556,15 +564,15 @@ gdn_chunk_scan_kernel(GdnChunkArgs c) {
     // round's chunks (a branch there makes the compiler's load waits conservative)
     int ch = 0;
     for (; ch + 3 <= n_chunks; ch += 3) {
-        chunk_step(o0, o2, g, ch, ch & 1, 0);
-        chunk_step(o1, o0, g, ch + 1, (ch + 1) & 1, 1);
-        chunk_step(o2, o1, g, ch + 2, ch & 1, 2);
+        chunk_step(o0, o2, g, ch, 0);
+        chunk_step(o1, o0, g, ch + 1, 1);
+        chunk_step(o2, o1, g, ch + 2, 2);
     }
-    if (ch < n_chunks) chunk_step(o0, o2, g, ch, ch & 1, 0);
-    if (ch + 1 < n_chunks) chunk_step(o1, o0, g, ch + 1, (ch + 1) & 1, 1);
+    if (ch < n_chunks) chunk_step(o0, o2, g, ch, 0);
+    if (ch + 1 < n_chunks) chunk_step(o1, o0, g, ch + 1, 1);
     if (n_chunks > 0) {                              // the last chunk's y
         __syncthreads();
-        put_y(n_chunks - 1, (n_chunks - 1) & 1);
+        put_y(n_chunks - 1);
     }
 #pragma unroll
     for (int cc = 0; cc < CW; ++cc)
