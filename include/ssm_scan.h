@@ -110,11 +110,22 @@ int ssm_scan_prefill(const ssm_scan_dims *dims, int32_t n_seqs, int32_t n_tokens
  *                   arguments; owned by the caller, contents need no
  *                   initialisation and are garbage afterwards.  With NULL or
  *                   too small a workspace the call runs unsplit.
- * A split sequence is scanned as segments in parallel (segment 0 from the true
- * start state, later ones from zero); a second kernel chains the segments' end
- * states, carry <- prod(dA over the segment) * carry + end, and writes the
- * final state to the slot; a third adds each later segment's carried-in state
- * to its y: y[t] += prod(dA from the segment start through t) * (C_t . carry).
+ * A split sequence is cut into segments that run in parallel, in one of two
+ * forms (three kernels each):
+ *   - d_state <= 128 (a multiple of 4), head_dim a multiple of 16, 16-byte
+ *     aligned arrays: the chunked matrix form on the matrix cores.  A state
+ *     pass computes every segment's end state but the last (segment 0 from
+ *     the true start state, later ones from zero); a second kernel chains
+ *     them, carry <- prod(dA over the segment) * carry + end, into the state
+ *     carried into each segment; a third scans every segment from its
+ *     carried-in state in 16-token chunks, writing final y and, for the last
+ *     segment, the slot.  Automatic planning keeps segments of at least 128
+ *     tokens (shorter batches run unsplit).
+ *   - otherwise: the register scan of every segment (segment 0 from the true
+ *     start state, later ones from zero), the same chaining, which also writes
+ *     the final state to the slot, and a correction of each later segment's y:
+ *     y[t] += prod(dA from the segment start through t) * (C_t . carry).
+ *     Automatic planning keeps segments of at least 256 tokens.
  * Real arithmetic equals the sequential recurrence exactly; in floating point
  * only the association changes (the time-split form of the scan that "perf(cuda):
  * keep the Mamba2 scan state in registers ... #90" leaves for later).

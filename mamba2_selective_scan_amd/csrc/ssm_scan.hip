@@ -300,7 +300,8 @@ Kind prefill_kind(const ShapeRow &row, bool vec, int opt, int64_t n_blocks) {
 // register segment scan: cut when the whole-sequence launch would give fewer
 // than 2 wavefronts per SIMD (1024 SIMDs), aiming at 4; for the matrix-core
 // segment scan (shapes it covers): aim at 2 wavefronts per SIMD of its own
-// geometry (4 waves per 64 rows of a head).  Segments have at least 256 tokens.
+// geometry (4 waves per 64 rows of a head).  Segments have at least 256 tokens
+// in the register form, 128 in the matrix-core form.
 struct SegPlan {
     int n_segs, seg_len;
 };
