@@ -136,6 +136,16 @@ def test_geometry(N, decode):
         assert g["vector_path"] == int(aligned and N % 4 == 0)
 
 
+def test_vector_path_needs_chunk_in_buffer_range():
+    """The vector path stages a chunk of up to 32 tokens' x (and B, C) through
+    buffer descriptors with 32-bit byte ranges: H * P (and G * N) times 32
+    tokens times 4 bytes must stay below 2^31, else the scalar path runs."""
+    assert m.geometry(64, 64, 128, 8, 1)["vector_path"] == 1
+    assert m.geometry(4096, 4092, 128, 8, 1)["vector_path"] == 1        # 128 B short of 2^31
+    assert m.geometry(4096, 4096, 128, 8, 1)["vector_path"] == 0        # 2^24 rows x 128 B = 2^31
+    assert m.geometry(65536, 256, 128, 1, 1)["vector_path"] == 0
+
+
 def test_no_kernel_uses_scratch():
     """Each lane's state array must stay in VGPRs: every kernel in the build's
     resource report has ScratchSize 0."""
