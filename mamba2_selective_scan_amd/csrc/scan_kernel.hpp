@@ -672,7 +672,12 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                             base[S::OFF_DT + tid] = lazy ? dtv / loc : dtv;
                             base[S::OFF_DA + tid] = lazy ? loc : dA;
                         }
-                        if (tid < S::NSUB) base[S::OFF_LAZY + tid] = lazy ? 1.f : 0.f;
+                        // sub-chunk k's flag, written by lane k (not lane k's own
+                        // sub-chunk's: lanes 0 .. NSUB-1 all sit in sub-chunk 0)
+                        bool flag = lazy_k[0];
+#pragma unroll
+                        for (int k = 1; k < S::NSUB; ++k) flag = (tid == k) ? lazy_k[k] : flag;
+                        if (tid < S::NSUB) base[S::OFF_LAZY + tid] = flag ? 1.f : 0.f;
                     }
                 }
             } else {

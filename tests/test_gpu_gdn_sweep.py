@@ -1,0 +1,83 @@
+"""GPU parity for the gated delta rule over seeded random batches: the
+per-token prefill, the chunked prefill (or its per-token fallback where the
+shape does not take chunks) and decode, against the fp32 oracle.
+
+Each draw picks the head counts (value heads a multiple of key heads), key and
+value widths, 1-4 sequences of 0-500 tokens with empty ones, fresh and
+resumed starts, scattered slots (fresh ones NaN-poisoned, unused ones
+sentinel-filled), and half the time q and k rows of length U[0.25, 1.4] with
+drawn, 0, 1/2 or 1 write strengths.  Bar as everywhere: max |gpu - ref| /
+(1 + |ref|) <= 1e-4 on y and on the final state of every used slot.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import ssm_inputs
+from gpu_helpers import run_gdn_gpu, say
+from test_gpu_gdn import assert_gdn_parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import mamba2_selective_scan_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+def _gdn_sweep_case(seed):
+    rng = np.random.Generator(np.random.PCG64(95000 + seed))
+    Hk = int(rng.integers(1, 5))
+    Hv = Hk * int(rng.integers(1, 4))
+    if seed % 2 == 0:                            # shapes the chunked form takes
+        Dk = int(rng.choice([64, 128]))
+        Dv = 16 * int(rng.integers(1, 9))
+    else:
+        Dk = int(rng.integers(1, 129))
+        Dv = int(rng.integers(1, 129))
+    n = int(rng.integers(1, 5))
+    lengths = [int(v) for v in rng.integers(0, 501, size=n)]
+    if rng.random() < 0.3:
+        lengths[int(rng.integers(0, n))] = 0
+    fresh = [int(v) for v in rng.integers(0, 2, size=n)]
+    slots = [int(v) for v in rng.permutation(n + 2)[:n]]
+    normed = rng.random() < 0.5
+    beta = [None, 0.0, 0.5, 1.0][int(rng.integers(0, 4))] if normed else None
+    case = ssm_inputs.make_gdn_case(Hv, Hk, Dk, Dv, lengths, fresh, 96000 + seed, slots=slots,
+                                    n_slots=n + 2, poison_fresh=True, sentinel_unused=True,
+                                    qk_norm=(0.25, 1.4) if normed else None, beta=beta,
+                                    name=f"gdn_sweep{seed}_Hv{Hv}_Hk{Hk}_Dk{Dk}_Dv{Dv}_{lengths}"
+                                         f"{'_normed' if normed else ''}_beta{beta}")
+    return case
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_gdn_random_shape_sweep(ssm, orc, seed):
+    case = _gdn_sweep_case(seed)
+    ws = ssm.gdn_workspace_size(case.Hv, case.Hk, case.Dk, case.Dv, case.n_seqs,
+                                int(case.lengths.max()))
+    say(f"{case.name}: chunked workspace {ws} bytes")
+    y32, s32 = orc.gdn_case(case)
+    y, st = run_gdn_gpu(case, "prefill")
+    assert_gdn_parity(case, y, st, y32, s32, label=f"{case.name} per token")
+    y, st = run_gdn_gpu(case, "prefill_ws")
+    assert_gdn_parity(case, y, st, y32, s32, label=f"{case.name} chunked")
+    # decode at the same shape: 1..40 one-token sequences, scattered slots
+    rng = np.random.Generator(np.random.PCG64(97000 + seed))
+    n = int(rng.integers(1, 41))
+    dec = ssm_inputs.make_gdn_case(case.Hv, case.Hk, case.Dk, case.Dv, [1] * n,
+                                   [int(v) for v in rng.integers(0, 2, size=n)], 98000 + seed,
+                                   slots=[int(v) for v in rng.permutation(n + 3)[:n]],
+                                   n_slots=n + 3, poison_fresh=True, sentinel_unused=True,
+                                   name=f"gdn_sweep{seed}_decode{n}")
+    y32, s32 = orc.gdn_case(dec)
+    y, st = run_gdn_gpu(dec, "decode")
+    assert_gdn_parity(dec, y, st, y32, s32)

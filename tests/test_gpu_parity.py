@@ -350,6 +350,68 @@ def test_split_prefill_decay_regimes(ssm, orc, segments):
     assert_parity(case, y, st, y64, st64, label=f"decay regimes segments={segments} vs fp64")
 
 
+@pytest.mark.parametrize("H,P,N,G", [(64, 64, 128, 8), (8, 32, 8, 4), (4, 64, 64, 2)])
+def test_prefill_one_token_second_subchunk(ssm, orc, H, P, N, G):
+    """One-pass prefill with 32-token chunks: sequences whose last chunk ends
+    one token into its second 16-token sub-chunk (lengths 17, 49 and 1041,
+    all 17 mod 32), beside ones ending on other sub-chunk edges.  That lone
+    token runs the direct update while the sub-chunk before it runs with the
+    decay deferred, so each sub-chunk must read its own form's flag."""
+    lengths = [17, 49, 1041, 16, 33, 0]
+    fresh = [1, 0, 1, 0, 1, 0]
+    assert ssm.geometry(H, P, N, G, len(lengths))["chunk_tokens"] == 32
+    case = ssm_inputs.make_case(H, P, N, G, lengths, fresh, seed=700 + N + P,
+                                slots=[3, 0, 5, 2, 6, 1], n_slots=8, poison_fresh=True,
+                                sentinel_unused=True, name=f"second_subchunk_H{H}_P{P}_N{N}")
+    say(f"{case.name}: lengths {lengths}")
+    y, st = run_gpu(case, "prefill")
+    y32, st32 = orc.scan_case(case, precision="f32")
+    assert_parity(case, y, st, y32, st32)
+
+
+def test_prefill_subchunks_decide_apart(ssm, orc):
+    """One-pass prefill with 32-token chunks where one 16-token sub-chunk of a
+    chunk decays past the deferral floor (direct update) and the other does
+    not (deferred), in both orders, in fresh and resumed sequences."""
+    import dataclasses
+    H, P, N, G = 4, 32, 128, 2
+    lengths = [96, 80]
+    case = ssm_inputs.make_case(H, P, N, G, lengths, [1, 0], seed=733)
+    assert ssm.geometry(H, P, N, G, 2)["chunk_tokens"] == 32
+    A = np.full(H, -8.0, np.float32)
+    dt = case.dt.copy()
+    # e^{-8 * 0.5 * 16} = e^-64 over a steep sub-chunk, far below the floor
+    for t0 in (0, 48, 96 + 16, 96 + 64):     # seq 0: sub-chunks 0 of chunk 0, 1 of chunk 1;
+        dt[t0:t0 + 16] = 0.5                 # seq 1: 1 of chunk 0, 0 of chunk 2 (16 tokens)
+    case = dataclasses.replace(case, A=A, dt=dt, name="subchunks_decide_apart")
+    y, st = run_gpu(case, "prefill")
+    y32, st32 = orc.scan_case(case, precision="f32")
+    assert_parity(case, y, st, y32, st32)
+
+
+def test_prefill_decay_regimes_one_pass(ssm, orc):
+    """The four decay regimes through the one-pass prefill (32-token chunks,
+    so the bursts regime mixes deferred and direct sub-chunks inside one
+    chunk), against the fp64 oracle.  Over 700 barely decaying tokens (heads
+    0-3) any sequential fp32 scan drifts past the bar -- the fp32 oracle by
+    up to 1.9e-4 -- so there y must stay within twice the fp32 oracle's own
+    error; every other head and the final state meet the bar."""
+    case = decay_regimes_case()
+    assert ssm.geometry(case.H, case.P, case.N, case.G, 2)["chunk_tokens"] == 32
+    y, st = run_gpu(case, "prefill")
+    y64, st64 = orc.scan_case(case, precision="f64")
+    y32, _ = orc.scan_case(case, precision="f32")
+    e_gpu = (np.abs(y - y64) / (1 + np.abs(y64))).max(axis=(0, 2))      # per head
+    e_f32 = (np.abs(y32 - y64) / (1 + np.abs(y64))).max(axis=(0, 2))
+    say(f"  per-head y error vs fp64: gpu {np.array2string(e_gpu, precision=2)}")
+    say(f"  fp32 oracle vs fp64:      {np.array2string(e_f32, precision=2)}")
+    assert np.all(np.isfinite(y))
+    assert np.all(e_gpu[4:] <= TOL), e_gpu
+    assert np.all(e_gpu[:4] <= np.maximum(TOL, 2 * e_f32[:4])), (e_gpu, e_f32)
+    used = np.unique(case.slot)
+    assert rel_err(st[used], st64[used]) <= TOL
+
+
 @pytest.mark.parametrize("segments", [2, 3, 7])
 @pytest.mark.parametrize("max_seqlen", [150, 40])
 def test_split_prefill_mixed_batch(ssm, orc, segments, max_seqlen):
@@ -494,6 +556,65 @@ def test_split_prefill_1x16384_auto(ssm, orc):
     del y64, st64
     y32, st32 = orc.scan_case(case, precision="f32")
     assert_parity(case, y, st, y32, st32, label="split 1x16384 vs fp32")
+
+
+def _sweep_case(seed):
+    """A seeded random batch for the shape sweep: heads, groups, head dim,
+    state size, lengths (empty ones included), fresh flags, scattered slots,
+    and a split plan (automatic or forced segments, max_seqlen exact or
+    understated).  Half the draws keep to the matrix-core split's shapes
+    (N % 4 == 0, N <= 128, P % 16 == 0)."""
+    rng = np.random.Generator(np.random.PCG64(90000 + seed))
+    H = int(rng.choice([1, 2, 3, 4, 6, 8]))
+    G = int(rng.choice([g for g in (1, 2, 3, 4, 6, 8) if H % g == 0]))
+    if seed % 2 == 0:
+        P = int(rng.choice([16, 32, 48, 64, 80, 96, 112, 128]))
+        N = 4 * int(rng.integers(1, 33))
+    else:
+        P = int(rng.integers(1, 129))
+        N = int(rng.integers(1, 257))
+    while H * P > 512:
+        P = max(1, P // 2)
+    n = int(rng.integers(1, 5))
+    lengths = [int(v) for v in rng.integers(0, 1101, size=n)]
+    if rng.random() < 0.3:
+        lengths[int(rng.integers(0, n))] = 0
+    fresh = [int(v) for v in rng.integers(0, 2, size=n)]
+    n_slots = n + 2
+    slots = [int(v) for v in rng.permutation(n_slots)[:n]]
+    segments = int(rng.choice([0, 0, 2, 3, 4, 6]))
+    longest = max(lengths)
+    max_seqlen = None if rng.random() < 0.6 or longest < 2 else int(rng.integers(1, longest))
+    case = ssm_inputs.make_case(H, P, N, G, lengths, fresh, seed=91000 + seed, slots=slots,
+                                n_slots=n_slots, poison_fresh=True, sentinel_unused=True,
+                                name=f"sweep{seed}_H{H}_G{G}_P{P}_N{N}_{lengths}")
+    return case, segments, max_seqlen
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shape_sweep(ssm, orc, seed):
+    """Seeded random batches through the one-pass prefill, the split prefill
+    (whichever form its plan picks) and decode at the same shape, against the
+    fp32 oracle; fresh slots poisoned with NaN, unused slots unchanged."""
+    case, segments, max_seqlen = _sweep_case(seed)
+    ms = int(case.lengths.max()) if max_seqlen is None else max_seqlen
+    plan = ssm.prefill_plan(case.H, case.P, case.N, case.G, case.n_seqs, ms, segments)
+    say(f"{case.name} segments={segments} max_seqlen={ms}: {plan}")
+    y32, st32 = orc.scan_case(case, precision="f32")
+    y, st = run_gpu(case, "prefill")
+    assert_parity(case, y, st, y32, st32, label=f"{case.name} one pass")
+    y, st = run_gpu(case, "prefill_ws", max_seqlen=max_seqlen, segments=segments)
+    assert_parity(case, y, st, y32, st32, label=f"{case.name} split")
+    # decode at the same shape: 1..40 one-token sequences, scattered slots
+    rng = np.random.Generator(np.random.PCG64(92000 + seed))
+    n = int(rng.integers(1, 41))
+    dec = ssm_inputs.make_case(case.H, case.P, case.N, case.G, [1] * n,
+                               [int(v) for v in rng.integers(0, 2, size=n)], seed=93000 + seed,
+                               slots=[int(v) for v in rng.permutation(n + 3)[:n]], n_slots=n + 3,
+                               poison_fresh=True, sentinel_unused=True, name=f"sweep{seed}_decode{n}")
+    y32, st32 = orc.scan_case(dec, precision="f32")
+    y, st = run_gpu(dec, "decode")
+    assert_parity(dec, y, st, y32, st32)
 
 
 def test_split_prefill_scalar_path(ssm, orc):
