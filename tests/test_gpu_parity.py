@@ -711,3 +711,53 @@ def test_option_snapshots(ssm, orc, name, mode):
         t1 = int(case.cu_seqlens[s + 1])
         if case.lengths[s] > 0:
             assert np.array_equal(snaps[t1 - 1], st[case.slot[s]]), s
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_option_sweep(ssm, orc, seed):
+    """Seeded random batches with a random set of options -- softplus, a dt
+    bias, A per (head, state), snapshots -- through a random entry point
+    (one-pass prefill, split prefill, decode), on the vector or the scalar
+    path, against the fp32 oracle; snapshots also bit for bit at each
+    sequence's end against the state written to its slot."""
+    rng = np.random.Generator(np.random.PCG64(94000 + seed))
+    mode = ["prefill", "prefill_ws", "decode"][seed % 3]
+    H = int(rng.choice([1, 2, 4, 6]))
+    G = int(rng.choice([g for g in (1, 2, 3, 6) if H % g == 0]))
+    if rng.random() < 0.5:
+        P, N = int(rng.choice([16, 32, 64, 96])), 4 * int(rng.integers(1, 33))
+    else:
+        P, N = int(rng.integers(1, 100)), int(rng.integers(1, 200))
+    n = int(rng.integers(1, 5)) if mode != "decode" else int(rng.integers(1, 30))
+    lengths = [1] * n if mode == "decode" else [int(v) for v in rng.integers(0, 500, size=n)]
+    snapshots = bool(rng.random() < 0.4)
+    if snapshots and mode != "decode":
+        lengths = [min(v, 200) for v in lengths]
+    case = ssm_inputs.make_case(H, P, N, G, lengths, [int(v) for v in rng.integers(0, 2, size=n)],
+                                seed=94500 + seed, slots=[int(v) for v in rng.permutation(n + 2)[:n]],
+                                n_slots=n + 2, poison_fresh=True, sentinel_unused=True)
+    kw = {}
+    if rng.random() < 0.5:
+        kw["dt_softplus"] = True
+    if rng.random() < 0.5:
+        bias = _bias(H, 94700 + seed)
+        # without softplus a bias must keep dt + bias > 0
+        kw["dt_bias"] = bias if kw.get("dt_softplus") else (np.abs(bias) * 0.02).astype(np.float32)
+    if rng.random() < 0.4:
+        case = _a_per_state(case, 94800 + seed)
+        kw["A_per_state"] = True
+    offset = int(rng.random() < 0.3)
+    shown = f"{n}x1" if mode == "decode" else str(lengths)
+    case.name = (f"option_sweep{seed}_{mode}_H{H}_G{G}_P{P}_N{N}_{shown}_"
+                 f"{sorted(kw)}{'_snapshots' if snapshots else ''}{'_scalar' if offset else ''}")
+    say(case.name)
+    extra = dict(segments=int(rng.choice([0, 2, 3]))) if mode == "prefill_ws" else {}
+    res = run_gpu(case, mode, offset_floats=offset, snapshots=snapshots, **extra, **kw)
+    ref = orc.scan_case(case, precision="f32", snapshots=snapshots, **kw)
+    assert_parity(case, res[0], res[1], ref[0], ref[1])
+    if snapshots:
+        snaps, st = res[2], res[1]
+        assert rel_err(snaps, ref[2]) <= TOL
+        for s in range(case.n_seqs):
+            if case.lengths[s] > 0:
+                assert np.array_equal(snaps[int(case.cu_seqlens[s + 1]) - 1], st[case.slot[s]]), s
