@@ -761,3 +761,35 @@ def test_random_option_sweep(ssm, orc, seed):
         for s in range(case.n_seqs):
             if case.lengths[s] > 0:
                 assert np.array_equal(snaps[int(case.cu_seqlens[s + 1]) - 1], st[case.slot[s]]), s
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_batch_sweep(ssm, orc, seed):
+    """Seeded random batches at wide layouts, of 2-12 or of 8-200 sequences
+    (mostly short, a few long), so the launch takes the grids that only such
+    batches reach: half chunks where a whole chunk's grid would not be
+    resident, plain block order, split plans over many sequences."""
+    rng = np.random.Generator(np.random.PCG64(98500 + seed))
+    H = int(rng.choice([16, 32, 64]))
+    P = int(rng.choice([32, 64, 96]))
+    N = int(rng.choice([64, 100, 128]))
+    G = int(rng.choice([g for g in (1, 2, 4, 8) if H % g == 0]))
+    n = int(rng.integers(2, 13)) if seed % 2 else int(rng.integers(8, 201))
+    long = rng.random(n) < (0.3 if seed % 2 else 0.08)
+    lengths = np.where(long, rng.integers(100, 400, size=n), rng.integers(0, 41, size=n))
+    lengths = [int(v) for v in lengths]
+    while sum(lengths) * H * P * N > 1.5e9:                     # keep the oracle to seconds
+        lengths = lengths[: len(lengths) * 3 // 4]
+    n = len(lengths)
+    case = ssm_inputs.make_case(H, P, N, G, lengths, [int(v) for v in rng.integers(0, 2, size=n)],
+                                seed=98600 + seed, slots=[int(v) for v in rng.permutation(n + 4)[:n]],
+                                n_slots=n + 4, poison_fresh=True, sentinel_unused=True,
+                                name=f"batch_sweep{seed}_H{H}_G{G}_P{P}_N{N}_{n}seqs_{sum(lengths)}tok")
+    geo = ssm.geometry(H, P, N, G, n)
+    plan = ssm.prefill_plan(H, P, N, G, n, max(lengths))
+    say(f"{case.name}: one pass {geo}; split plan {plan}")
+    y32, st32 = orc.scan_case(case, precision="f32")
+    y, st = run_gpu(case, "prefill")
+    assert_parity(case, y, st, y32, st32, label=f"{case.name} one pass")
+    y, st = run_gpu(case, "prefill_ws")
+    assert_parity(case, y, st, y32, st32, label=f"{case.name} split")
