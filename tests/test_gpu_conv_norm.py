@@ -188,3 +188,51 @@ def test_norm_eps_edges(ssm, orc):
     case.y[:] = 0.0
     case.eps = 1e-5
     assert np.array_equal(run_norm_gpu(case), np.zeros_like(case.y))
+
+
+# ------------------------------------------------------------------ sweeps
+@pytest.mark.parametrize("seed", range(12))
+def test_conv_random_sweep(ssm, orc, seed):
+    """Seeded random conv batches: channel count, taps, 1-40 sequences of
+    0-300 tokens (empty ones included), fresh and resumed, scattered slots,
+    the prefill or decode entry, vector or scalar path, with or without
+    snapshots (prefill only)."""
+    rng = np.random.Generator(np.random.PCG64(97500 + seed))
+    K = int(rng.integers(1, 5))
+    D = int(rng.choice([int(rng.integers(1, 3000)), 4 * int(rng.integers(1, 1600))]))
+    mode = "decode" if seed % 3 == 2 else "prefill"
+    n = int(rng.integers(1, 41))
+    lengths = [1] * n if mode == "decode" else [int(v) for v in rng.integers(0, 301, size=n)]
+    if mode == "prefill" and rng.random() < 0.5:
+        lengths[int(rng.integers(0, n))] = 0
+    snapshots = K > 1 and rng.random() < 0.3 and mode == "prefill"   # the decode entry takes none
+    offset = int(rng.random() < 0.3)
+    case = ssm_inputs.make_conv_case(D, K, lengths, [int(v) for v in rng.integers(0, 2, size=n)],
+                                     97600 + seed, slots=rng.permutation(n + 3)[:n].astype(np.int32),
+                                     n_slots=n + 3, poison_fresh=True, sentinel_unused=True,
+                                     name=f"conv_sweep{seed}_{mode}_D{D}_K{K}_{n}seqs_{sum(lengths)}tok"
+                                          f"{'_snapshots' if snapshots else ''}{'_scalar' if offset else ''}")
+    say(case.name)
+    res = run_conv_gpu(case, mode, offset_floats=offset, snapshots=snapshots)
+    ref = orc.conv_case(case, snapshots=snapshots)
+    assert_conv_parity(case, res[0], res[1], ref[0], ref[1])
+    if snapshots:
+        assert np.array_equal(res[2], ref[2]), "snapshots differ"
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_norm_random_sweep(ssm, orc, seed):
+    """Seeded random gated RMSNorm shapes: rows, heads, row length (odd ones
+    included), scaled inputs, vector or scalar path."""
+    rng = np.random.Generator(np.random.PCG64(97800 + seed))
+    T, H = int(rng.integers(1, 300)), int(rng.integers(1, 9))
+    L = int(rng.choice([int(rng.integers(1, 2000)), 4 * int(rng.integers(1, 600))]))
+    case = ssm_inputs.make_norm_case(T, H, L, 97900 + seed, eps=float(rng.choice([1e-5, 1e-6, 0.0])),
+                                     y_std=float(rng.choice([1.0, 1e-3, 30.0])),
+                                     name=f"norm_sweep{seed}_T{T}_H{H}_L{L}")
+    offset = int(rng.random() < 0.3)
+    say(f"{case.name} eps={case.eps} offset={offset}")
+    out = run_norm_gpu(case, offset_floats=offset)
+    e = rel_err(out, orc.norm_case(case))
+    say(f"  max rel err {e:.3e}")
+    assert np.all(np.isfinite(out)) and e <= TOL

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import ssm_inputs
-from gpu_helpers import run_gdn_gpu, say
+from gpu_helpers import TOL, run_gdn_gpu, say
 from test_gpu_gdn import assert_gdn_parity
 
 pytestmark = pytest.mark.gpu
@@ -81,3 +81,37 @@ def test_gdn_random_shape_sweep(ssm, orc, seed):
     y32, s32 = orc.gdn_case(dec)
     y, st = run_gdn_gpu(dec, "decode")
     assert_gdn_parity(dec, y, st, y32, s32)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_gdn_random_option_sweep(ssm, orc, seed):
+    """Seeded random delta-rule batches with snapshots or arrays off 16-byte
+    alignment (the scalar path), through the per-token prefill or decode:
+    y and state against the fp32 oracle, snapshots too, and each sequence's
+    last snapshot bit for bit the state written to its slot."""
+    rng = np.random.Generator(np.random.PCG64(99000 + seed))
+    mode = "decode" if seed % 3 == 2 else "prefill"
+    Hk = int(rng.integers(1, 4))
+    Hv = Hk * int(rng.integers(1, 3))
+    Dk, Dv = int(rng.integers(1, 129)), int(rng.integers(1, 97))
+    n = int(rng.integers(1, 25)) if mode == "decode" else int(rng.integers(1, 4))
+    lengths = [1] * n if mode == "decode" else [int(v) for v in rng.integers(0, 120, size=n)]
+    snapshots = bool(seed % 2 == 0)
+    offset = int(rng.random() < 0.5)
+    case = ssm_inputs.make_gdn_case(Hv, Hk, Dk, Dv, lengths, [int(v) for v in rng.integers(0, 2, size=n)],
+                                    99500 + seed, slots=[int(v) for v in rng.permutation(n + 2)[:n]],
+                                    n_slots=n + 2, poison_fresh=True, sentinel_unused=True,
+                                    name=f"gdn_option_sweep{seed}_{mode}_Hv{Hv}_Hk{Hk}_Dk{Dk}_Dv{Dv}_"
+                                         f"{n}seqs{'_snapshots' if snapshots else ''}"
+                                         f"{'_scalar' if offset else ''}")
+    say(case.name)
+    res = run_gdn_gpu(case, mode, offset_floats=offset, snapshots=snapshots)
+    ref = orc.gdn_case(case, snapshots=snapshots)
+    assert_gdn_parity(case, res[0], res[1], ref[0], ref[1])
+    if snapshots:
+        sn, st = res[2], res[1]
+        err = np.abs(sn - ref[2]) / (1 + np.abs(ref[2]))
+        assert err.size == 0 or err.max() <= TOL
+        for s in range(case.n_seqs):
+            if case.lengths[s] > 0:
+                assert np.array_equal(sn[int(case.cu_seqlens[s + 1]) - 1], st[case.slot[s]]), s
