@@ -64,6 +64,44 @@ def test_static_scratch_matches_workspace_entry():
         assert_parity(case, y_s, st_s, y32, st32, label=f"{case.name} static vs fp32 oracle")
 
 
+def test_static_scratch_random_sweep():
+    """Twelve seeded random batches back to back, in no size order (so each
+    call finds the previous one's leftovers in the scratch): heads, head dim,
+    state size, lengths, fresh flags, scattered slots, forced or automatic
+    segments.  Bit for bit against the workspace entry, and to the oracle's
+    bar."""
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import mamba2_selective_scan_amd as ssm
+    orc = oracle.default()
+    for seed in range(12):
+        rng = np.random.Generator(np.random.PCG64(99700 + seed))
+        H = int(rng.choice([1, 2, 4, 8, 16]))
+        G = int(rng.choice([g for g in (1, 2, 4) if H % g == 0]))
+        if seed % 2 == 0:
+            P, N = int(rng.choice([16, 32, 64, 96])), 4 * int(rng.integers(1, 33))
+        else:
+            P, N = int(rng.integers(1, 100)), int(rng.integers(1, 260))
+        n = int(rng.integers(1, 6))
+        lengths = [int(v) for v in rng.integers(0, 1500, size=n)]
+        case = ssm_inputs.make_case(H, P, N, G, lengths, [int(v) for v in rng.integers(0, 2, size=n)],
+                                    seed=99800 + seed, slots=[int(v) for v in rng.permutation(n + 2)[:n]],
+                                    n_slots=n + 2, poison_fresh=True, sentinel_unused=True,
+                                    name=f"static_sweep{seed}_H{H}_G{G}_P{P}_N{N}_{lengths}")
+        segments = int(rng.choice([0, 2, 3, 5]))
+        max_seqlen = max(lengths)
+        need = ssm.workspace_size(H, P, N, G, n, case.n_tokens, max_seqlen, segments)
+        say(f"{case.name} segments={segments}: {need} bytes of scratch")
+        if need > ssm.STATIC_SCRATCH_BYTES:
+            continue
+        y_s, st_s = _run(ssm, case, "static", max_seqlen, segments)
+        y_w, st_w = _run(ssm, case, "ws", max_seqlen, segments)
+        assert np.array_equal(y_s, y_w), case.name
+        assert np.array_equal(st_s, st_w, equal_nan=True), case.name
+        y32, st32 = orc.scan_case(case, precision="f32")
+        assert_parity(case, y_s, st_s, y32, st32, label=f"{case.name} static vs fp32 oracle")
+
+
 def test_static_scratch_refuses_oversized_split():
     import torch
     import mamba2_selective_scan_amd as ssm
