@@ -799,11 +799,14 @@ def main():
                          "achieved_GBs": round(prefill_bytes() / (pf_ms * 1e-3) / 1e9, 1)},
             "counters": counters.get("split"),
         })
+        geo1 = ssm.geometry(H, P, N, G, 1)
         result["prefill_valu"] = dict(stats(ms1), **{
             "workload": "prefill 1 seq x 4096 tokens, fresh",
-            "path": "ssm_scan_prefill: one pass per (head, 16-row block), state in registers, "
-                    "y by DPP reduce-scatter, chunks of 32 tokens staged in LDS (the VALU path)",
-            "geometry": ssm.geometry(H, P, N, G, 1),
+            "path": f"ssm_scan_prefill: one pass per (head, {geo1['rows_per_block']}-row block), "
+                    f"state in registers ({geo1['lanes_per_row']} lanes x {geo1['elems_per_lane']} "
+                    f"per row), y by DPP reduce-scatter, chunks of {geo1['chunk_tokens']} tokens "
+                    "staged in LDS (the VALU path)",
+            "geometry": geo1,
             "roofline": {"bound": "alu", "achieved": round(tflops1, 3),
                          "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops1 / FP32_VALU_PEAK_TFLOPS, 4),
