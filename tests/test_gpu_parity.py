@@ -795,7 +795,7 @@ def test_random_batch_sweep(ssm, orc, seed):
     assert_parity(case, y, st, y32, st32, label=f"{case.name} split")
 
 
-def _extreme_case(seed):
+def _extreme_case(seed, decode=False):
     """A seeded batch with values at the edges of the method's range: per head,
     no decay (A = 0), dt of exactly 0 on some tokens, steep bursts (dt up to
     8, so a token's decay underflows fp32), inputs scaled by 1e-3 or 1e3, and
@@ -807,10 +807,13 @@ def _extreme_case(seed):
     N = int(rng.choice([16, 64, 100, 128]))
     n = int(rng.integers(1, 4))
     lengths = [int(v) for v in rng.integers(1, 700, size=n)]
+    if decode:                                               # one token each, more sequences
+        n = int(rng.integers(1, 40))
+        lengths = [1] * n
     case = ssm_inputs.make_case(H, P, N, G, lengths, [int(v) for v in rng.integers(0, 2, size=n)],
                                 seed=93600 + seed, slots=[int(v) for v in rng.permutation(n + 1)[:n]],
                                 n_slots=n + 1, state_std=float(rng.choice([0.5, 30.0])),
-                                name=f"extreme{seed}_G{G}_P{P}_N{N}_{lengths}")
+                                name=f"extreme{seed}_G{G}_P{P}_N{N}_{f'{n}x1' if decode else lengths}")
     T = case.n_tokens
     A, dt, x = case.A.copy(), case.dt.copy(), case.x.copy()
     A[0] = 0.0                                               # no decay at all
@@ -826,21 +829,19 @@ def _extreme_case(seed):
 @pytest.mark.parametrize("seed", range(8))
 def test_random_extreme_sweep(ssm, orc, seed):
     """Edge values (see _extreme_case) through the one-pass and the split
-    prefill, against the fp64 oracle.  Heads 2-7 (inputs scaled by 1e-3 or
+    prefill, and through decode (a batch of one-token sequences drawn the same
+    way), against the fp64 oracle.  Heads 2-7 (inputs scaled by 1e-3 or
     not, dt of 0 and decay bursts) meet the elementwise bar.  Head 0 (no
     decay over hundreds of tokens) and head 1 (inputs scaled by 1e3) sum many
     large terms of both signs into some small outputs, where no fp32 scan has
     elementwise relative accuracy (the fp32 oracle itself misses 1e-4 by up
     to 30x there); they meet the bar normwise: max |gpu - ref| over the head
     <= 1e-4 (1 + max |ref| over the head)."""
-    case = _extreme_case(seed)
-    say(case.name)
-    y64, st64 = orc.scan_case(case, precision="f64")
-    y32, _ = orc.scan_case(case, precision="f32")
-    used = np.unique(case.slot)
-    say(f"  fp32 oracle elementwise y error, heads 0, 1: {rel_err(y32[:, 0], y64[:, 0]):.2e}, "
-        f"{rel_err(y32[:, 1], y64[:, 1]):.2e}")
-    for mode in ("prefill", "prefill_ws"):
+    for case, mode in ((_extreme_case(seed), "prefill"), (_extreme_case(seed), "prefill_ws"),
+                       (_extreme_case(seed, decode=True), "decode")):
+        say(f"{case.name} {mode}")
+        y64, st64 = orc.scan_case(case, precision="f64")
+        used = np.unique(case.slot)
         y, st = run_gpu(case, mode)
         assert np.all(np.isfinite(y)) and np.all(np.isfinite(st[used]))
         for h in range(case.H):
