@@ -734,6 +734,24 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                 return part;
             }
         };
+        // The same operands for token t0 + kk of a group, from pointers formed
+        // once per group (kk a compile-time constant: its offsets fold into the
+        // LDS instructions instead of a per-token address computation).
+        struct GroupPtr {
+            const float *c, *x, *s;
+        };
+        auto group_ptr = [&](const float *base, int t0) __attribute__((always_inline)) {
+            return GroupPtr{base + S::OFF_C + 4 * r + t0 * NP, base + S::OFF_X + t0 * RB + i, base + t0};
+        };
+        auto token_load_g = [&](const GroupPtr &g, int kk) __attribute__((always_inline)) {
+            TokIn in;
+            lds_groups<R, J>(in.c, g.c + kk * NP);
+            lds_groups<R, J>(in.b, g.c + (S::OFF_B - S::OFF_C) + kk * NP);
+            in.x = g.x[kk * RB];
+            in.dt = g.s[S::OFF_DT + kk];
+            in.dA = g.s[S::OFF_DA + kk];
+            return in;
+        };
         auto token_part = [&](const float *base, int tt, auto lazy_tag) -> float __attribute__((always_inline)) {
             TokIn in = token_load(base, tt);
             return token_part_in(in, tt, lazy_tag);
@@ -776,10 +794,11 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
                 for (; t0 + KY <= nt; t0 += KY) {
                     float part[KY];
                     TokIn in[2];
-                    in[0] = token_load(base, t0);
+                    const GroupPtr gp = group_ptr(base, t0);
+                    in[0] = token_load_g(gp, 0);
 #pragma unroll
                     for (int kk = 0; kk < KY; ++kk) {
-                        if (kk + 1 < KY) in[(kk + 1) & 1] = token_load(base, t0 + kk + 1);
+                        if (kk + 1 < KY) in[(kk + 1) & 1] = token_load_g(gp, kk + 1);
                         __builtin_amdgcn_sched_barrier(0);
                         part[kk] = token_part_in(in[kk & 1], t0 + kk, lazy_tag);
                     }
