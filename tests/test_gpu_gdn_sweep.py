@@ -115,3 +115,24 @@ def test_gdn_random_option_sweep(ssm, orc, seed):
         for s in range(case.n_seqs):
             if case.lengths[s] > 0:
                 assert np.array_equal(sn[int(case.cu_seqlens[s + 1]) - 1], st[case.slot[s]]), s
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_gdn_random_batch_sweep(ssm, orc, seed):
+    """Seeded random batches of 8-48 sequences (mostly short, a few long) at
+    the model geometry (Hv 32, Hk 16, Dk = Dv = 128), so the chunked scan runs
+    more workgroups than CUs (two per CU) and the per-token kernel a large
+    grid; both prefills and the fp32 oracle."""
+    rng = np.random.Generator(np.random.PCG64(99300 + seed))
+    n = int(rng.integers(8, 49))
+    long = rng.random(n) < 0.1
+    lengths = [int(v) for v in np.where(long, rng.integers(100, 500, size=n), rng.integers(0, 60, size=n))]
+    case = ssm_inputs.make_gdn_case(32, 16, 128, 128, lengths, [int(v) for v in rng.integers(0, 2, size=n)],
+                                    99400 + seed, slots=[int(v) for v in rng.permutation(n + 3)[:n]],
+                                    n_slots=n + 3, poison_fresh=True, sentinel_unused=True,
+                                    name=f"gdn_batch_sweep{seed}_{n}seqs_{sum(lengths)}tok")
+    say(case.name)
+    y32, s32 = orc.gdn_case(case)
+    for mode in ("prefill", "prefill_ws"):
+        y, st = run_gdn_gpu(case, mode)
+        assert_gdn_parity(case, y, st, y32, s32, label=f"{case.name} {mode}")
