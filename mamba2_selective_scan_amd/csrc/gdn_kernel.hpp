@@ -324,10 +324,36 @@ __global__ void __launch_bounds__(kThreads) gdn_kernel(GdnArgs a) {
             float *Ys = lds + buf * S::BUF + S::OFF_Y + i;
             float y_keep = 0.f;
             int t0 = 0;
+            // KY tokens at a time from pointers formed once per group (the
+            // tokens' offsets fold into the LDS instructions), each token's
+            // operands read one token ahead of its arithmetic
+            struct Tok {
+                f4 kv[J], qv[J];
+                float decay, beta, qk, v;
+            };
             for (; t0 + KY <= nt; t0 += KY) {
+                const float *gk = base + S::OFF_K + 4 * r + t0 * NP;
+                const float *gv = base + S::OFF_V + t0 * RB + i;
+                const float *gs = base + t0;
+                auto load = [&](int kk) __attribute__((always_inline)) {
+                    Tok o;
+                    lds_groups<R, J>(o.kv, gk + kk * NP);
+                    lds_groups<R, J>(o.qv, gk + (S::OFF_Q - S::OFF_K) + kk * NP);
+                    o.decay = gs[S::OFF_DECAY + kk];
+                    o.beta = gs[S::OFF_BETA + kk];
+                    o.qk = gs[S::OFF_QK + kk];
+                    o.v = gv[kk * RB];
+                    return o;
+                };
+                Tok in[2];
+                in[0] = load(0);
 #pragma unroll
                 for (int kk = 0; kk < KY; ++kk) {
-                    const float yv = token_y(base, t0 + kk);
+                    if (kk + 1 < KY) in[(kk + 1) & 1] = load(kk + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const Tok &o = in[kk & 1];
+                    const float yv = token(o.kv, o.qv, o.decay, o.beta, o.qk, o.v);
+                    if constexpr (SNAP) snapshot(chunk_t0 + t0 + kk);
                     y_keep = (rk == kk) ? yv : y_keep;
                 }
                 Ys[(t0 + rk) * S::YR] = y_keep;
