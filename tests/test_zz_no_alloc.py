@@ -8,7 +8,8 @@ run back to back, larger first: the headline 1 x 4096 prefill (16 segments,
 33 MB of scratch), then a smaller batch on the matrix-core split, then the
 mixed batch on the register-path split (which also uses the running decays).
 A call that would need more than the scratch holds is refused before anything
-is enqueued.
+is enqueued.  The entry point also runs under HIP graph capture: four replays,
+bit for bit against eager calls.
 """
 import numpy as np
 import pytest
@@ -100,6 +101,46 @@ def test_static_scratch_random_sweep():
         assert np.array_equal(st_s, st_w, equal_nan=True), case.name
         y32, st32 = orc.scan_case(case, precision="f32")
         assert_parity(case, y_s, st_s, y32, st32, label=f"{case.name} static vs fp32 oracle")
+
+
+def test_static_scratch_under_graph_capture():
+    """The entry point's purpose: a split prefill captured in a HIP graph
+    (after one eager call, which looks the scratch up).  Every replay, with
+    eager calls and synchronisations between them, gives the same bits as the
+    same call made eagerly on a copy of the inputs; resumed sequences carry
+    their state forward replay by replay, as the eager copy does."""
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import mamba2_selective_scan_amd as ssm
+    case = ssm_inputs.make_case(8, 64, 128, 2, [1200, 700, 0, 333], [1, 0, 1, 0], seed=79,
+                                slots=[3, 0, 1, 4], n_slots=6, name="static_graph")
+    max_seqlen, segments = 1200, 4
+    assert ssm.prefill_plan(8, 64, 128, 2, 4, max_seqlen, segments)["segments"] == 4
+    g_in = ssm.to_device(case, "cuda:0")
+    e_in = ssm.to_device(case, "cuda:0")
+    yg = torch.empty((case.n_tokens, case.H, case.P), device="cuda:0")
+    ye = torch.empty_like(yg)
+
+    def call(d, y):
+        ssm.prefill_static(d["x"], d["dt"], d["A"], d["B"], d["C"], d["state"], d["cu_seqlens"],
+                           d["slot"], d["fresh"], max_seqlen, segments=segments, y=y)
+
+    call(g_in, yg)                     # eager on both copies: the scratch is looked up here
+    call(e_in, ye)
+    torch.cuda.synchronize()
+    assert torch.equal(yg, ye)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(g_in, yg)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        call(e_in, ye)
+        torch.cuda.synchronize()
+        assert torch.equal(yg, ye), rep
+        assert torch.equal(g_in["state"], e_in["state"]), rep
+    say(f"static split prefill under graph capture: 4 replays bit for bit")
 
 
 def test_static_scratch_refuses_oversized_split():
