@@ -155,6 +155,46 @@ def test_prefix_sum_exact(ssm):
     assert np.array_equal(st[0, 2:, :, 2], run[-1, 2:])
 
 
+@pytest.mark.parametrize("mode", ["prefill", "prefill_ws", "decode"])
+def test_scaling_by_two_is_exact(ssm, mode):
+    """The recurrence is linear in (x, the start state), and doubling is exact
+    in floating point, so doubling x and every start state doubles y and the
+    final states bit for bit, on every path (the split's matrix products
+    included)."""
+    import dataclasses
+    if mode == "decode":
+        case = ssm_inputs.workload("decode16")
+    elif mode == "prefill_ws":
+        case = ssm_inputs.make_case(8, 64, 128, 2, [700, 300, 0], [0, 1, 0], seed=31)
+    else:
+        case = ssm_inputs.workload("mixed")
+    twice = dataclasses.replace(case, x=case.x * np.float32(2), state=case.state * np.float32(2))
+    kw = dict(segments=3) if mode == "prefill_ws" else {}
+    y1, s1 = run_gpu(case, mode, **kw)
+    y2, s2 = run_gpu(twice, mode, **kw)
+    used = np.unique(case.slot)
+    assert np.array_equal(y2, 2 * y1)
+    assert np.array_equal(s2[used], 2 * s1[used])
+
+
+@pytest.mark.parametrize("mode", ["prefill", "prefill_ws", "decode"])
+def test_group_equivalence_is_exact(ssm, mode):
+    """G = H with each head's B and C repeated from its group equals G = 2
+    bit for bit: the group map only addresses the same numbers."""
+    import dataclasses
+    if mode == "decode":
+        case = ssm_inputs.make_case(8, 64, 128, 2, [1] * 12, [i % 2 for i in range(12)], seed=33)
+    else:
+        case = ssm_inputs.make_case(8, 64, 128, 2, [333, 1, 80, 0, 200], [1, 0, 1, 0, 0], seed=34)
+    rep = case.H // case.G
+    per_head = dataclasses.replace(case, G=case.H, B=np.repeat(case.B, rep, axis=1),
+                                   C=np.repeat(case.C, rep, axis=1))
+    kw = dict(segments=2) if mode == "prefill_ws" else {}
+    y1, s1 = run_gpu(case, mode, **kw)
+    y2, s2 = run_gpu(per_head, mode, **kw)
+    assert np.array_equal(y1, y2) and np.array_equal(s1, s2, equal_nan=True)
+
+
 def test_deterministic(ssm):
     case = ssm_inputs.workload("mixed")
     y1, s1 = run_gpu(case, "prefill")
