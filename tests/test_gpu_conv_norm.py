@@ -190,6 +190,15 @@ def test_norm_eps_edges(ssm, orc):
     assert np.array_equal(run_norm_gpu(case), np.zeros_like(case.y))
 
 
+def test_norm_scale_invariance_is_exact(ssm):
+    """With eps = 0 the norm of 2y equals the norm of y bit for bit: the mean
+    square takes an exact factor 4, its square root an exact factor 2."""
+    import dataclasses
+    case = ssm_inputs.make_norm_case(64, 8, 256, 977, eps=0.0, name="norm_scale")
+    twice = dataclasses.replace(case, y=case.y * np.float32(2))
+    assert np.array_equal(run_norm_gpu(case), run_norm_gpu(twice))
+
+
 # ------------------------------------------------------------------ sweeps
 @pytest.mark.parametrize("seed", range(12))
 def test_conv_random_sweep(ssm, orc, seed):

@@ -136,3 +136,22 @@ def test_gdn_random_batch_sweep(ssm, orc, seed):
     for mode in ("prefill", "prefill_ws"):
         y, st = run_gdn_gpu(case, mode)
         assert_gdn_parity(case, y, st, y32, s32, label=f"{case.name} {mode}")
+
+
+@pytest.mark.parametrize("mode", ["prefill", "prefill_ws", "decode"])
+def test_gdn_scaling_by_two_is_exact(ssm, mode):
+    """The delta rule is linear in (v, the start state) -- the keys enter
+    only through the decayed, rank-1 transition -- and doubling is exact, so
+    doubling v and every start state doubles y and the final states bit for
+    bit, per token, in the chunked matrix form and in decode."""
+    import dataclasses
+    if mode == "decode":
+        case = ssm_inputs.make_gdn_case(8, 4, 128, 64, [1] * 10, [i % 2 for i in range(10)], 97050)
+    else:
+        case = ssm_inputs.make_gdn_case(8, 4, 128, 64, [300, 33, 0, 130], [0, 1, 0, 1], 97051)
+    twice = dataclasses.replace(case, v=case.v * np.float32(2), state=case.state * np.float32(2))
+    y1, s1 = run_gdn_gpu(case, mode)
+    y2, s2 = run_gdn_gpu(twice, mode)
+    used = np.unique(case.slot)
+    assert np.array_equal(y2, 2 * y1)
+    assert np.array_equal(s2[used], 2 * s1[used])
